@@ -1,0 +1,269 @@
+#!/usr/bin/env python3
+"""Benchmark: batch-1 rotated W4A16 dequant GEMV on one MI355X.
+
+One step = one pass of the hot path over one batch: the seven projections
+of a 4B-class decoder block (q 2560->4096, k/v 2560->1024, o 4096->2560,
+gate/up 2560->9728, down 9728->2560), int4 codes with fp16 scale and zero
+per group of 128 along K, block-128 random Hadamard rotation of the
+activations fused into the product, M = 1, fp16 outputs.  The seven
+linears have independent inputs, so one step is a single grouped launch.
+
+Weights are cold: a rotating pool of distinct weight copies (>= 1 GB, well
+above the 256 MB Infinity Cache) is cycled, one copy per step.  Steps are
+replayed from a HIP graph so the host launch path stays out of the timed
+region.  The kernel's own duration per launch is measured with HIP events
+around single launches on the launch stream; the roofline figure is
+algorithmic bytes per launch over that duration.
+
+Prints one JSON line on stdout; details go to stderr.
+
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--workload block_int4] [--m 1]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+METRIC = "batch-1 RHT+W4A16 dequant GEMV: µs/linear and achieved HBM GB/s vs peak"
+PEAK_HBM_GBS = 8000.0
+POOL_BYTES = 1 << 30
+COUNTERS = os.path.join(ROOT, "profiles", "gemv_traffic_counters.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def bytes_per_weight(bits: int) -> float:
+    # packed codes plus one fp16 scale and one fp16 zero per 128 weights
+    return bits / 8.0 + 4.0 / 128.0
+
+
+def algorithmic_bytes(lins, m: int) -> int:
+    """What the method itself must move for one pass: codes + scales + zeros,
+    activations in, outputs out, rotation signs."""
+    total = 0
+    for lin in lins:
+        total += int(lin.n * lin.k * bytes_per_weight(lin.bits))
+        total += 2 * m * lin.k                      # fp16 activations
+        total += (4 if lin.out_f32 else 2) * m * lin.n
+        total += lin.k // 8 if lin.rht else 0        # sign bits
+    return total
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for f in ("gemv.hip", "wq_internal.h"):
+        with open(os.path.join(ROOT, "dequant_gemv_rht_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def cpu_baseline(wl, lins, m, budget_s: float):
+    """The fp64 oracle (explicit rotation, scalar dequant, C triple loop) timed on
+    this host over whole steps of the same workload, until ~budget_s of work."""
+    from oracle import linear as OL
+    from oracle import rtn as OR
+    prepared = []
+    for i, lin in enumerate(lins):
+        w, x, signs, _ = W.linear_inputs(0, wl.wid, i, lin, m)
+        q, s, z = OR.prepare(w, signs, lin.bits)
+        prepared.append((q, s, z, x, signs))
+        del w
+    threads = OL.default_threads()
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        for (q, s, z, x, signs) in prepared:
+            OL.linear(q, s, z, x, signs, threads=threads)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    per_step = el / steps
+    nbytes = algorithmic_bytes(lins, m)
+    return {"value": round(nbytes / per_step / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{steps} full step(s) of the same workload ({len(lins)} linears, M={m}); "
+                      f"{per_step * 1e3:.1f} ms per step, {per_step * 1e6 / len(lins):.0f} us per linear; "
+                      f"rotation + dequant + fp64 triple loop, excluding quantisation"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="block_int4")
+    ap.add_argument("--m", type=int, default=1)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pool-bytes", type=int, default=POOL_BYTES)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the path runs on a single MI355X and has no "
+              "multi-GPU mode; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import dequant_gemv_rht_amd as dq
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    dq.lib()  # fail loudly if the library is missing
+
+    wl = W.WORKLOADS[args.workload]
+    m = args.m
+    lins = [l for l in wl.linears if l.bits != 0 and not l.out_f32]
+    bits = lins[0].bits
+    nbytes = algorithmic_bytes(lins, m)
+    log(f"workload {wl.name}: {len(lins)} linears, M={m}, {nbytes / 1e6:.3f} MB algorithmic per step")
+
+    # ---- weights: generated on the host, prepared on the GPU (untimed)
+    base, xs = [], []
+    for i, lin in enumerate(lins):
+        w, x, signs, _ = W.linear_inputs(0, wl.wid, i, lin, m)
+        sg = torch.from_numpy(signs.view(np.int32)).cuda()
+        base.append(dq.quantize_weight(torch.from_numpy(w).cuda(), lin.bits, sg))
+        xs.append(torch.from_numpy(x).cuda())
+        del w
+    torch.cuda.synchronize()
+    weight_bytes = sum(q.codes.numel() * 4 + q.scales.numel() * 4 for q in base)
+    copies = max(2, math.ceil(args.pool_bytes / weight_bytes))
+    pool = [base]
+    for _ in range(copies - 1):
+        pool.append([dq.QWeight(q.bits, q.n, q.k, q.codes.clone(), q.scales.clone(), q.zeros.clone(),
+                                q.signs) for q in base])
+    ys = [torch.empty((m, lin.n), dtype=torch.float16, device="cuda") for lin in lins]
+    ws = dq.new_workspace(dq.wq_linear_batch_workspace(base, m))
+    calls = [dq.BatchCall(p, xs, ys, True, ws) for p in pool]
+    torch.cuda.synchronize()
+    log(f"pool: {copies} copies x {weight_bytes / 1e6:.1f} MB = {copies * weight_bytes / 1e9:.2f} GB")
+
+    stream = torch.cuda.Stream()
+    sptr = stream.cuda_stream
+
+    # ---- warmup (eager), then the timed steps from one graph of exactly K steps
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            calls[i % copies](sptr)
+    stream.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for i in range(args.steps):
+            calls[i % copies](sptr)
+    with torch.cuda.stream(stream):
+        graph.replay()                      # untimed replay: graph upload
+    torch.cuda.synchronize()
+
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        t0.record(stream)
+        graph.replay()
+        t1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = t0.elapsed_time(t1)
+    ms_per_step = ms_total / args.steps
+
+    # ---- per-launch kernel duration: events around single launches
+    n_single = max(50, copies * 3)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_single)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n_single)]
+    with torch.cuda.stream(stream):
+        for i in range(n_single):
+            starts[i].record(stream)
+            calls[i % copies](sptr)
+            ends[i].record(stream)
+    torch.cuda.synchronize()
+    durs = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    launch_ms = float(np.mean(durs))
+
+    # ---- eager per-step time (no graph) for context
+    with torch.cuda.stream(stream):
+        t0.record(stream)
+        for i in range(args.steps):
+            calls[i % copies](sptr)
+        t1.record(stream)
+    torch.cuda.synchronize()
+    eager_ms_per_step = t0.elapsed_time(t1) / args.steps
+
+    gbs = nbytes / (ms_per_step * 1e-3) / 1e9
+    achieved = nbytes / (launch_ms * 1e-3) / 1e9
+    log(f"graph: {ms_per_step * 1e3:.2f} us/step = {gbs:.0f} GB/s; eager {eager_ms_per_step * 1e3:.2f} us/step; "
+        f"kernel (events) mean {launch_ms * 1e3:.2f} us, p10 {durs[len(durs) // 10] * 1e3:.2f}, "
+        f"p90 {durs[9 * len(durs) // 10] * 1e3:.2f} -> {achieved:.0f} GB/s")
+
+    traffic = None
+    digest = source_digest()
+    if os.path.exists(COUNTERS):
+        try:
+            rec = json.load(open(COUNTERS))
+            key = f"{wl.name}/m{m}"
+            if rec.get("source_digest") == digest and key in rec.get("per_launch_bytes", {}):
+                traffic = rec["per_launch_bytes"][key]
+        except (OSError, ValueError):
+            traffic = None
+
+    result = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.title + f", M={m}",
+            "m": m, "bits": bits, "group": 128, "linears": len(lins),
+            "algorithmic_bytes_per_step": nbytes,
+            "launch": "one grouped launch per step (7 independent linears), replayed from a HIP graph",
+            "weight_pool": f"{copies} copies, {copies * weight_bytes / 1e9:.2f} GB (cold weights)",
+        },
+        "us_per_linear": round(ms_per_step * 1e3 / len(lins), 4),
+        "eager_us_per_step": round(eager_ms_per_step * 1e3, 3),
+        "frac_of_peak_hbm": round(gbs / PEAK_HBM_GBS, 4),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+            "kernel": f"gemv_kernel<{bits}, M-tile {1 if m == 1 else m}>",
+            "kernel_us": round(launch_ms * 1e3, 3),
+            "bytes_per_launch": nbytes,
+            "source_digest": digest,
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline: timing the oracle ...")
+        result["cpu_baseline"] = cpu_baseline(wl, lins, m, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

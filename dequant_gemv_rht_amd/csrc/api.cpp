@@ -1,0 +1,430 @@
+// C ABI of libwq: argument checks, workspace layout and kernel dispatch.
+// Every check runs on the host before any HIP call, so a rejected call
+// enqueues nothing.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "wq_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+wq_status fail(wq_status st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+void clear_err() { g_err[0] = 0; }
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool uniform_bits(int b) { return b == 3 || b == 4 || b == 6 || b == 8; }
+
+int mtile(int64_t m) {
+  if (m <= 1) return 1;
+  if (m <= 2) return 2;
+  if (m <= 4) return 4;
+  if (m <= 8) return 8;
+  return 16;
+}
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// validate a weight descriptor; `need_rht` true when the call rotates
+wq_status check_weight(const wq_weight *w, const char *who) {
+  if (!w) return fail(WQ_E_ARG, "%s: weight descriptor is NULL", who);
+  if (!(uniform_bits(w->bits) || w->bits == 0))
+    return fail(WQ_E_UNSUPPORTED, "%s: bits=%d (supported: 3, 4, 6, 8, 0 = mixed 6/8)", who, w->bits);
+  if (w->group != WQ_GROUP) return fail(WQ_E_UNSUPPORTED, "%s: group=%d (only 128)", who, w->group);
+  if (w->n <= 0 || w->k <= 0) return fail(WQ_E_ARG, "%s: n=%lld k=%lld must be positive", who,
+                                          (long long)w->n, (long long)w->k);
+  if (w->k % WQ_GROUP) return fail(WQ_E_ARG, "%s: k=%lld is not a multiple of 128", who, (long long)w->k);
+  if (w->n > (int64_t)INT32_MAX || w->k > (int64_t)INT32_MAX)
+    return fail(WQ_E_UNSUPPORTED, "%s: n or k above 2^31-1", who);
+  if (!w->codes || !w->scales || !w->zeros)
+    return fail(WQ_E_ARG, "%s: codes, scales and zeros must be non-NULL", who);
+  if (!aligned16(w->codes) || !aligned16(w->scales) || !aligned16(w->zeros))
+    return fail(WQ_E_ALIGN, "%s: codes/scales/zeros must be 16-byte aligned", who);
+  if (w->bits == 0) {
+    if (w->n % WQ_MIXED_ROWS) return fail(WQ_E_ARG, "%s: mixed width needs n %% 64 == 0 (n=%lld)", who,
+                                          (long long)w->n);
+    if (!w->block_bits || !w->block_off)
+      return fail(WQ_E_ARG, "%s: mixed width needs block_bits and block_off", who);
+  }
+  if (w->rht_signs) {
+    if (w->rht_block != WQ_RHT_BLOCK)
+      return fail(WQ_E_UNSUPPORTED, "%s: rht_block=%d (only 128)", who, w->rht_block);
+    if (!aligned16(w->rht_signs)) return fail(WQ_E_ALIGN, "%s: rht_signs must be 16-byte aligned", who);
+  }
+  return WQ_OK;
+}
+
+wq_status hip_status(hipError_t e, const char *who) {
+  if (e == hipSuccess) return WQ_OK;
+  return fail(WQ_E_HIP, "%s: %s", who, hipGetErrorString(e));
+}
+
+// Workgroup layout of one linear in the GEMV path: whole rows per
+// workgroup, K walked inside; the rotated activations of a K chunk sit in LDS.
+struct GemvPlan {
+  int mode, rows, row_blocks, kc, lds;
+};
+
+GemvPlan gemv_plan(const wq_weight &w, int64_t m) {
+  GemvPlan p;
+  const int mt = mtile(m);
+  wq::gemv_shape(w.bits, mt, w.k, p.mode, p.rows);
+  p.row_blocks = (int)((w.n + p.rows - 1) / p.rows);
+  p.kc = wq::gemv_chunk(mt, w.k);
+  p.lds = wq::gemv_lds_bytes(mt, p.kc, p.rows, w.k);
+  return p;
+}
+
+int device_cus() {
+  thread_local int cached_dev = -1, cached_cus = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev != cached_dev) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached_dev = dev;
+    cached_cus = n;
+  }
+  return cached_cus;
+}
+
+constexpr int kMaxLds = 160 * 1024;
+
+// Persistent stream kernel plan: workgroups (one per CU) split among the
+// linears in proportion to their bytes; each gets an even number of rows.
+bool plan_stream(int count, const wq_weight *w, int64_t m, int *wg, int *rows_per_wg, int *lds) {
+  const int mt = mtile(m);
+  if (w[0].bits == 0 || mt > 4) return false;
+  const int ncu = device_cus();
+  if (count > ncu) return false;
+  double bytes[WQ_MAX_BATCH], total = 0;
+  int64_t maxwg[WQ_MAX_BATCH];
+  for (int i = 0; i < count; ++i) {
+    bytes[i] = (double)w[i].n * (double)w[i].k * (w[i].bits / 8.0 + 4.0 / 128.0);
+    total += bytes[i];
+    maxwg[i] = (w[i].n + 1) / 2;
+  }
+  int sum = 0;
+  for (int i = 0; i < count; ++i) {
+    int64_t g = (int64_t)(ncu * bytes[i] / total);
+    if (g < 1) g = 1;
+    if (g > maxwg[i]) g = maxwg[i];
+    wg[i] = (int)g;
+    sum += wg[i];
+  }
+  while (sum > ncu) {            // shrink the largest share
+    int b = 0;
+    for (int i = 1; i < count; ++i)
+      if (wg[i] > wg[b]) b = i;
+    if (wg[b] <= 1) return false;
+    --wg[b];
+    --sum;
+  }
+  while (sum < ncu) {            // give spare CUs to the most loaded linear
+    int b = -1;
+    double best = 0;
+    for (int i = 0; i < count; ++i)
+      if (wg[i] < maxwg[i] && bytes[i] / wg[i] > best) {
+        best = bytes[i] / wg[i];
+        b = i;
+      }
+    if (b < 0) break;
+    ++wg[b];
+    ++sum;
+  }
+  *lds = 0;
+  for (int i = 0; i < count; ++i) {
+    int64_t r = (w[i].n + wg[i] - 1) / wg[i];
+    r = (r + 1) / 2 * 2;
+    rows_per_wg[i] = (int)r;
+    wg[i] = (int)((w[i].n + r - 1) / r);
+    const int need = wq::gemv_stream_lds_bytes(mt, w[i].k, (int)r);
+    if (need > *lds) *lds = need;
+  }
+  return *lds <= kMaxLds;
+}
+
+// Launch one GEMV over `count` linears with batch rows m (<= 16).
+wq_status run_gemv(int count, const wq_weight *w, const uint16_t *const *x, const int64_t *ldx,
+                   int64_t m, void *const *y, const wq_dtype *ydt, const int64_t *ldy,
+                   bool rotate, hipStream_t s) {
+  wq::GemvArgs a;
+  memset(&a, 0, sizeof a);
+  a.count = count;
+  a.m = (int32_t)m;
+  // longest rows first, so the longest workgroups start first
+  int order[WQ_MAX_BATCH];
+  for (int i = 0; i < count; ++i) order[i] = i;
+  for (int i = 1; i < count; ++i)
+    for (int j = i; j > 0 && w[order[j]].k > w[order[j - 1]].k; --j) {
+      int t = order[j];
+      order[j] = order[j - 1];
+      order[j - 1] = t;
+    }
+  wq_weight ws[WQ_MAX_BATCH];
+  for (int o = 0; o < count; ++o) ws[o] = w[order[o]];
+  int wg[WQ_MAX_BATCH], rpw[WQ_MAX_BATCH], slds = 0;
+  const bool stream = plan_stream(count, ws, m, wg, rpw, &slds);
+  int64_t tiles = 0;
+  int lds = 0;
+  for (int o = 0; o < count; ++o) {
+    const int i = order[o];
+    GemvPlan p = gemv_plan(w[i], m);
+    wq::LinDesc &L = a.lin[o];
+    L.codes = w[i].codes;
+    L.scales = w[i].scales;
+    L.zeros = w[i].zeros;
+    L.block_bits = w[i].block_bits;
+    L.block_off = w[i].block_off;
+    L.signs = rotate ? w[i].rht_signs : nullptr;
+    L.x = x[i];
+    L.y = y[i];
+    L.ldx = ldx[i];
+    L.ldy = ldy[i];
+    L.n = (int32_t)w[i].n;
+    L.k = (int32_t)w[i].k;
+    L.kc = p.kc;
+    L.mode = p.mode;
+    L.row_blocks = p.row_blocks;
+    L.out_f32 = ydt[i] == WQ_F32;
+    L.tile_begin = (int32_t)tiles;
+    if (stream) {
+      L.rows_per_wg = rpw[o];
+      tiles += wg[o];
+    } else {
+      tiles += p.row_blocks;
+      if (p.lds > lds) lds = p.lds;
+    }
+  }
+  if (tiles > INT32_MAX) return fail(WQ_E_UNSUPPORTED, "wq_linear: too many workgroups");
+  a.tiles = (int32_t)tiles;
+  if (stream) {
+    a.lds_bytes = slds;
+    return hip_status(wq::launch_gemv_stream(w[0].bits, mtile(m), a, s), "wq_linear");
+  }
+  a.lds_bytes = lds;
+  return hip_status(wq::launch_gemv(w[0].bits, mtile(m), a, s), "wq_linear");
+}
+
+wq_status check_io(const wq_weight &w, const uint16_t *x, int64_t m, int64_t ldx, const void *y,
+                   wq_dtype ydt, int64_t ldy, const char *who) {
+  if (m <= 0) return fail(WQ_E_ARG, "%s: m=%lld must be positive", who, (long long)m);
+  if (!x || !y) return fail(WQ_E_ARG, "%s: x and y must be non-NULL", who);
+  if (!aligned16(x) || !aligned16(y)) return fail(WQ_E_ALIGN, "%s: x and y must be 16-byte aligned", who);
+  if (ldx < w.k) return fail(WQ_E_ARG, "%s: ldx=%lld < k=%lld", who, (long long)ldx, (long long)w.k);
+  if (ldx % 8) return fail(WQ_E_ALIGN, "%s: ldx must be a multiple of 8 (16-byte rows)", who);
+  if (ldy < w.n) return fail(WQ_E_ARG, "%s: ldy=%lld < n=%lld", who, (long long)ldy, (long long)w.n);
+  if (ydt != WQ_F16 && ydt != WQ_F32) return fail(WQ_E_ARG, "%s: y_dtype must be WQ_F16 or WQ_F32", who);
+  return WQ_OK;
+}
+
+// Matrix-core path: the rotated activations (fp16 [m][ldr]) live at the
+// start of the workspace, followed by what the GEMM itself needs.
+int64_t rotated_ld(const wq_weight &w) { return (w.k + 7) / 8 * 8; }
+
+size_t rotated_bytes(const wq_weight &w, int64_t m) {
+  return w.rht_signs ? align256((size_t)m * (size_t)rotated_ld(w) * sizeof(uint16_t)) : 0;
+}
+
+size_t gemm_path_workspace(const wq_weight &w, int64_t m) {
+  return rotated_bytes(w, m) + wq::gemm_workspace(w, m);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *wq_last_error(void) { return g_err; }
+
+size_t wq_packed_words(int32_t bits, int64_t n, int64_t k, const uint8_t *block_bits_host) {
+  clear_err();
+  if (n <= 0 || k <= 0 || k % WQ_GROUP) {
+    fail(WQ_E_ARG, "wq_packed_words: need n > 0 and k a positive multiple of 128");
+    return 0;
+  }
+  if (uniform_bits(bits)) return (size_t)n * (size_t)(k / 32) * (size_t)bits;
+  if (bits != 0) {
+    fail(WQ_E_UNSUPPORTED, "wq_packed_words: bits=%d", bits);
+    return 0;
+  }
+  if (n % WQ_MIXED_ROWS || !block_bits_host) {
+    fail(WQ_E_ARG, "wq_packed_words: mixed width needs n %% 64 == 0 and host block_bits");
+    return 0;
+  }
+  size_t total = 0;
+  for (int64_t i = 0; i < n / WQ_MIXED_ROWS; ++i) {
+    const int b = block_bits_host[i];
+    if (b != 6 && b != 8) {
+      fail(WQ_E_ARG, "wq_packed_words: block_bits[%lld]=%d (6 or 8)", (long long)i, b);
+      return 0;
+    }
+    total += (size_t)WQ_MIXED_ROWS * (size_t)(k / 32) * (size_t)b;
+  }
+  return total;
+}
+
+wq_status wq_quantize(int32_t bits, int64_t n, int64_t k, const float *w, const uint32_t *rht_signs,
+                      const uint8_t *block_bits, uint8_t *codes, uint16_t *scales, uint16_t *zeros,
+                      void *stream) {
+  clear_err();
+  if (!(uniform_bits(bits) || bits == 0)) return fail(WQ_E_UNSUPPORTED, "wq_quantize: bits=%d", bits);
+  if (n <= 0 || k <= 0 || k % WQ_GROUP) return fail(WQ_E_ARG, "wq_quantize: need n > 0, k %% 128 == 0");
+  if (!w || !codes || !scales || !zeros) return fail(WQ_E_ARG, "wq_quantize: NULL buffer");
+  if (bits == 0 && (n % WQ_MIXED_ROWS || !block_bits))
+    return fail(WQ_E_ARG, "wq_quantize: mixed width needs n %% 64 == 0 and block_bits");
+  if (!aligned16(w) || !aligned16(codes) || !aligned16(scales) || !aligned16(zeros) ||
+      (rht_signs && !aligned16(rht_signs)))
+    return fail(WQ_E_ALIGN, "wq_quantize: buffers must be 16-byte aligned");
+  return hip_status(wq::launch_quantize(bits, n, k, w, rht_signs, block_bits, codes, scales, zeros,
+                                        (hipStream_t)stream), "wq_quantize");
+}
+
+wq_status wq_pack(int32_t bits, int64_t n, int64_t k, const uint8_t *codes, const uint8_t *block_bits,
+                  uint32_t *packed, uint64_t *block_off, void *stream) {
+  clear_err();
+  if (!(uniform_bits(bits) || bits == 0)) return fail(WQ_E_UNSUPPORTED, "wq_pack: bits=%d", bits);
+  if (n <= 0 || k <= 0 || k % WQ_GROUP) return fail(WQ_E_ARG, "wq_pack: need n > 0, k %% 128 == 0");
+  if (!codes || !packed) return fail(WQ_E_ARG, "wq_pack: NULL buffer");
+  if (bits == 0 && (n % WQ_MIXED_ROWS || !block_bits || !block_off))
+    return fail(WQ_E_ARG, "wq_pack: mixed width needs n %% 64 == 0, block_bits and block_off");
+  if (!aligned16(codes) || !aligned16(packed) || (block_off && !aligned16(block_off)))
+    return fail(WQ_E_ALIGN, "wq_pack: buffers must be 16-byte aligned");
+  return hip_status(wq::launch_pack(bits, n, k, codes, block_bits, packed, block_off, (hipStream_t)stream),
+                    "wq_pack");
+}
+
+wq_status wq_unpack(int32_t bits, int64_t n, int64_t k, const uint32_t *packed, const uint8_t *block_bits,
+                    const uint64_t *block_off, uint8_t *codes, void *stream) {
+  clear_err();
+  if (!(uniform_bits(bits) || bits == 0)) return fail(WQ_E_UNSUPPORTED, "wq_unpack: bits=%d", bits);
+  if (n <= 0 || k <= 0 || k % WQ_GROUP) return fail(WQ_E_ARG, "wq_unpack: need n > 0, k %% 128 == 0");
+  if (!codes || !packed) return fail(WQ_E_ARG, "wq_unpack: NULL buffer");
+  if (bits == 0 && (n % WQ_MIXED_ROWS || !block_bits || !block_off))
+    return fail(WQ_E_ARG, "wq_unpack: mixed width needs n %% 64 == 0, block_bits and block_off");
+  if (!aligned16(codes) || !aligned16(packed)) return fail(WQ_E_ALIGN, "wq_unpack: buffers must be 16-byte aligned");
+  return hip_status(wq::launch_unpack(bits, n, k, packed, block_bits, block_off, codes, (hipStream_t)stream),
+                    "wq_unpack");
+}
+
+wq_status rht_apply(const uint16_t *x, uint16_t *y, const uint32_t *signs, int64_t m, int64_t k, int64_t ldx,
+                    int64_t ldy, int32_t block, void *stream) {
+  clear_err();
+  if (block != WQ_RHT_BLOCK) return fail(WQ_E_UNSUPPORTED, "rht_apply: block=%d (only 128)", block);
+  if (m < 0 || k <= 0 || k % WQ_RHT_BLOCK) return fail(WQ_E_ARG, "rht_apply: need m >= 0, k %% 128 == 0");
+  if (!x || !y || !signs) return fail(WQ_E_ARG, "rht_apply: NULL buffer");
+  if (ldx < k || ldy < k) return fail(WQ_E_ARG, "rht_apply: ldx and ldy must be >= k");
+  if (ldx % 8 || ldy % 8) return fail(WQ_E_ALIGN, "rht_apply: ldx and ldy must be multiples of 8");
+  if (!aligned16(x) || !aligned16(y) || !aligned16(signs))
+    return fail(WQ_E_ALIGN, "rht_apply: buffers must be 16-byte aligned");
+  if (x == y && ldx != ldy) return fail(WQ_E_ARG, "rht_apply: in place needs ldx == ldy");
+  return hip_status(wq::launch_rht(x, y, signs, m, k, ldx, ldy, (hipStream_t)stream), "rht_apply");
+}
+
+size_t wq_linear_workspace(const wq_weight *w, int64_t m) {
+  clear_err();
+  if (check_weight(w, "wq_linear_workspace") != WQ_OK) return (size_t)-1;
+  if (m <= 0) {
+    fail(WQ_E_ARG, "wq_linear_workspace: m must be positive");
+    return (size_t)-1;
+  }
+  if (m >= 64) return gemm_path_workspace(*w, m);
+  return 0;   // the GEMV needs no workspace
+}
+
+wq_status wq_linear(const wq_weight *w, const uint16_t *x, int64_t m, int64_t ldx, void *y,
+                    wq_dtype y_dtype, int64_t ldy, uint32_t flags, void *workspace, size_t workspace_bytes,
+                    void *stream) {
+  clear_err();
+  wq_status st = check_weight(w, "wq_linear");
+  if (st != WQ_OK) return st;
+  st = check_io(*w, x, m, ldx, y, y_dtype, ldy, "wq_linear");
+  if (st != WQ_OK) return st;
+  if (flags & ~WQ_FUSE_RHT) return fail(WQ_E_ARG, "wq_linear: unknown flags 0x%x", flags);
+  const bool rotate = (flags & WQ_FUSE_RHT) && w->rht_signs;
+  const size_t need = wq_linear_workspace(w, m);
+  if (need > workspace_bytes || (need && !workspace))
+    return fail(WQ_E_WORKSPACE, "wq_linear: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  if (workspace && !aligned16(workspace)) return fail(WQ_E_ALIGN, "wq_linear: workspace must be 16-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  if (m >= 64) {
+    // Matrix-core path: rotate into the workspace first, then the GEMM.
+    if (!wq::gemm_available(w->bits))
+      return fail(WQ_E_UNSUPPORTED, "wq_linear: no matrix-core kernel for bits=%d at m=%lld", w->bits,
+                  (long long)m);
+    const uint16_t *xr = x;
+    int64_t ldr = ldx;
+    char *ws = static_cast<char *>(workspace);
+    if (rotate) {
+      uint16_t *xt = reinterpret_cast<uint16_t *>(ws);
+      ldr = rotated_ld(*w);
+      st = hip_status(wq::launch_rht(x, xt, w->rht_signs, m, w->k, ldx, ldr, s), "wq_linear");
+      if (st != WQ_OK) return st;
+      xr = xt;
+    }
+    ws += rotated_bytes(*w, m);
+    return hip_status(wq::launch_gemm(*w, xr, m, ldr, y, y_dtype == WQ_F32, ldy, ws, s), "wq_linear");
+  }
+  // GEMV, in chunks of 16 batch rows
+  const size_t esz = y_dtype == WQ_F32 ? 4 : 2;
+  for (int64_t m0 = 0; m0 < m; m0 += 16) {
+    const int64_t mc = (m - m0) < 16 ? (m - m0) : 16;
+    const uint16_t *xc = x + m0 * ldx;
+    void *yc = static_cast<char *>(y) + (size_t)m0 * (size_t)ldy * esz;
+    st = run_gemv(1, w, &xc, &ldx, mc, &yc, &y_dtype, &ldy, rotate, s);
+    if (st != WQ_OK) return st;
+  }
+  return WQ_OK;
+}
+
+size_t wq_linear_batch_workspace(int32_t count, const wq_weight *w, int64_t m) {
+  clear_err();
+  if (count <= 0 || count > WQ_MAX_BATCH || !w) {
+    fail(WQ_E_ARG, "wq_linear_batch_workspace: count must be 1..%d", WQ_MAX_BATCH);
+    return (size_t)-1;
+  }
+  if (m <= 0 || m > 16) {
+    fail(WQ_E_UNSUPPORTED, "wq_linear_batch_workspace: m must be 1..16");
+    return (size_t)-1;
+  }
+  for (int i = 0; i < count; ++i)
+    if (check_weight(&w[i], "wq_linear_batch_workspace") != WQ_OK) return (size_t)-1;
+  return 0;   // the GEMV needs no workspace
+}
+
+wq_status wq_linear_batch(int32_t count, const wq_weight *w, const uint16_t *const *x, const int64_t *ldx,
+                          int64_t m, void *const *y, const wq_dtype *y_dtype, const int64_t *ldy, uint32_t flags,
+                          void *workspace, size_t workspace_bytes, void *stream) {
+  clear_err();
+  if (count <= 0 || count > WQ_MAX_BATCH) return fail(WQ_E_ARG, "wq_linear_batch: count must be 1..%d", WQ_MAX_BATCH);
+  if (!w || !x || !ldx || !y || !y_dtype || !ldy) return fail(WQ_E_ARG, "wq_linear_batch: NULL argument array");
+  if (m <= 0 || m > 16) return fail(WQ_E_UNSUPPORTED, "wq_linear_batch: m must be 1..16");
+  if (flags & ~WQ_FUSE_RHT) return fail(WQ_E_ARG, "wq_linear_batch: unknown flags 0x%x", flags);
+  for (int i = 0; i < count; ++i) {
+    wq_status st = check_weight(&w[i], "wq_linear_batch");
+    if (st != WQ_OK) return st;
+    st = check_io(w[i], x[i], m, ldx[i], y[i], y_dtype[i], ldy[i], "wq_linear_batch");
+    if (st != WQ_OK) return st;
+    if (w[i].bits != w[0].bits)
+      return fail(WQ_E_UNSUPPORTED, "wq_linear_batch: all weights must share one code width");
+    if (((flags & WQ_FUSE_RHT) && w[i].rht_signs) != ((flags & WQ_FUSE_RHT) && w[0].rht_signs))
+      return fail(WQ_E_UNSUPPORTED, "wq_linear_batch: rotate all linears or none");
+  }
+  (void)workspace;
+  (void)workspace_bytes;
+  const bool rotate = (flags & WQ_FUSE_RHT) && w[0].rht_signs;
+  return run_gemv(count, w, x, ldx, m, y, y_dtype, ldy, rotate, (hipStream_t)stream);
+}
+
+}  // extern "C"

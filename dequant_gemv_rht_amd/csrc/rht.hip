@@ -1,0 +1,57 @@
+// Standalone block random Hadamard rotation of fp16 activations (gfx950).
+//
+// y[m][128j : 128j+128] = H D_j x[m][128j : 128j+128] / sqrt(128)
+// (model card "24B0978 - Week 01 - Track 2, 20% target", paragraph on the
+// random Hadamard transform: a fast Walsh-Hadamard transform of log2(block)
+// add/sub stages applied to the activations at run time).
+//
+// One 128-block per 16-lane DPP row: lane jj holds elements 8jj..8jj+7,
+// butterflies of stride 1, 2, 4 run inside the lane and strides 8..64 across
+// lanes by DPP.  fp32 inside, one rounding to fp16 at the end.
+#include "wq_internal.h"
+
+namespace wq {
+using namespace dev;
+
+namespace {
+
+__global__ __launch_bounds__(256) void rht_kernel(const uint16_t *__restrict__ x, uint16_t *y,
+                                                  const uint32_t *__restrict__ signs, int64_t m,
+                                                  int64_t k, int64_t ldx, int64_t ldy) {
+  const int64_t nb = k / 128;
+  const int64_t item = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int jj = threadIdx.x & 15;
+  if (item >= m * nb) return;   // whole 16-lane rows leave together
+  const int64_t row = item / nb, b = item % nb;
+  const int64_t kk = b * 128 + 8 * jj;
+  const uint4 raw = *reinterpret_cast<const uint4 *>(x + row * ldx + kk);
+  float v[8];
+  v[0] = half_bits_to_float(raw.x & 0xFFFF); v[1] = half_bits_to_float(raw.x >> 16);
+  v[2] = half_bits_to_float(raw.y & 0xFFFF); v[3] = half_bits_to_float(raw.y >> 16);
+  v[4] = half_bits_to_float(raw.z & 0xFFFF); v[5] = half_bits_to_float(raw.z >> 16);
+  v[6] = half_bits_to_float(raw.w & 0xFFFF); v[7] = half_bits_to_float(raw.w >> 16);
+  const uint32_t sb = signs[kk >> 5] >> (kk & 31);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = ((sb >> e) & 1u) ? -v[e] : v[e];
+  fwht128_row16_signed(v, jj);
+  const float sc = fwht_lane_sign(jj) * 0.08838834764831845f;
+  uint4 out;
+  out.x = pack_half2(v[0] * sc, v[1] * sc);
+  out.y = pack_half2(v[2] * sc, v[3] * sc);
+  out.z = pack_half2(v[4] * sc, v[5] * sc);
+  out.w = pack_half2(v[6] * sc, v[7] * sc);
+  *reinterpret_cast<uint4 *>(y + row * ldy + kk) = out;
+}
+
+}  // namespace
+
+hipError_t launch_rht(const uint16_t *x, uint16_t *y, const uint32_t *signs, int64_t m, int64_t k,
+                      int64_t ldx, int64_t ldy, hipStream_t s) {
+  const int64_t items = m * (k / 128);
+  const int64_t blocks = (items + 15) / 16;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(rht_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, y, signs, m, k, ldx, ldy);
+  return hipGetLastError();
+}
+
+}  // namespace wq

@@ -1,0 +1,232 @@
+// Internal declarations shared by the libwq translation units (not part of
+// the C ABI).  Kernels are written for gfx950 (CDNA4): wave64, DPP row
+// operations within 16-lane rows, v_dot2_f32_f16.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "../../include/wq.h"
+
+namespace wq {
+
+constexpr int kGroup = 128;        // quantisation group along K = rotation block
+constexpr int kSeg = 512;          // K per GEMV tile segment: 16 lanes x 32 codes
+constexpr int kSlice = 32;         // codes per lane per row
+constexpr int kThreads = 256;      // GEMV workgroup
+constexpr int kMaxBatch = WQ_MAX_BATCH;
+
+// ---------------------------------------------------------------------------
+// GEMV launch description
+// ---------------------------------------------------------------------------
+struct LinDesc {
+  const uint32_t *codes;
+  const uint16_t *scales;
+  const uint16_t *zeros;
+  const uint8_t *block_bits;    // mixed width only
+  const uint64_t *block_off;    // mixed width only
+  const uint32_t *signs;        // nullptr: activations used as given
+  const uint16_t *x;
+  void *y;
+  int64_t ldx, ldy;
+  int32_t n, k;
+  int32_t kc;                   // K per LDS chunk of staged activations (multiple of 512)
+  int32_t mode;                 // tiled kernel's tile shape: 0 short K, 1 long K
+  int32_t rows_per_wg;          // stream kernel: output rows per workgroup (even)
+  int32_t row_blocks;
+  int32_t tile_begin;           // first workgroup of this linear in the grid
+  int32_t out_f32;
+};
+
+struct GemvArgs {
+  LinDesc lin[kMaxBatch];
+  int32_t count;
+  int32_t m;                    // batch rows actually present (<= MT)
+  int32_t tiles;                // total workgroups
+  int32_t lds_bytes;            // dynamic LDS per workgroup
+};
+
+// Host-side launchers (gemv*.hip).  `bits` 0 = mixed.  mt = 1,2,4,8,16.
+hipError_t launch_gemv(int bits, int mt, const GemvArgs &a, hipStream_t s);
+// Persistent stream kernel: one 1024-thread workgroup per CU, uniform code
+// width, batch tile <= 4, the linear's whole rotated K range in LDS.
+constexpr int kStreamThreads = 1024;
+hipError_t launch_gemv_stream(int bits, int mt, const GemvArgs &a, hipStream_t s);
+int gemv_stream_lds_bytes(int mt, int64_t k, int rows_per_wg);
+void gemv_shape(int bits, int mt, int64_t k, int &mode, int &rows);
+int gemv_chunk(int mt, int64_t k);              // K per LDS chunk
+int gemv_lds_bytes(int mt, int chunk, int rows, int64_t k);
+
+// Other launchers.
+hipError_t launch_rht(const uint16_t *x, uint16_t *y, const uint32_t *signs, int64_t m,
+                      int64_t k, int64_t ldx, int64_t ldy, hipStream_t s);
+hipError_t launch_quantize(int bits, int64_t n, int64_t k, const float *w,
+                           const uint32_t *signs, const uint8_t *block_bits, uint8_t *codes,
+                           uint16_t *scales, uint16_t *zeros, hipStream_t s);
+hipError_t launch_pack(int bits, int64_t n, int64_t k, const uint8_t *codes,
+                       const uint8_t *block_bits, uint32_t *packed, uint64_t *block_off,
+                       hipStream_t s);
+hipError_t launch_unpack(int bits, int64_t n, int64_t k, const uint32_t *packed,
+                         const uint8_t *block_bits, const uint64_t *block_off, uint8_t *codes,
+                         hipStream_t s);
+
+// MFMA GEMM for m >= 64 (gemm.hip).  xr: fp16 activations already rotated
+// (or unrotated weights), [m][ldx].
+bool gemm_available(int bits);
+size_t gemm_workspace(const wq_weight &w, int64_t m);
+hipError_t launch_gemm(const wq_weight &w, const uint16_t *xr, int64_t m, int64_t ldx, void *y,
+                       int out_f32, int64_t ldy, void *workspace, hipStream_t s);
+
+}  // namespace wq
+
+// ---------------------------------------------------------------------------
+// Device helpers
+// ---------------------------------------------------------------------------
+#if defined(__HIP__)
+namespace wq {
+namespace dev {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x3 __attribute__((ext_vector_type(3)));
+
+// Raw buffer addressing: a load whose offset lies outside the resource's
+// byte range returns zero without touching memory, which lets every load be
+// issued unconditionally (straight-line code, exact vmcnt waits).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOOB = 0x80000000u;          // an offset past any resource
+constexpr int kRsrcWord3 = 0x00020000;           // gfx9 raw buffer descriptor word 3
+constexpr int kNT = 2;                           // aux: non-temporal (streamed once)
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, kRsrcWord3);
+}
+
+// DPP controls (GFX9 encoding).
+constexpr int kQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kQuadRev = 0x1B;       // quad_perm [3,2,1,0]  (lane ^ 3)
+constexpr int kRowRor8 = 0x128;      // row_ror:8            (lane ^ 8 in a row)
+constexpr int kRowMirror = 0x140;    // lane ^ 15 in a row
+constexpr int kRowHalfMirror = 0x141; // lane ^ 7 within 8 lanes
+
+// Lane permutation within 16-lane rows.  All source lanes of these
+// permutations exist, so no "old" value is needed and the move can be folded
+// into the instruction that consumes it (v_add_f32_dpp, v_fmac_f32_dpp).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+
+// value of lane (this ^ 4) within a 16-lane row: (lane ^ 7) ^ 3
+__device__ __forceinline__ float dpp_xor4(float v) {
+  return dpp<kQuadRev>(dpp<kRowHalfMirror>(v));
+}
+
+// Sum over the 16 lanes of a DPP row; every lane gets the total.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp<kQuadXor1>(v);
+  v += dpp<kQuadXor2>(v);
+  v += dpp<kRowHalfMirror>(v);
+  v += dpp<kRowMirror>(v);
+  return v;
+}
+
+// One butterfly stage across lanes: lanes whose `upper` bit is set hold the
+// second element of each pair.  new = low + high (low lane), low - high
+// (high lane), i.e. partner + (upper ? -mine : mine).
+template <int CTRL>
+__device__ __forceinline__ void xstage(float (&v)[8], bool upper) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float p = dpp<CTRL>(v[e]);
+    v[e] = p + (upper ? -v[e] : v[e]);
+  }
+}
+
+__device__ __forceinline__ void xstage_xor4(float (&v)[8], bool upper) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float p = dpp_xor4(v[e]);
+    v[e] = p + (upper ? -v[e] : v[e]);
+  }
+}
+
+// Walsh-Hadamard transform (Sylvester order, no scaling) of one 128-block
+// spread over the 16 lanes of a DPP row: lane jj holds elements 8jj..8jj+7.
+// Stages with strides 1, 2, 4 are inside a lane; strides 8, 16, 32, 64 pair
+// lane jj with lane jj ^ 1, ^ 2, ^ 4, ^ 8.
+__device__ __forceinline__ void fwht128_row16(float (&v)[8], int jj) {
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if (!(e & h)) {
+        float a = v[e], b = v[e + h];
+        v[e] = a + b;
+        v[e + h] = a - b;
+      }
+    }
+  }
+  xstage<kQuadXor1>(v, jj & 1);
+  xstage<kQuadXor2>(v, jj & 2);
+  xstage_xor4(v, jj & 4);
+  xstage<kRowRor8>(v, jj & 8);
+}
+
+// The same transform with each cross-lane stage as one fused multiply-add
+// fed by DPP: stored = mine + beta * partner, beta = -1 on the lane holding
+// the pair's second element.  The high lane then holds the negated
+// difference, so after the four cross-lane stages lane jj holds the
+// transform times (-1)^popcount(jj); callers fold that sign into their
+// scale (fwht_lane_sign).
+template <int CTRL>
+__device__ __forceinline__ void xstage_fma(float (&v)[8], float beta) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = fmaf(dpp<CTRL>(v[e]), beta, v[e]);
+}
+
+__device__ __forceinline__ void fwht128_row16_signed(float (&v)[8], int jj) {
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if (!(e & h)) {
+        float a = v[e], b = v[e + h];
+        v[e] = a + b;
+        v[e + h] = a - b;
+      }
+    }
+  }
+  xstage_fma<kQuadXor1>(v, (jj & 1) ? -1.0f : 1.0f);
+  xstage_fma<kQuadXor2>(v, (jj & 2) ? -1.0f : 1.0f);
+  {
+    const float beta = (jj & 4) ? -1.0f : 1.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = fmaf(dpp_xor4(v[e]), beta, v[e]);
+  }
+  xstage_fma<kRowRor8>(v, (jj & 8) ? -1.0f : 1.0f);
+}
+
+__device__ __forceinline__ float fwht_lane_sign(int jj) {
+  return (__builtin_popcount(jj & 15) & 1) ? -1.0f : 1.0f;
+}
+
+__device__ __forceinline__ uint32_t pack_half2(float lo, float hi) {
+  _Float16 a = (_Float16)lo, b = (_Float16)hi;   // round to nearest even
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c, false);
+}
+
+}  // namespace dev
+}  // namespace wq
+#endif

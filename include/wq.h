@@ -1,0 +1,206 @@
+/*
+ * wq.h - C ABI of libwq: a rotated, grouped-affine low-bit linear layer for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What the layer computes.  The weight of a linear layer with N output rows
+ * and K input channels is stored as integer codes q (3, 4, 6 or 8 bits) with
+ * one fp16 scale s and one fp16 zero point z per group of 128 consecutive
+ * entries along K, and a weight is w = (q - z) * s.  The dequantised weight
+ * is never written to memory: it is formed in registers inside the product.
+ * Source: model card "24B0978 - Week 01 - Track 2, 20% target -
+ * Submission 01", section "How these techniques accelerate inference on
+ * CUDA", paragraph on group-wise affine integer quantisation.
+ *
+ * Before quantisation each weight row was rotated by a block random Hadamard
+ * transform R = H . D / sqrt(128) per block of 128 channels (H: Sylvester
+ * Hadamard matrix, D: random +-1 diagonal, one sign per input channel).  At
+ * run time the same R is applied to the activations, so the layer computes
+ *     y[m][n] = sum_k What[n][k] * (R x[m])[k].
+ * Source: same card and section, paragraph on the random Hadamard transform;
+ * model card "24B0978 - Week 02 - Track 2, 40% target - Submission 01",
+ * section "Recipe" (rotation per weight block before quantisation).
+ *
+ * Conventions for every entry point:
+ *  - Pointers are device pointers unless the argument says "host".
+ *  - Every device pointer must be 16-byte aligned.
+ *  - fp16 values travel as uint16_t bit patterns (IEEE binary16).
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Work is enqueued asynchronously on it; nothing synchronises.
+ *  - The library never allocates or frees device memory and never copies
+ *    between host and device.  Buffers belong to the caller and must stay
+ *    valid until the enqueued work has finished.
+ *  - Arguments are checked on the host before anything is enqueued; a bad
+ *    argument returns a negative wq_status and wq_last_error() says why.
+ *    WQ_E_HIP reports a failed launch.  Faults inside a kernel surface as
+ *    errors of the caller's next synchronising HIP call.
+ *  - Calls are thread-safe.  Two calls that share a workspace must not run
+ *    concurrently (order them on one stream).
+ *
+ * Data layout in device memory (the cards fix none of it; this is the
+ * library's format):
+ *  - codes: output rows one after another; the codes of one row are
+ *    contiguous along K.  A row of K codes at b bits takes K*b/32 words.
+ *      int4: 8 codes per uint32, code j of a word in bits [4j, 4j+4);
+ *      int8: 4 codes per uint32, code j in byte j;
+ *      int3: 32 codes per 3 uint32, int6: 16 codes per 3 uint32; the three
+ *            words form the 96-bit little-endian integer w0|w1<<32|w2<<64
+ *            and code j of the run sits in bits [b*j, b*j+b).
+ *  - scales, zeros: fp16 [N][K/128], row-major.
+ *  - mixed width: rows are cut into blocks of 64; block i is coded at
+ *    block_bits[i] bits (6 or 8) with the layout above; blocks follow each
+ *    other with no padding; block i starts at word block_off[i], and
+ *    block_off[N/64] is the total word count.  Source: model card
+ *    "25M2111-Week02-Track2-40-Submission01", section "Method, selection,
+ *    and reproduction" (dense mixed-width codes in 64-row blocks with byte
+ *    selectors).
+ *  - rotation signs: uint32 [K/32] bit vector; bit (k & 31) of word (k >> 5)
+ *    set means d[k] = -1.
+ *  - activations x: fp16 [M][ldx] row-major, ldx >= K; outputs y: fp16 or
+ *    fp32 [M][ldy] row-major, ldy >= N.
+ */
+#ifndef WQ_H
+#define WQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum wq_status {
+  WQ_OK = 0,
+  WQ_E_ARG = -1,          /* null pointer, bad size or value */
+  WQ_E_UNSUPPORTED = -2,  /* valid request this library does not implement */
+  WQ_E_ALIGN = -3,        /* a pointer is not 16-byte aligned */
+  WQ_E_WORKSPACE = -4,    /* workspace missing or too small */
+  WQ_E_HIP = -5           /* the HIP runtime reported an error */
+} wq_status;
+
+typedef enum wq_dtype { WQ_F16 = 1, WQ_F32 = 2 } wq_dtype;
+
+/* wq_linear flag: rotate the activations (per 128-block, with the weight's
+ * signs) inside the product.  Without it, x is used as given. */
+#define WQ_FUSE_RHT 1u
+
+#define WQ_GROUP 128
+#define WQ_RHT_BLOCK 128
+#define WQ_MIXED_ROWS 64
+#define WQ_MAX_BATCH 8
+
+/* A quantised weight.  The struct itself is a host object; the arrays it
+ * points to are device arrays in the layout described above. */
+typedef struct wq_weight {
+  int32_t bits;                 /* 3, 4, 6 or 8; 0 = mixed 6/8 (block_bits) */
+  int32_t group;                /* must be 128 */
+  int64_t n;                    /* output rows */
+  int64_t k;                    /* input channels, a multiple of 128 */
+  const uint32_t *codes;        /* packed codes (wq_pack) */
+  const uint16_t *scales;       /* fp16 [n][k/128] */
+  const uint16_t *zeros;        /* fp16 [n][k/128]; any value, not only integers */
+  const uint8_t *block_bits;    /* mixed only: [n/64], each 6 or 8; else NULL */
+  const uint64_t *block_off;    /* mixed only: [n/64 + 1] word offsets; else NULL */
+  const uint32_t *rht_signs;    /* [k/32] sign bits, or NULL for no rotation */
+  int32_t rht_block;            /* 128 when rht_signs != NULL, else 0 */
+} wq_weight;
+
+/* Number of uint32 words wq_pack writes for an n x k code matrix.  For
+ * mixed width (bits == 0) pass the per-block widths in host memory; else
+ * pass NULL.  Returns 0 for an invalid request (see wq_last_error). */
+size_t wq_packed_words(int32_t bits, int64_t n, int64_t k, const uint8_t *block_bits_host);
+
+/* Offline weight preparation: rotate every row of w by R (if rht_signs is
+ * not NULL) in fp64, round the rotated weight to fp32, then quantise each
+ * group of 128 by round-to-nearest:
+ *   lo = min(min v, 0), hi = max(max v, 0),
+ *   s  = fp16((hi - lo) / qmax) (nearest, ties to even; 1 if it is 0),
+ *   z  = clamp(rint(-lo / s), 0, qmax), q = clamp(rint(v / s + z), 0, qmax),
+ * in fp64, rint rounding half to even, qmax = 2^bits - 1.  The cards name
+ * round-to-nearest for this format but give no formula; this is the
+ * library's reading.  Sources: "24B0978 - Week 02 - Track 2, 40% target",
+ * sections "Recipe" and "Recipe (exact)" (RTN, 8 bits, group 128; rotation
+ * applied per weight block before quantisation).
+ *   w          fp32 [n][k], read only
+ *   rht_signs  [k/32] sign bits or NULL
+ *   bits       3, 4, 6, 8, or 0 with block_bits (device, [n/64]) for mixed
+ *   codes      out: uint8 [n][k], one code per byte
+ *   scales     out: fp16 [n][k/128];  zeros: out fp16 [n][k/128] */
+wq_status wq_quantize(int32_t bits, int64_t n, int64_t k, const float *w,
+                      const uint32_t *rht_signs, const uint8_t *block_bits,
+                      uint8_t *codes, uint16_t *scales, uint16_t *zeros, void *stream);
+
+/* Pack one-code-per-byte codes (uint8 [n][k], each < 2^bits) into the code
+ * layout above.  packed must hold wq_packed_words(...) words.  For mixed
+ * width (bits == 0), block_bits is the device array [n/64] and block_off
+ * (device, [n/64 + 1]) receives the block word offsets; otherwise both are
+ * NULL.  Codes are not range-checked: bits above the width are dropped.
+ * Sources: "24B0978 - Week 01 - Track 2", paragraph on the absence of
+ * unstructured sparsity (dense packed codes with a regular stride);
+ * "24B0908 ... Mixed-precision GPTQ", section "CUDA speedup potential"
+ * (packed int3 read directly by the kernel). */
+wq_status wq_pack(int32_t bits, int64_t n, int64_t k, const uint8_t *codes,
+                  const uint8_t *block_bits, uint32_t *packed, uint64_t *block_off,
+                  void *stream);
+
+/* Inverse of wq_pack (a checking tool): packed words -> uint8 [n][k] codes.
+ * For mixed width pass block_bits and the block_off written by wq_pack. */
+wq_status wq_unpack(int32_t bits, int64_t n, int64_t k, const uint32_t *packed,
+                    const uint8_t *block_bits, const uint64_t *block_off,
+                    uint8_t *codes, void *stream);
+
+/* Block random Hadamard rotation of activations:
+ *   y[m][128j : 128j+128] = H . D_j . x[m][128j : 128j+128] / sqrt(128)
+ * computed as log2(128) = 7 butterfly stages of adds and subtracts in fp32,
+ * rounded once to fp16 (nearest even).  y may equal x (in place) when
+ * ldy == ldx.  Source: "24B0978 - Week 01 - Track 2", paragraph on the
+ * random Hadamard transform (fast Walsh-Hadamard transform on the
+ * activations at run time).
+ *   x  fp16 [m][ldx];  y  out fp16 [m][ldy];  signs  [k/32] sign bits
+ *   block must be 128; k a multiple of 128. */
+wq_status rht_apply(const uint16_t *x, uint16_t *y, const uint32_t *signs,
+                    int64_t m, int64_t k, int64_t ldx, int64_t ldy, int32_t block,
+                    void *stream);
+
+/* Bytes of workspace wq_linear needs for this weight and batch size m.
+ * 0 means none is needed.  Returns (size_t)-1 for an invalid request. */
+size_t wq_linear_workspace(const wq_weight *w, int64_t m);
+
+/* The layer: y[m][n] = sum_k (q[n][k] - z[n][g]) * s[n][g] * x'[m][k],
+ * g = k / 128, x' = R x[m] when flags has WQ_FUSE_RHT and w->rht_signs is
+ * set, else x' = x[m].  The scale is applied once per group to the group's
+ * partial sum and products accumulate in fp32 (source: "24B0978 - Week 01
+ * - Track 2", paragraph on group-wise affine integer quantisation).
+ * m <= 16 runs the dequantising GEMV; 17 <= m < 64 runs it in chunks of 16
+ * rows; m >= 64 runs the matrix-core GEMM (the weight is dequantised to
+ * fp16 in registers before the contraction).  The rotated activations are
+ * rounded to fp16 before the product.
+ *   w          host struct describing the device weight
+ *   x          fp16 [m][ldx]
+ *   y          out: fp16 or fp32 [m][ldy] (y_dtype)
+ *   workspace  device scratch of at least wq_linear_workspace(w, m) bytes.
+ *              It must be zero-filled once before its first use; every
+ *              call leaves it zero-filled again.
+ */
+wq_status wq_linear(const wq_weight *w, const uint16_t *x, int64_t m, int64_t ldx,
+                    void *y, wq_dtype y_dtype, int64_t ldy, uint32_t flags,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
+/* Several independent linears in one launch (up to WQ_MAX_BATCH), each with
+ * its own weight, activations and output, all at the same batch size m
+ * (m <= 16).  Same math, layout and workspace rules as wq_linear, applied to
+ * each w[i], x[i], y[i].  Arrays of length `count` are host arrays. */
+size_t wq_linear_batch_workspace(int32_t count, const wq_weight *w, int64_t m);
+wq_status wq_linear_batch(int32_t count, const wq_weight *w,
+                          const uint16_t *const *x, const int64_t *ldx, int64_t m,
+                          void *const *y, const wq_dtype *y_dtype, const int64_t *ldy,
+                          uint32_t flags, void *workspace, size_t workspace_bytes,
+                          void *stream);
+
+/* Message for the last failed call on this thread ("" if none). */
+const char *wq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WQ_H */

@@ -1,0 +1,154 @@
+"""The C ABI library: it loads, exports every symbol the header declares, and
+rejects bad arguments on the host before touching the GPU (CPU only).
+
+Only argument-checking paths are called here: each returns before any HIP
+call, so no GPU is needed.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import dequant_gemv_rht_amd as dq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wq.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^(?:wq_status|size_t|const char \*)\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(dq.LIB_PATH):
+        pytest.fail("libwq.so is not built: run python -m dequant_gemv_rht_amd.build")
+    return dq.lib()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ["wq_pack", "rht_apply", "wq_linear", "wq_quantize", "wq_unpack",
+                     "wq_linear_workspace", "wq_linear_batch", "wq_packed_words", "wq_last_error"]:
+        assert required in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert name in dq.SIGNATURES, f"binding lacks {name}"
+
+
+def test_binding_names_match_abi():
+    for name in ["wq_pack", "rht_apply", "wq_linear", "wq_quantize", "wq_unpack", "wq_linear_batch",
+                 "wq_linear_workspace", "wq_packed_words"]:
+        assert callable(getattr(dq, name)), name
+
+
+def test_packed_words(lib):
+    assert lib.wq_packed_words(4, 512, 1024, None) == 512 * 1024 // 8
+    assert lib.wq_packed_words(3, 10, 128, None) == 10 * 12
+    assert lib.wq_packed_words(6, 10, 128, None) == 10 * 24
+    assert lib.wq_packed_words(8, 10, 128, None) == 10 * 32
+    sel = (ctypes.c_uint8 * 3)(6, 8, 6)
+    assert lib.wq_packed_words(0, 192, 128, sel) == 64 * 24 + 64 * 32 + 64 * 24
+    assert lib.wq_packed_words(5, 10, 128, None) == 0
+    assert "bits=5" in lib.wq_last_error().decode()
+    assert lib.wq_packed_words(4, 10, 100, None) == 0
+    bad = (ctypes.c_uint8 * 1)(7)
+    assert lib.wq_packed_words(0, 64, 128, bad) == 0
+
+
+def _weight(**kw):
+    base = dict(bits=4, group=128, n=64, k=256, codes=16, scales=16, zeros=16, block_bits=None,
+                block_off=None, rht_signs=None, rht_block=0)
+    base.update(kw)
+    return dq.WqWeight(**base)
+
+
+@pytest.mark.parametrize("kw,status,text", [
+    (dict(bits=5), dq.WQ_E_UNSUPPORTED, "bits=5"),
+    (dict(group=64), dq.WQ_E_UNSUPPORTED, "group"),
+    (dict(k=200), dq.WQ_E_ARG, "multiple of 128"),
+    (dict(n=0), dq.WQ_E_ARG, "positive"),
+    (dict(codes=None), dq.WQ_E_ARG, "non-NULL"),
+    (dict(codes=8), dq.WQ_E_ALIGN, "aligned"),
+    (dict(bits=0, n=96), dq.WQ_E_ARG, "n % 64"),
+    (dict(bits=0), dq.WQ_E_ARG, "block_bits"),
+    (dict(rht_signs=16, rht_block=64), dq.WQ_E_UNSUPPORTED, "rht_block"),
+])
+def test_linear_rejects_bad_weights(lib, kw, status, text):
+    w = _weight(**kw)
+    st = lib.wq_linear(ctypes.byref(w), 16, 1, 256, 16, dq.WQ_F16, 64, 0, 16, 1 << 20, None)
+    assert st == status
+    assert text in lib.wq_last_error().decode()
+
+
+@pytest.mark.parametrize("args,status,text", [
+    (dict(m=0), dq.WQ_E_ARG, "m=0"),
+    (dict(x=None), dq.WQ_E_ARG, "non-NULL"),
+    (dict(x=24), dq.WQ_E_ALIGN, "aligned"),
+    (dict(ldx=100), dq.WQ_E_ARG, "ldx"),
+    (dict(ldx=260), dq.WQ_E_ALIGN, "multiple of 8"),
+    (dict(ldy=10), dq.WQ_E_ARG, "ldy"),
+    (dict(ydt=7), dq.WQ_E_ARG, "y_dtype"),
+    (dict(flags=2), dq.WQ_E_ARG, "flags"),
+    (dict(ws=0, m=64, signs=16, flags=1), dq.WQ_E_WORKSPACE, "workspace"),
+    (dict(ws=64 * 256, m=64, signs=16, flags=1), dq.WQ_E_WORKSPACE, "workspace"),
+])
+def test_linear_rejects_bad_io(lib, args, status, text):
+    a = dict(m=1, x=16, ldx=256, y=16, ydt=dq.WQ_F16, ldy=64, flags=0, ws=1 << 20, k=256, signs=None)
+    a.update(args)
+    w = _weight(k=a["k"], rht_signs=a["signs"], rht_block=128 if a["signs"] else 0)
+    st = lib.wq_linear(ctypes.byref(w), a["x"], a["m"], a["ldx"], a["y"], a["ydt"], a["ldy"], a["flags"],
+                       16, a["ws"], None)
+    assert st == status, lib.wq_last_error()
+    assert text in lib.wq_last_error().decode()
+
+
+def test_workspace_sizes(lib):
+    # the GEMV (m < 64) keeps its partial sums in LDS: no workspace at any K
+    assert lib.wq_linear_workspace(ctypes.byref(_weight()), 1) == 0
+    w = _weight(n=4096, k=2560, rht_signs=16, rht_block=128)
+    for m in (1, 16, 63):
+        assert lib.wq_linear_workspace(ctypes.byref(w), m) == 0
+    # the matrix-core path (m >= 64) stages the rotated activations, fp16 [m][k]
+    assert lib.wq_linear_workspace(ctypes.byref(w), 64) >= 64 * 2560 * 2
+    assert lib.wq_linear_workspace(ctypes.byref(w), 0) == ctypes.c_size_t(-1).value
+
+
+def test_other_entry_points_reject(lib):
+    assert lib.rht_apply(16, 16, 16, 1, 256, 256, 256, 64, None) == dq.WQ_E_UNSUPPORTED
+    assert lib.rht_apply(16, 16, 16, 1, 100, 256, 256, 128, None) == dq.WQ_E_ARG
+    assert lib.rht_apply(16, 16, 16, 1, 256, 264, 256, 128, None) == dq.WQ_E_ARG
+    assert lib.wq_pack(7, 4, 128, 16, None, 16, None, None) == dq.WQ_E_UNSUPPORTED
+    assert lib.wq_pack(0, 64, 128, 16, None, 16, None, None) == dq.WQ_E_ARG
+    assert lib.wq_unpack(4, 4, 128, None, None, None, 16, None) == dq.WQ_E_ARG
+    assert lib.wq_quantize(4, 4, 100, 16, None, None, 16, 16, 16, None) == dq.WQ_E_ARG
+    assert lib.wq_quantize(4, 4, 128, 16, 8, None, 16, 16, 16, None) == dq.WQ_E_ALIGN
+    arr = (dq.WqWeight * 2)(_weight(), _weight(bits=3))
+    xs = (ctypes.c_void_p * 2)(16, 16)
+    lds = (ctypes.c_int64 * 2)(256, 256)
+    ys = (ctypes.c_void_p * 2)(16, 16)
+    dts = (ctypes.c_int32 * 2)(dq.WQ_F16, dq.WQ_F16)
+    ldy = (ctypes.c_int64 * 2)(64, 64)
+    assert lib.wq_linear_batch(2, arr, xs, lds, 1, ys, dts, ldy, 0, 16, 1 << 20, None) == dq.WQ_E_UNSUPPORTED
+    assert "one code width" in lib.wq_last_error().decode()
+    assert lib.wq_linear_batch(9, arr, xs, lds, 1, ys, dts, ldy, 0, 16, 1 << 20, None) == dq.WQ_E_ARG
+    assert lib.wq_linear_batch(2, arr, xs, lds, 17, ys, dts, ldy, 0, 16, 1 << 20, None) == dq.WQ_E_UNSUPPORTED
+
+
+def test_matrix_core_path_workspace_covers_rotated_activations(lib):
+    # m >= 64 rotates the activations into the workspace before the product,
+    # so the workspace must hold fp16 [m][k] and a smaller one is refused
+    # before anything is launched.
+    w = _weight(n=256, k=2560, rht_signs=16, rht_block=128)
+    need = lib.wq_linear_workspace(ctypes.byref(w), 512)
+    assert need >= 512 * 2560 * 2
+    st = lib.wq_linear(ctypes.byref(w), 16, 512, 2560, 16, dq.WQ_F16, 256, dq.WQ_FUSE_RHT, 16, 16, None)
+    assert st == dq.WQ_E_WORKSPACE
+    assert "workspace" in lib.wq_last_error().decode()

@@ -1,0 +1,252 @@
+"""GPU parity: the HIP library against the CPU oracle on small and ragged
+shapes (several tiles, partial segments, odd batch sizes), through the C ABI.
+
+Integer work (packing, unpacking, quantised codes, scales and zeros) must
+match bit for bit; outputs must meet the tolerance in ``gpu_util``.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import dequant_gemv_rht_amd as dq
+import workloads as W
+from oracle import hadamard as OH
+from oracle import linear as OL
+from oracle import pack as OP
+from oracle import rtn as OR
+
+from gpu_util import check_close, dev, dev_u32, host_f16_bits, host_u32, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(n, k, m, seed, rht=True, std=0.02):
+    rng = np.random.default_rng(seed)
+    w = W.weight(k, n, rng, std=std)
+    x = W.activations(m, k, rng)
+    signs = W.sign_bits(k, rng) if rht else None
+    return w, x, signs
+
+
+# ---------------------------------------------------------------- packing
+
+@pytest.mark.parametrize("bits", [3, 4, 6, 8])
+def test_pack_unpack_bit_exact(bits):
+    say(f"pack bits={bits}")
+    rng = np.random.default_rng(bits)
+    n, k = 37, 384
+    q = rng.integers(0, 1 << bits, size=(n, k), dtype=np.uint8)
+    want = OP.pack(q, bits)
+    packed, off = dq.wq_pack(dev(q), bits)
+    torch.cuda.synchronize()
+    assert off is None
+    assert np.array_equal(host_u32(packed).reshape(n, -1), want)
+    back = dq.wq_unpack(dev_u32(want.ravel()), bits, n, k)
+    assert np.array_equal(back.cpu().numpy(), q)
+
+
+def test_pack_mixed_bit_exact():
+    say("pack mixed")
+    rng = np.random.default_rng(7)
+    sel = np.array([6, 8, 6, 8], np.uint8)
+    n, k = 256, 256
+    q = np.concatenate([rng.integers(0, 1 << int(b), size=(64, k), dtype=np.uint8) for b in sel])
+    want, want_off = OP.pack_mixed(q, sel)
+    packed, off = dq.wq_pack(dev(q), 0, dev(sel))
+    torch.cuda.synchronize()
+    assert np.array_equal(host_u32(packed), want)
+    assert np.array_equal(off.cpu().numpy().astype(np.uint64), want_off)
+    back = dq.wq_unpack(dev_u32(want), 0, n, k, dev(sel), off)
+    assert np.array_equal(back.cpu().numpy(), q)
+
+
+# ------------------------------------------------------------- quantiser
+
+@pytest.mark.parametrize("bits", [3, 4, 6, 8])
+@pytest.mark.parametrize("rht", [True, False])
+def test_quantize_bit_exact(bits, rht):
+    say(f"quantize bits={bits} rht={rht}")
+    w, _, signs = _inputs(40, 640, 1, 100 + bits, rht)
+    w[3, 128:256] = 0.0                      # an all-zero group
+    w[5, :128] = np.float32(0.37)            # a constant positive group
+    q, s, z = OR.prepare(w, signs, bits)
+    qg, sg, zg = dq.wq_quantize(dev(w), bits, dev_u32(signs) if rht else None)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_f16_bits(sg), s.view(np.uint16))
+    assert np.array_equal(host_f16_bits(zg), z.view(np.uint16))
+    assert np.array_equal(qg.cpu().numpy(), q)
+
+
+def test_quantize_mixed_bit_exact():
+    say("quantize mixed")
+    w, _, signs = _inputs(192, 512, 1, 55)
+    sel = np.array([8, 6, 8], np.uint8)
+    q, s, z = OR.prepare(w, signs, np.repeat(sel, 64))
+    qg, sg, zg = dq.wq_quantize(dev(w), 0, dev_u32(signs), dev(sel))
+    torch.cuda.synchronize()
+    assert np.array_equal(qg.cpu().numpy(), q)
+    assert np.array_equal(host_f16_bits(sg), s.view(np.uint16))
+    assert np.array_equal(host_f16_bits(zg), z.view(np.uint16))
+
+
+# -------------------------------------------------------------- rotation
+
+@pytest.mark.parametrize("m,k", [(1, 128), (5, 1024), (3, 9728)])
+def test_rht_apply(m, k):
+    say(f"rht m={m} k={k}")
+    rng = np.random.default_rng(k + m)
+    x = W.activations(m, k, rng)
+    signs = W.sign_bits(k, rng)
+    ref = OH.rht(x.astype(np.float64), signs)
+    y = dq.rht_apply(dev(x), dev_u32(signs)).cpu().numpy().astype(np.float64)
+    # one rounding to fp16 of a value computed in fp32: within one fp16 ulp
+    ulp = np.maximum(np.abs(ref), 2.0 ** -14) * 2.0 ** -10
+    assert np.all(np.abs(y - ref) <= ulp)
+
+
+def test_rht_apply_in_place_and_strided():
+    say("rht in place / strided")
+    rng = np.random.default_rng(3)
+    m, k, ld = 4, 512, 520
+    buf = W.activations(m, ld, rng)
+    signs = W.sign_bits(k, rng)
+    ref = OH.rht(buf[:, :k].astype(np.float64), signs)
+    t = dev(buf)
+    view = t[:, :k]
+    dq.lib()
+    st = dq.lib().rht_apply(view.data_ptr(), view.data_ptr(), dev_u32(signs).data_ptr(), m, k, ld, ld, 128,
+                            torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    out = t.cpu().numpy()
+    ulp = np.maximum(np.abs(ref), 2.0 ** -14) * 2.0 ** -10
+    assert np.all(np.abs(out[:, :k].astype(np.float64) - ref) <= ulp)
+    assert np.array_equal(out[:, k:], buf[:, k:])      # padding untouched
+
+
+# ----------------------------------------------------------------- linear
+
+def _gpu_weight(w, signs, bits, sel=None):
+    return dq.quantize_weight(dev(w), bits, dev_u32(signs) if signs is not None else None,
+                              dev(sel) if sel is not None else None)
+
+
+def _run_case(n, k, m, bits, rht, out_f32, seed):
+    w, x, signs = _inputs(n, k, m, seed, rht)
+    q, s, z = OR.prepare(w, signs, bits)
+    ref = OL.linear(q, s, z, x, signs)
+    qw = _gpu_weight(w, signs, bits)
+    y = dq.wq_linear(qw, dev(x), torch.float32 if out_f32 else torch.float16, fuse_rht=rht)
+    return check_close(y.float().cpu().numpy(), ref, f"n={n} k={k} m={m} bits={bits}")
+
+
+@pytest.mark.parametrize("bits", [3, 4, 6, 8])
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 8, 13, 16])
+def test_linear_bits_by_batch(bits, m):
+    say(f"linear bits={bits} m={m}")
+    _run_case(200, 1024, m, bits, True, False, 1000 * bits + m)
+
+
+@pytest.mark.parametrize("n,k", [(1, 128), (17, 384), (130, 2560), (64, 9728), (300, 640)])
+@pytest.mark.parametrize("rht", [True, False])
+@pytest.mark.parametrize("out_f32", [False, True])
+def test_linear_shapes(n, k, rht, out_f32):
+    say(f"linear n={n} k={k} rht={rht} f32={out_f32}")
+    _run_case(n, k, 3, 4, rht, out_f32, n + k)
+
+
+@pytest.mark.parametrize("m", [17, 40])
+def test_linear_batch_chunks(m):
+    say(f"linear chunked m={m}")
+    _run_case(96, 512, m, 4, True, False, m)
+
+
+@pytest.mark.parametrize("bits", [3, 4, 6, 8])
+def test_linear_trained_scales_and_zeros(bits):
+    say(f"linear trained s,z bits={bits}")
+    n, k, m = 150, 768, 2
+    w, x, signs = _inputs(n, k, m, 77 + bits)
+    q, s, z = OR.prepare(w, signs, bits)
+    s2, z2 = W.trained_scale_zero(s, z, np.random.default_rng(bits), (1 << bits) - 1)
+    assert np.any(z2.astype(np.float32) != np.round(z2.astype(np.float32)))
+    ref = OL.linear(q, s2, z2, x, signs)
+    packed, _ = dq.wq_pack(dev(q), bits)
+    qw = dq.QWeight(bits, n, k, packed, dev(s2), dev(z2), dev_u32(signs))
+    y = dq.wq_linear(qw, dev(x))
+    check_close(y.float().cpu().numpy(), ref, "trained s,z")
+
+
+@pytest.mark.parametrize("m", [1, 4])
+@pytest.mark.parametrize("rht", [True, False])
+def test_linear_mixed(m, rht):
+    say(f"linear mixed m={m} rht={rht}")
+    n, k = 320, 1024
+    w, x, signs = _inputs(n, k, m, 900 + m, rht)
+    sel = np.array([6, 8, 8, 6, 6], np.uint8)
+    q, s, z = OR.prepare(w, signs, np.repeat(sel, 64))
+    ref = OL.linear(q, s, z, x, signs)
+    qw = _gpu_weight(w, signs, 0, sel)
+    y = dq.wq_linear(qw, dev(x), fuse_rht=rht)
+    check_close(y.float().cpu().numpy(), ref, "mixed")
+
+
+def test_mixed_all_six_equals_uniform_six():
+    say("mixed all-6 == int6")
+    n, k = 128, 512
+    w, x, signs = _inputs(n, k, 1, 31)
+    sel = np.array([6, 6], np.uint8)
+    a = dq.wq_linear(_gpu_weight(w, signs, 0, sel), dev(x))
+    b = dq.wq_linear(_gpu_weight(w, signs, 6), dev(x))
+    assert torch.equal(a, b)
+
+
+def test_batch_call_matches_single_calls():
+    say("batch == single")
+    shapes = [(256, 2560), (64, 1024), (130, 4096)]
+    ws, xs, qs = [], [], []
+    for i, (n, k) in enumerate(shapes):
+        w, x, signs = _inputs(n, k, 4, 40 + i)
+        qs.append(_gpu_weight(w, signs, 4))
+        xs.append(dev(x))
+    singles = [dq.wq_linear(q, x) for q, x in zip(qs, xs)]
+    batch = dq.wq_linear_batch(qs, xs)
+    for a, b in zip(singles, batch):
+        assert torch.equal(a, b)
+
+
+def test_deterministic_and_workspace_left_zero():
+    say("determinism")
+    w, x, signs = _inputs(512, 4096, 2, 5)
+    qw = _gpu_weight(w, signs, 4)
+    ws = dq.new_workspace(dq.wq_linear_workspace(qw, 2))
+    xd = dev(x)
+    first = dq.wq_linear(qw, xd, workspace=ws)
+    for _ in range(5):
+        assert torch.equal(dq.wq_linear(qw, xd, workspace=ws), first)
+    torch.cuda.synchronize()
+    # fp32 partials may stay; the arrival counters (the tail) must be zero again
+    n_counter_bytes = (512 + 127) // 128 * 4
+    assert int(ws[-256:][:n_counter_bytes].count_nonzero()) == 0
+
+
+def test_graph_replay_matches_eager():
+    say("graph replay")
+    w, x, signs = _inputs(384, 2560, 1, 6)
+    qw = _gpu_weight(w, signs, 4)
+    xd = dev(x)
+    ws = dq.new_workspace(dq.wq_linear_workspace(qw, 1))
+    eager = dq.wq_linear(qw, xd, workspace=ws)
+    out = torch.empty_like(eager)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        dq.wq_linear(qw, xd, workspace=ws, out=out)   # warm up on the capture stream
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        dq.wq_linear(qw, xd, workspace=ws, out=out)
+    for _ in range(4):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager)
+        assert torch.equal(dq.wq_linear(qw, xd, workspace=ws), eager)
