@@ -104,7 +104,7 @@ constexpr int kMaxLds = 160 * 1024;
 
 // Persistent stream kernel plan: workgroups (one per CU) split among the
 // linears in proportion to their bytes; each gets an even number of rows.
-bool plan_stream(int count, const wq_weight *w, int64_t m, int *wg, int *rows_per_wg, int *lds) {
+bool plan_stream(int count, const wq_weight *w, int64_t m, int *wg, int *rows_per_wg, int *lds, bool *ring) {
   const int mt = mtile(m);
   if (w[0].bits == 0 || mt > 4) return false;
   const int ncu = device_cus();
@@ -145,14 +145,20 @@ bool plan_stream(int count, const wq_weight *w, int64_t m, int *wg, int *rows_pe
     ++sum;
   }
   *lds = 0;
+  int ring_lds = 0;
   for (int i = 0; i < count; ++i) {
     int64_t r = (w[i].n + wg[i] - 1) / wg[i];
     r = (r + 1) / 2 * 2;
     rows_per_wg[i] = (int)r;
     wg[i] = (int)((w[i].n + r - 1) / r);
-    const int need = wq::gemv_stream_lds_bytes(mt, w[i].k, (int)r);
+    const int need = wq::gemv_stream_lds_bytes(w[i].bits, mt, w[i].k, (int)r, false);
     if (need > *lds) *lds = need;
+    const int rneed = wq::gemv_stream_lds_bytes(w[i].bits, mt, w[i].k, (int)r, true);
+    if (rneed > ring_lds) ring_lds = rneed;
   }
+  // batch 1: stage the weights through the LDS ring whenever it fits
+  *ring = mt == 1 && ring_lds <= kMaxLds;
+  if (*ring) *lds = ring_lds;
   return *lds <= kMaxLds;
 }
 
@@ -176,7 +182,8 @@ wq_status run_gemv(int count, const wq_weight *w, const uint16_t *const *x, cons
   wq_weight ws[WQ_MAX_BATCH];
   for (int o = 0; o < count; ++o) ws[o] = w[order[o]];
   int wg[WQ_MAX_BATCH], rpw[WQ_MAX_BATCH], slds = 0;
-  const bool stream = plan_stream(count, ws, m, wg, rpw, &slds);
+  bool ring = false;
+  const bool stream = plan_stream(count, ws, m, wg, rpw, &slds, &ring);
   int64_t tiles = 0;
   int lds = 0;
   for (int o = 0; o < count; ++o) {
@@ -212,6 +219,7 @@ wq_status run_gemv(int count, const wq_weight *w, const uint16_t *const *x, cons
   a.tiles = (int32_t)tiles;
   if (stream) {
     a.lds_bytes = slds;
+    a.ring = ring ? 1 : 0;
     return hip_status(wq::launch_gemv_stream(w[0].bits, mtile(m), a, s), "wq_linear");
   }
   a.lds_bytes = lds;

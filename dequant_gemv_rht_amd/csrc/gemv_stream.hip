@@ -14,14 +14,17 @@
 // and each workgroup a contiguous range of rows.  A workgroup
 //   1. rotates its linear's activations for the whole K once into LDS (the
 //      rotation is paid once per workgroup, not once per tile);
-//   2. splits its (row pair, 512-wide K segment) tasks into 64 contiguous,
-//      equal runs, one per 16-lane DPP row;
-//   3. streams each run with D tasks of code, scale and zero loads in flight
-//      (raw buffer loads: out-of-range lanes read zero without memory
-//      traffic, so every load is issued on a straight-line path);
-//   4. accumulates consecutive segments of a row pair in registers, sums the
-//      16 lanes by DPP when the pair (or the run) ends, and leaves the
-//      partial in LDS at [row][first segment of the run piece];
+//   2. numbers its (row pair, 512-wide K segment) tasks row-pair-major and
+//      deals them out round-robin to its 64 16-lane DPP rows: at step i, DPP
+//      row g takes task 64 i + g, so each step the workgroup reads one
+//      contiguous run of its row block (two adjacent rows are adjacent in
+//      memory), which keeps DRAM pages open instead of scattering 128
+//      concurrent row streams per workgroup;
+//   3. keeps D steps of code loads in flight (raw buffer loads: out-of-range
+//      lanes read zero without memory traffic, so every load is issued on a
+//      straight-line path);
+//   4. sums each task's two row partials over the 16 lanes by DPP and leaves
+//      them in LDS at [row][segment];
 //   5. adds each row's partials in segment order (deterministic) and stores.
 //
 // Unpacking.  A code pair becomes two fp16 values (1024 + q) with one
@@ -272,8 +275,6 @@ __device__ __forceinline__ void stream_rows(const LinDesc &L, int m_valid, int r
   const int K = L.k, KS = (K + kSeg - 1) / kSeg, G = K / kGroup, S = K / kSlice;
   const int wpr = S * BITS;
   const int NP = (rows + 1) >> 1, T = NP * KS;
-  const int Tr = (T + kRG - 1) / kRG;       // tasks per DPP row
-  const int tb = min(T, rg * Tr), te = min(T, tb + Tr);
   const bool full = (K % kSeg) == 0;        // every lane's slice exists in every segment
   const StreamLds lay = stream_lds(MT, S, KS, G, NP);
   uint32_t *xp = smem;
@@ -314,22 +315,24 @@ __device__ __forceinline__ void stream_rows(const LinDesc &L, int m_valid, int r
     zr[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rz, off, 0, 0));
   }
 
-  // 2. the first D tasks of this DPP row's run
+  // 2. the first D steps of this DPP row's tasks: task = rg + 64 i
   const uint32_t seg_step = 16 * BITS * 4;                      // bytes per segment along a row
-  const uint32_t pair_step = (uint32_t)(2 * wpr * 4) - (uint32_t)KS * seg_step;
-  uint32_t co = __umul24((uint32_t)(tb / KS), (uint32_t)(2 * wpr * 4)) + (uint32_t)(tb % KS) * seg_step +
-                (uint32_t)j * (BITS * 4);
-  int is = tb % KS;
+  const uint32_t pair_bytes = (uint32_t)(2 * wpr * 4);
+  const int ds = kRG % KS, dp = kRG / KS;                       // task advance per step
+  const uint32_t dco = (uint32_t)dp * pair_bytes + (uint32_t)ds * seg_step;
+  const uint32_t wrap = pair_bytes - (uint32_t)KS * seg_step;   // extra bytes when the segment wraps
+  int is = rg % KS;
+  uint32_t co = __umul24((uint32_t)(rg / KS), pair_bytes) + (uint32_t)is * seg_step + (uint32_t)j * (BITS * 4);
   uint32_t cw[D][2][BITS];
 #pragma unroll
   for (int d = 0; d < D; ++d) {
-    const bool ok = tb + d < te && (full || is * 16 + j < S);
+    const bool ok = rg + kRG * d < T && (full || is * 16 + j < S);
     load_slice<BITS>(rc, ok ? co : kOOB, cw[d][0]);
     load_slice<BITS>(rc, ok ? co + wpr * 4 : kOOB, cw[d][1]);
-    co += seg_step;
-    if (++is == KS) { is = 0; co += pair_step; }
+    co += dco;
+    is += ds;
+    if (is >= KS) { is -= KS; co += wrap; }
   }
-
   // 3. scales and zeros into LDS as fp32, then the rotation
 #pragma unroll
   for (int q = 0; q < ZL; ++q) {
@@ -366,21 +369,15 @@ __device__ __forceinline__ void stream_rows(const LinDesc &L, int m_valid, int r
   }
   __syncthreads();
 
-  // 4. stream the run
+  // 4. stream the tasks
   const UnpackConsts uc = unpack_consts<BITS>();
-  float acc[2][MT];
-#pragma unroll
-  for (int r = 0; r < 2; ++r)
-#pragma unroll
-    for (int m = 0; m < MT; ++m) acc[r][m] = 0.f;
-  int cp = tb / KS, cs = tb % KS;   // task being computed
-  int sfirst = cs;
-
-  for (int i0 = 0; i0 < Tr; i0 += D) {
+  int cp = rg / KS, cs = rg % KS;   // task being computed
+  const int steps = (T + kRG - 1) / kRG;
+  for (int i0 = 0; i0 < steps; i0 += D) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      const int tau = tb + i0 + d;
-      if (tau < te) {
+      const int tau = rg + kRG * (i0 + d);
+      if (tau < T) {
         const int slice = cs * 16 + j;
         const bool sv = full || slice < S;
         const int sl = sv ? slice : 0;
@@ -389,6 +386,7 @@ __device__ __forceinline__ void stream_rows(const LinDesc &L, int m_valid, int r
         const float2 sz1 = *reinterpret_cast<const float2 *>(&szl[2 * (zi + G)]);
         const float sf[2] = {sv ? sz0.x : 0.f, sv ? sz1.x : 0.f};
         const float zf[2] = {sz0.y, sz1.y};
+        float acc[2][MT];
         // s * (sum (1024+q') x' - 1024 XS - z X) = s * sum (q - z) x
         if constexpr (MT <= 2) {
           // both rows' code pairs live, each activation slice read once
@@ -410,7 +408,7 @@ __device__ __forceinline__ void stream_rows(const LinDesc &L, int m_valid, int r
               float dd = 0.f;
 #pragma unroll
               for (int q = 0; q < 16; ++q) dd = dot2(pr[r][q], xv[q], dd);
-              acc[r][m] = fmaf(sf[r], fmaf(-zf[r], xq.x, dd - xq.y), acc[r][m]);
+              acc[r][m] = sf[r] * fmaf(-zf[r], xq.x, dd - xq.y);
             }
           }
         } else {
@@ -432,30 +430,30 @@ __device__ __forceinline__ void stream_rows(const LinDesc &L, int m_valid, int r
               float dd = 0.f;
 #pragma unroll
               for (int q = 0; q < 16; ++q) dd = dot2(pr[q], xv[q], dd);
-              acc[r][m] = fmaf(sf[r], fmaf(-zf[r], xq.x, dd - xq.y), acc[r][m]);
+              acc[r][m] = sf[r] * fmaf(-zf[r], xq.x, dd - xq.y);
             }
           }
         }
-        // the pair's last segment or the run's last task: flush
-        if (cs == KS - 1 || tau == te - 1) {
+        // the task's two row partials, summed over the 16 lanes
+        const uint32_t pb = __umul24((uint32_t)(2 * cp * KS + cs), (uint32_t)MT);
 #pragma unroll
-          for (int r = 0; r < 2; ++r)
+        for (int r = 0; r < 2; ++r)
 #pragma unroll
-            for (int m = 0; m < MT; ++m) {
-              const float v = row16_sum(acc[r][m]);
-              acc[r][m] = 0.f;
-              if (j == 0) part[__umul24((uint32_t)((2 * cp + r) * KS + sfirst), MT) + m] = v;
-            }
-          sfirst = (cs == KS - 1) ? 0 : cs + 1;
-        }
-        if (++cs == KS) { cs = 0; ++cp; }
+          for (int m = 0; m < MT; ++m) {
+            const float v = row16_sum(acc[r][m]);
+            if (j == 0) part[pb + r * KS * MT + m] = v;
+          }
+        cs += ds;
+        cp += dp;
+        if (cs >= KS) { cs -= KS; ++cp; }
       }
-      // refill this buffer with the task D ahead
-      const bool ok = tau + D < te && (full || is * 16 + j < S);
+      // refill this buffer with the task D steps ahead
+      const bool ok = tau + kRG * D < T && (full || is * 16 + j < S);
       load_slice<BITS>(rc, ok ? co : kOOB, cw[d][0]);
       load_slice<BITS>(rc, ok ? co + wpr * 4 : kOOB, cw[d][1]);
-      co += seg_step;
-      if (++is == KS) { is = 0; co += pair_step; }
+      co += dco;
+      is += ds;
+      if (is >= KS) { is -= KS; co += wrap; }
     }
   }
   __syncthreads();
@@ -467,6 +465,409 @@ __device__ __forceinline__ void stream_rows(const LinDesc &L, int m_valid, int r
     for (int s = 0; s < KS; ++s) sum += part[(row * KS + s) * MT + m];
     store_out(L, m, r0 + row, sum);
   }
+}
+
+// ---------------------------------------------------------------------------
+// Batch 1: the weight stream staged through an LDS ring.
+//
+// Codes travel from HBM to LDS by direct buffer-to-LDS loads, which hold no
+// registers while in flight, so R steps of every wave's tasks are
+// outstanding from the first instructions on: the workgroup's first steps
+// of weights stream in while its activations are still being fetched and
+// rotated.  Each wave owns its ring slots and reads back only what its own
+// lanes loaded (lane L's bytes land at slot + L * chunk), so a slot is ready
+// once the wave's own vector-load counter has drained past it; no barrier.
+// Scales and zeros travel the same way (lanes 0..3 of a task's 16 fetch the
+// task's 2 rows x 4 groups, two groups per 4-byte load).  The counter is
+// waited on explicitly: every step issues the same number of loads on a
+// straight-line path (out-of-range tasks read zero), so the count of loads
+// younger than a slot is a constant, and no register is loaded inside the
+// loop, so the compiler has no load of its own to wait for there.
+// ---------------------------------------------------------------------------
+
+// A row's BITS words per lane travel as direct loads of 16 or 4 bytes per
+// lane (lane L's bytes land at chunk + L * size): int3 3 x 4, int4 16,
+// int6 16 + 4 + 4, int8 16 + 16.  Chunk c covers words [word(c), word(c) +
+// size / 4) and sits at byte 64 * 4 * word(c) of the row's region.
+template <int BITS>
+struct Ring {
+  static constexpr int nc = BITS == 3 ? 3 : BITS == 4 ? 1 : BITS == 6 ? 3 : 2;   // loads per row
+  __host__ __device__ static constexpr int size(int c) { return BITS == 3 ? 4 : (BITS == 6 && c > 0) ? 4 : 16; }
+  __host__ __device__ static constexpr int word(int c) { return BITS == 3 ? c : BITS == 6 ? (c == 0 ? 0 : 3 + c) : 4 * c; }
+  static constexpr int row = 64 * 4 * BITS;                         // bytes per row per wave per step
+  static constexpr int codes = 2 * row;                             // code bytes per wave per step
+  static constexpr int slot = codes + 2 * 64 * 4;                   // + scales, zeros
+  static constexpr int depth = BITS == 3 ? 4 : BITS == 4 ? 3 : 2;  // steps in flight
+  static constexpr int q = 2 * nc + 2;                             // vector loads per wave per step
+};
+
+// Keeps the compiler from turning a select feeding a load's offset into a
+// branch around two copies of the load (which would change the load count).
+__device__ __forceinline__ uint32_t opaque(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
+
+// One row's direct loads of a step: chunk c of every lane to its region.
+template <int BITS, int C = 0>
+__device__ __forceinline__ void ring_row_loads(rsrc_t rc, uint8_t *row, bool ok, uint32_t off) {
+  using RS = Ring<BITS>;
+#if defined(__HIP_DEVICE_COMPILE__)   // 16-byte LDS loads exist only in the gfx950 pass
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (lds_ptr_t)(row + 256 * RS::word(C)), RS::size(C),
+                                           opaque(ok ? off + 4 * RS::word(C) : kOOB), 0, 0, kNT);
+#endif
+  if constexpr (C + 1 < RS::nc) ring_row_loads<BITS, C + 1>(rc, row, ok, off);
+}
+
+// Load-side position of a 16-lane task row in its workgroup's task list
+// (task lt = (row pair, segment ls)), and the step issue into ring slot d.
+template <int BITS, bool FULL>
+struct RingCursor {
+  using RS = Ring<BITS>;
+  rsrc_t rc, rsc, rz;
+  uint8_t *ring;
+  int wave, j, T, S, KS, wpr, ds;
+  uint32_t dco, wco;
+  int dso, wso;
+  int lt, ls;
+  uint32_t lco;   // byte offset of this lane's code words, row 0 of the task
+  int lso;        // byte offset of the scale/zero pair this lane fetches (lanes 0..3)
+
+  __device__ __forceinline__ void issue(int d) {
+    const bool ok = lt < T && (FULL || ls * 16 + j < S);
+    uint8_t *slot = ring + (d * (kStreamThreads / 64) + wave) * RS::slot;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) ring_row_loads<BITS>(rc, slot + r * RS::row, ok, lco + r * wpr * 4);
+    const bool oks = lt < T && j < 4 && (FULL || ls * 16 + 8 * (j & 1) < S);
+    const uint32_t so = opaque(oks ? (uint32_t)lso : kOOB);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsc, (lds_ptr_t)(slot + RS::codes), 4, so, 0, 0, kNT);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rz, (lds_ptr_t)(slot + RS::codes + 256), 4, so, 0, 0, kNT);
+    lt += kRG;
+    lco += dco;
+    lso += dso;
+    ls += ds;
+    if (ls >= KS) {
+      ls -= KS;
+      lco += wco;
+      lso += wso;
+    }
+  }
+};
+
+// LDS layout of a ring workgroup, in bytes.
+struct RingLds {
+  int xs, part, ring, total;
+};
+
+__host__ __device__ inline RingLds ring_lds(int S, int KS, int np, int slot, int depth) {
+  RingLds l;
+  l.xs = S * kSliceStride * 4;                      // activations: [S][20] u32
+  l.part = l.xs + S * 8;                            // slice sums: [S][2] f32
+  l.ring = (l.part + 2 * np * KS * 4 + 15) & ~15;   // partials: [2np][KS] f32
+  l.total = l.ring + depth * (kStreamThreads / 64) * slot;
+  return l;
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Wait until at most n * Q vector loads are outstanding (n < R, uniform).
+template <int R, int Q>
+__device__ __forceinline__ void wait_vmcnt_younger(int n) {
+  if constexpr (R > 3) {
+    if (n >= 3) { wait_vmcnt<3 * Q>(); return; }
+  }
+  if constexpr (R > 2) {
+    if (n == 2) { wait_vmcnt<2 * Q>(); return; }
+  }
+  if (n == 1) { wait_vmcnt<Q>(); return; }
+  wait_vmcnt<0>();
+}
+
+__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(lds_ptr_t)p;
+}
+
+// A task's LDS operands, read in one asm statement that also waits for
+// them: the activation slice (4 x 16 bytes) and its two sums, the scales and
+// zeros of the lane's group (rows 0, 1), and the lane's code words of both
+// rows from the ring slot.  Keeping these reads out of the compiler's view
+// keeps it from tying them to the ring's direct loads with waits of its own.
+struct TaskOps {
+  u32x4 x[4];
+  uint64_t xq;   // the slice's two sums (a 64-bit scalar: a two-element vector output is not bound as a pair)
+  uint32_t s0, s1, z0, z1;
+};
+
+template <int BITS>
+__device__ __forceinline__ void read_task(uint32_t xa, uint32_t xsa, uint32_t sza, uint32_t ca16, uint32_t ca4,
+                                          TaskOps &o, uint32_t (&w)[2][BITS]) {
+#define WQ_OPS_READS                    \
+  "ds_read_b128 %[x0], %[xa]\n\t"       \
+  "ds_read_b128 %[x1], %[xa] offset:16\n\t" \
+  "ds_read_b128 %[x2], %[xa] offset:32\n\t" \
+  "ds_read_b128 %[x3], %[xa] offset:48\n\t" \
+  "ds_read_b64 %[xq], %[xsa]\n\t"       \
+  "ds_read_u16 %[s0], %[sza]\n\t"       \
+  "ds_read_u16 %[s1], %[sza] offset:8\n\t" \
+  "ds_read_u16 %[z0], %[sza] offset:256\n\t" \
+  "ds_read_u16 %[z1], %[sza] offset:264\n\t"
+#define WQ_OPS_OUT                                                                                      \
+  [x0] "=&v"(o.x[0]), [x1] "=&v"(o.x[1]), [x2] "=&v"(o.x[2]), [x3] "=&v"(o.x[3]), [xq] "=&v"(o.xq),     \
+      [s0] "=&v"(o.s0), [s1] "=&v"(o.s1), [z0] "=&v"(o.z0), [z1] "=&v"(o.z1)
+#define WQ_OPS_IN [xa] "v"(xa), [xsa] "v"(xsa), [sza] "v"(sza), [ca16] "v"(ca16), [ca4] "v"(ca4)
+  if constexpr (BITS == 4) {
+    // row r: 16 bytes at r * 1024 + 16 L
+    u32x4 c0, c1;
+    asm volatile(WQ_OPS_READS
+                 "ds_read_b128 %[c0], %[ca16]\n\t"
+                 "ds_read_b128 %[c1], %[ca16] offset:1024\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : WQ_OPS_OUT, [c0] "=&v"(c0), [c1] "=&v"(c1)
+                 : WQ_OPS_IN
+                 : "memory");
+    w[0][0] = c0.x; w[0][1] = c0.y; w[0][2] = c0.z; w[0][3] = c0.w;
+    w[1][0] = c1.x; w[1][1] = c1.y; w[1][2] = c1.z; w[1][3] = c1.w;
+  } else if constexpr (BITS == 8) {
+    // row r: words 0..3 at r * 2048 + 16 L, words 4..7 at r * 2048 + 1024 + 16 L
+    u32x4 c0, c1, c2, c3;
+    asm volatile(WQ_OPS_READS
+                 "ds_read_b128 %[c0], %[ca16]\n\t"
+                 "ds_read_b128 %[c1], %[ca16] offset:1024\n\t"
+                 "ds_read_b128 %[c2], %[ca16] offset:2048\n\t"
+                 "ds_read_b128 %[c3], %[ca16] offset:3072\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : WQ_OPS_OUT, [c0] "=&v"(c0), [c1] "=&v"(c1), [c2] "=&v"(c2), [c3] "=&v"(c3)
+                 : WQ_OPS_IN
+                 : "memory");
+    w[0][0] = c0.x; w[0][1] = c0.y; w[0][2] = c0.z; w[0][3] = c0.w;
+    w[0][4] = c1.x; w[0][5] = c1.y; w[0][6] = c1.z; w[0][7] = c1.w;
+    w[1][0] = c2.x; w[1][1] = c2.y; w[1][2] = c2.z; w[1][3] = c2.w;
+    w[1][4] = c3.x; w[1][5] = c3.y; w[1][6] = c3.z; w[1][7] = c3.w;
+  } else if constexpr (BITS == 3) {
+    // row r: word k at r * 768 + 256 k + 4 L
+    uint32_t c[6];
+    asm volatile(WQ_OPS_READS
+                 "ds_read_b32 %[c0], %[ca4]\n\t"
+                 "ds_read_b32 %[c1], %[ca4] offset:256\n\t"
+                 "ds_read_b32 %[c2], %[ca4] offset:512\n\t"
+                 "ds_read_b32 %[c3], %[ca4] offset:768\n\t"
+                 "ds_read_b32 %[c4], %[ca4] offset:1024\n\t"
+                 "ds_read_b32 %[c5], %[ca4] offset:1280\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : WQ_OPS_OUT, [c0] "=&v"(c[0]), [c1] "=&v"(c[1]), [c2] "=&v"(c[2]), [c3] "=&v"(c[3]),
+                   [c4] "=&v"(c[4]), [c5] "=&v"(c[5])
+                 : WQ_OPS_IN
+                 : "memory");
+#pragma unroll
+    for (int e = 0; e < 3; ++e) {
+      w[0][e] = c[e];
+      w[1][e] = c[3 + e];
+    }
+  } else {
+    // int6 row r: words 0..3 at r * 1536 + 16 L, word 4 at r * 1536 + 1024 + 4 L,
+    // word 5 at r * 1536 + 1280 + 4 L
+    u32x4 c0, c1;
+    uint32_t d0, d1, d2, d3;
+    asm volatile(WQ_OPS_READS
+                 "ds_read_b128 %[c0], %[ca16]\n\t"
+                 "ds_read_b32 %[d0], %[ca4] offset:1024\n\t"
+                 "ds_read_b32 %[d1], %[ca4] offset:1280\n\t"
+                 "ds_read_b128 %[c1], %[ca16] offset:1536\n\t"
+                 "ds_read_b32 %[d2], %[ca4] offset:2560\n\t"
+                 "ds_read_b32 %[d3], %[ca4] offset:2816\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : WQ_OPS_OUT, [c0] "=&v"(c0), [c1] "=&v"(c1), [d0] "=&v"(d0), [d1] "=&v"(d1), [d2] "=&v"(d2),
+                   [d3] "=&v"(d3)
+                 : WQ_OPS_IN
+                 : "memory");
+    w[0][0] = c0.x; w[0][1] = c0.y; w[0][2] = c0.z; w[0][3] = c0.w; w[0][4] = d0; w[0][5] = d1;
+    w[1][0] = c1.x; w[1][1] = c1.y; w[1][2] = c1.z; w[1][3] = c1.w; w[1][4] = d2; w[1][5] = d3;
+  }
+#undef WQ_OPS_READS
+#undef WQ_OPS_OUT
+#undef WQ_OPS_IN
+}
+
+__device__ __forceinline__ void lds_store(uint32_t addr, float v) {
+  asm volatile("ds_write_b32 %0, %1" ::"v"(addr), "v"(v) : "memory");
+}
+
+// Marks loaded registers as consumed on every path, so that no load issued
+// before the ring loop is still outstanding in the compiler's bookkeeping
+// when the loop starts (it would otherwise drain all vector loads there).
+__device__ __forceinline__ void consume(u32x4 a, uint32_t b) { asm volatile("" ::"v"(a), "v"(b)); }
+
+// Workgroup barrier for LDS data only: waits for this wave's LDS accesses,
+// not for its vector loads (the ring's loads stay in flight across it).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <int BITS, bool FULL>
+__device__ __forceinline__ void stream_ring(const LinDesc &L, int r0, int rows, uint32_t *smem) {
+  using RS = Ring<BITS>;
+  constexpr int R = RS::depth, Q = RS::q;
+  constexpr int XC = 2;
+  const int t = threadIdx.x, rg = t >> 4, j = t & 15, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int K = L.k, KS = (K + kSeg - 1) / kSeg, G = K / kGroup, S = K / kSlice;
+  const int wpr = S * BITS;
+  const int NP = (rows + 1) >> 1, T = NP * KS;
+  const RingLds lay = ring_lds(S, KS, NP, RS::slot, R);
+  uint8_t *lds = reinterpret_cast<uint8_t *>(smem);
+  uint32_t *xp = smem;
+  float *xs = reinterpret_cast<float *>(lds + lay.xs);
+  float *part = reinterpret_cast<float *>(lds + lay.part);
+  uint8_t *ring = lds + lay.ring;
+
+  const rsrc_t rc = make_rsrc(L.codes + (size_t)r0 * wpr, (uint32_t)rows * wpr * 4);
+  // scale/zero ranges rounded up to the 4-byte loads: the extra bytes share
+  // the last valid 4-byte granule and only feed lanes that are masked off
+  const uint32_t szb = ((uint32_t)rows * G * 2 + 3u) & ~3u;
+  const rsrc_t rsc = make_rsrc(L.scales + (size_t)r0 * G, szb);
+  const rsrc_t rz = make_rsrc(L.zeros + (size_t)r0 * G, szb);
+  const rsrc_t rx = make_rsrc(L.x, (uint32_t)K * 2);
+  const rsrc_t rsg = make_rsrc(L.signs, L.signs ? (uint32_t)(K / 8) : 0u);
+  const bool rotate = L.signs != nullptr;
+
+  // 1. activations and signs first
+  const int nb = K / kGroup, items = nb;
+  u32x4 xr[XC];
+  uint32_t sw[XC];
+#pragma unroll
+  for (int q = 0; q < XC; ++q) {
+    uint32_t xo, so;
+    item_offsets<1>(L, nb, items, rg + kRG * q, j, xo, so);
+    xr[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, xo, 0, 0));
+    sw[q] = rotate ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsg, so, 0, 0) : 0u;
+  }
+
+  // 2. the first R steps of the weight stream.  Task tau = rg + 64 i is
+  //    (row pair tau / KS, segment tau % KS); load-side position below.
+  const uint32_t seg_step = 16 * BITS * 4;
+  const uint32_t pair_bytes = (uint32_t)(2 * wpr * 4);
+  const int ds = kRG % KS, dp = kRG / KS;
+  const uint32_t dco = (uint32_t)dp * pair_bytes + (uint32_t)ds * seg_step;
+  const uint32_t wco = pair_bytes - (uint32_t)KS * seg_step;
+  const int dso = 2 * (2 * dp * G + 4 * ds), wso = 2 * (2 * G - 4 * KS);
+  RingCursor<BITS, FULL> cur;
+  cur.rc = rc; cur.rsc = rsc; cur.rz = rz;
+  cur.ring = ring; cur.wave = wave; cur.j = j; cur.T = T; cur.S = S; cur.KS = KS; cur.wpr = wpr;
+  cur.ds = ds; cur.dco = dco; cur.wco = wco; cur.dso = dso; cur.wso = wso;
+  cur.lt = rg;
+  cur.ls = rg % KS;
+  cur.lco = (uint32_t)(rg / KS) * pair_bytes + (uint32_t)cur.ls * seg_step + (uint32_t)j * (BITS * 4);
+  // lanes j < 4 fetch scales/zeros of row 2p + (j >> 1), groups 4s + 2(j & 1) + {0, 1}
+  cur.lso = 2 * (2 * (rg / KS) * G + 4 * cur.ls) + (j >> 1) * 2 * G + (j & 1) * 4;
+  const int steps = (T + kRG - 1) / kRG;   // steps of this workgroup (uniform)
+#pragma unroll
+  for (int d = 0; d < R; ++d)
+    if (d < steps) cur.issue(d);
+
+  // 3. rotation into LDS
+#pragma unroll
+  for (int q = 0; q < XC; ++q) {
+    consume(xr[q], sw[q]);
+    rotate_item<BITS, 1>(rotate, xr[q], sw[q], nb, items, rg + kRG * q, j, xp, xs, S);
+  }
+  for (int it0 = kRG * XC; it0 < items; it0 += kRG) {
+    uint32_t xo, so;
+    item_offsets<1>(L, nb, items, it0 + rg, j, xo, so);
+    const u32x4 raw = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, xo, 0, 0));
+    const uint32_t w1 = rotate ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsg, so, 0, 0) : 0u;
+    consume(raw, w1);
+    rotate_item<BITS, 1>(rotate, raw, w1, nb, items, it0 + rg, j, xp, xs, S);
+  }
+  lds_barrier();
+
+  // 4. consume the ring
+  const UnpackConsts uc = unpack_consts<BITS>();
+  const uint32_t xa0 = lds_addr(xp), xsa0 = lds_addr(xs), parta0 = lds_addr(part);
+  int cp = rg / KS, cs = rg % KS;   // task being computed
+  for (int i = 0; i < steps; ++i) {
+    const int d = i % R;
+    {
+      // wait for step i; the loads of steps i+1 .. min(i+R, steps)-1 may stay in flight
+      const int younger = min(R - 1, steps - 1 - i);
+      wait_vmcnt_younger<R, Q>(younger);
+      if (rg + kRG * i < T) {
+        const uint8_t *slot = ring + (d * (kStreamThreads / 64) + wave) * RS::slot;
+        const int slice = cs * 16 + j;
+        const bool sv = FULL || slice < S;
+        const int sl = sv ? slice : 0;
+        TaskOps o;
+        uint32_t cw[2][BITS];
+        // scales/zeros of this lane's group (rows 0, 1) were fetched by lanes
+        // 0..3 of its task: 4 bytes each at task * 64 + 4 * (2 row + group / 2)
+        read_task<BITS>(xa0 + sl * (kSliceStride * 4), xsa0 + sl * 8,
+                        lds_addr(slot + RS::codes + (lane & 48) * 4 + (j >> 2) * 2), lds_addr(slot) + lane * 16,
+                        lds_addr(slot) + lane * 4, o, cw);
+        uint32_t xv[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          xv[4 * q + 0] = o.x[q].x; xv[4 * q + 1] = o.x[q].y; xv[4 * q + 2] = o.x[q].z; xv[4 * q + 3] = o.x[q].w;
+        }
+        const float xsum = __builtin_bit_cast(float, (uint32_t)o.xq), xoff = __builtin_bit_cast(float, (uint32_t)(o.xq >> 32));
+        const float sc[2] = {half_bits_to_float(o.s0), half_bits_to_float(o.s1)};
+        const float zc[2] = {half_bits_to_float(o.z0), half_bits_to_float(o.z1)};
+        float a[2];
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          uint32_t pr[16];
+          unpack_pairs<BITS>(cw[r], uc, pr);
+          // s * (sum (1024+q') x' - 1024 XS - z X) = s * sum (q - z) x
+          float dd = fmaf(-zc[r], xsum, -xoff);
+#pragma unroll
+          for (int q = 0; q < 16; ++q) dd = dot2(pr[q], xv[q], dd);
+          a[r] = (sv ? sc[r] : 0.f) * dd;
+        }
+        // both rows summed over the 16 lanes at once: after the first
+        // exchange, even lanes carry row 0 and odd lanes row 1
+        const bool odd = j & 1;
+        float v = (odd ? a[1] : a[0]) + dpp<kQuadXor1>(odd ? a[0] : a[1]);
+        v += dpp<kQuadXor2>(v);
+        v += dpp<kRowRor4>(v);
+        v += dpp<kRowRor8>(v);
+        if (j < 2) lds_store(parta0 + ((2 * cp + j) * KS + cs) * 4, v);
+        cs += ds;
+        cp += dp;
+        if (cs >= KS) {
+          cs -= KS;
+          ++cp;
+        }
+      }
+      wait_lgkm0();   // this slot's bytes are in registers before it is refilled
+      if (i + R < steps) cur.issue(d);
+    }
+  }
+  wait_vmcnt<0>();    // no load may still be writing LDS when the workgroup ends
+  __syncthreads();
+
+  // 5. add each row's partials in segment order, store
+  for (int e = t; e < rows; e += kStreamThreads) {
+    float sum = 0.f;
+    for (int s = 0; s < KS; ++s) sum += part[e * KS + s];
+    store_out(L, 0, r0 + e, sum);
+  }
+}
+
+template <int BITS, bool FULL>
+__global__ __launch_bounds__(kStreamThreads) void gemv_ring_kernel(GemvArgs a) {
+  extern __shared__ uint32_t smem[];
+  const int w = blockIdx.x;
+  int l = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxBatch; ++i)
+    if (i < a.count && w >= a.lin[i].tile_begin) l = i;
+  const LinDesc L = select_desc<LinDesc>(a, l);
+  const int r0 = (w - L.tile_begin) * L.rows_per_wg;
+  if (r0 >= L.n) return;
+  stream_ring<BITS, FULL>(L, r0, min(L.rows_per_wg, L.n - r0), smem);
 }
 
 // Tasks (two code loads each) a lane keeps in flight.  A 1024-thread
@@ -495,6 +896,16 @@ __global__ __launch_bounds__(kStreamThreads) void gemv_stream_kernel(GemvArgs a)
 
 template <int BITS>
 hipError_t launch_bits(int mt, const GemvArgs &a, hipStream_t s) {
+  if (a.ring) {
+    if (mt != 1) return hipErrorInvalidValue;
+    bool full = true;
+    for (int i = 0; i < a.count; ++i) full = full && a.lin[i].k % kSeg == 0;
+    if (full)
+      hipLaunchKernelGGL((gemv_ring_kernel<BITS, true>), dim3(a.tiles), dim3(kStreamThreads), a.lds_bytes, s, a);
+    else
+      hipLaunchKernelGGL((gemv_ring_kernel<BITS, false>), dim3(a.tiles), dim3(kStreamThreads), a.lds_bytes, s, a);
+    return hipGetLastError();
+  }
   switch (mt) {
     case 1:
       hipLaunchKernelGGL((gemv_stream_kernel<BITS, 1>), dim3(a.tiles), dim3(kStreamThreads), a.lds_bytes, s, a);
@@ -513,11 +924,19 @@ hipError_t launch_bits(int mt, const GemvArgs &a, hipStream_t s) {
 
 }  // namespace
 
-int gemv_stream_lds_bytes(int mt, int64_t k, int rows_per_wg) {
+int gemv_stream_lds_bytes(int bits, int mt, int64_t k, int rows_per_wg, bool ring) {
   const int64_t S = k / kSlice, KS = (k + kSeg - 1) / kSeg, G = k / kGroup;
   const int64_t np = (rows_per_wg + 1) / 2;
   if (S * kSliceStride * mt + np * (KS + G) * 2 * mt > (int64_t)1 << 26) return 1 << 30;
-  return stream_lds(mt, (int)S, (int)KS, (int)G, (int)np).total * 4;
+  if (!ring) return stream_lds(mt, (int)S, (int)KS, (int)G, (int)np).total * 4;
+  if (mt != 1) return 1 << 30;
+  switch (bits) {
+    case 3: return ring_lds((int)S, (int)KS, (int)np, Ring<3>::slot, Ring<3>::depth).total;
+    case 4: return ring_lds((int)S, (int)KS, (int)np, Ring<4>::slot, Ring<4>::depth).total;
+    case 6: return ring_lds((int)S, (int)KS, (int)np, Ring<6>::slot, Ring<6>::depth).total;
+    case 8: return ring_lds((int)S, (int)KS, (int)np, Ring<8>::slot, Ring<8>::depth).total;
+  }
+  return 1 << 30;
 }
 
 hipError_t launch_gemv_stream(int bits, int mt, const GemvArgs &a, hipStream_t s) {

@@ -45,6 +45,7 @@ struct GemvArgs {
   int32_t m;                    // batch rows actually present (<= MT)
   int32_t tiles;                // total workgroups
   int32_t lds_bytes;            // dynamic LDS per workgroup
+  int32_t ring;                 // stream kernel, batch 1: weights staged through an LDS ring
 };
 
 // Host-side launchers (gemv*.hip).  `bits` 0 = mixed.  mt = 1,2,4,8,16.
@@ -53,7 +54,8 @@ hipError_t launch_gemv(int bits, int mt, const GemvArgs &a, hipStream_t s);
 // width, batch tile <= 4, the linear's whole rotated K range in LDS.
 constexpr int kStreamThreads = 1024;
 hipError_t launch_gemv_stream(int bits, int mt, const GemvArgs &a, hipStream_t s);
-int gemv_stream_lds_bytes(int mt, int64_t k, int rows_per_wg);
+// LDS bytes of one stream workgroup; ring = batch-1 kernel with the LDS ring
+int gemv_stream_lds_bytes(int bits, int mt, int64_t k, int rows_per_wg, bool ring);
 void gemv_shape(int bits, int mt, int64_t k, int &mode, int &rows);
 int gemv_chunk(int mt, int64_t k);              // K per LDS chunk
 int gemv_lds_bytes(int mt, int chunk, int rows, int64_t k);
@@ -108,6 +110,7 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *p, uint32_t bytes) {
 constexpr int kQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
 constexpr int kQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
 constexpr int kQuadRev = 0x1B;       // quad_perm [3,2,1,0]  (lane ^ 3)
+constexpr int kRowRor4 = 0x124;      // row_ror:4            (lane + 4 mod 16 in a row)
 constexpr int kRowRor8 = 0x128;      // row_ror:8            (lane ^ 8 in a row)
 constexpr int kRowMirror = 0x140;    // lane ^ 15 in a row
 constexpr int kRowHalfMirror = 0x141; // lane ^ 7 within 8 lanes

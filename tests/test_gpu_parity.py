@@ -191,13 +191,20 @@ def test_linear_mixed(m, rht):
 
 
 def test_mixed_all_six_equals_uniform_six():
+    # At m = 2 the mixed-width and uniform kernels share the arithmetic and
+    # its order, so all-6-bit blocks must give the uniform int6 result bit
+    # for bit.  At m = 1 the uniform path stages weights through LDS and sums
+    # in another order: there both are held to the oracle.
     say("mixed all-6 == int6")
     n, k = 128, 512
-    w, x, signs = _inputs(n, k, 1, 31)
+    w, x, signs = _inputs(n, k, 2, 31)
     sel = np.array([6, 6], np.uint8)
-    a = dq.wq_linear(_gpu_weight(w, signs, 0, sel), dev(x))
-    b = dq.wq_linear(_gpu_weight(w, signs, 6), dev(x))
-    assert torch.equal(a, b)
+    mixed, uni = _gpu_weight(w, signs, 0, sel), _gpu_weight(w, signs, 6)
+    assert torch.equal(dq.wq_linear(mixed, dev(x)), dq.wq_linear(uni, dev(x)))
+    q, s, z = OR.prepare(w, signs, 6)
+    ref = OL.linear(q, s, z, x[:1], signs)
+    for qw in (mixed, uni):
+        check_close(dq.wq_linear(qw, dev(x[:1])).float().cpu().numpy(), ref, "all-6 m=1")
 
 
 def test_batch_call_matches_single_calls():
