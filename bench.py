@@ -65,11 +65,33 @@ def algorithmic_bytes(lins, m: int) -> int:
 
 
 def source_digest() -> str:
+    """Digest of the sources that decide the measured kernel and its launch."""
     h = hashlib.sha256()
-    for f in ("gemv.hip", "wq_internal.h"):
+    for f in ("gemv_stream.hip", "gemv.hip", "wq_internal.h", "api.cpp"):
         with open(os.path.join(ROOT, "dequant_gemv_rht_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+def calibrate_copy(nbytes: int, reps: int) -> None:
+    """A plain device copy of known size (read nbytes, write nbytes), for
+    scaling the FETCH_SIZE / WRITE_SIZE counters of a profiled run."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "copy", "bytes_read": nbytes, "bytes_written": nbytes, "reps": reps}),
+          flush=True)
+
+
+def kernel_name(bits: int, m: int) -> str:
+    """The kernel one step launches (the planner's choice for these shapes)."""
+    if m == 1:
+        return f"gemv_ring_kernel<{bits}, true> (LDS-ring weight stream)"
+    return f"gemv_stream_kernel<{bits}, {1 if m == 1 else 2 if m == 2 else 4}> (register prefetch)"
 
 
 def cpu_baseline(wl, lins, m, budget_s: float):
@@ -112,6 +134,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pool-bytes", type=int, default=POOL_BYTES)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run a plain copy of BYTES (for counter calibration) and exit")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -127,6 +151,9 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy, max(1, args.steps))
+        return
     dq.lib()  # fail loudly if the library is missing
 
     wl = W.WORKLOADS[args.workload]
@@ -184,7 +211,11 @@ def main():
     ms_total = t0.elapsed_time(t1)
     ms_per_step = ms_total / args.steps
 
-    # ---- per-launch kernel duration: events around single launches
+    # ---- per-launch duration of the dominant kernel: a step is exactly one
+    # launch of it, so the timed region over K steps gives it directly (events
+    # recorded on the launch stream).  Single eager launches bracketed by
+    # events are reported beside it for context.
+    launch_ms = ms_per_step
     n_single = max(50, copies * 3)
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_single)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(n_single)]
@@ -195,7 +226,6 @@ def main():
             ends[i].record(stream)
     torch.cuda.synchronize()
     durs = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
-    launch_ms = float(np.mean(durs))
 
     # ---- eager per-step time (no graph) for context
     with torch.cuda.stream(stream):
@@ -209,8 +239,8 @@ def main():
     gbs = nbytes / (ms_per_step * 1e-3) / 1e9
     achieved = nbytes / (launch_ms * 1e-3) / 1e9
     log(f"graph: {ms_per_step * 1e3:.2f} us/step = {gbs:.0f} GB/s; eager {eager_ms_per_step * 1e3:.2f} us/step; "
-        f"kernel (events) mean {launch_ms * 1e3:.2f} us, p10 {durs[len(durs) // 10] * 1e3:.2f}, "
-        f"p90 {durs[9 * len(durs) // 10] * 1e3:.2f} -> {achieved:.0f} GB/s")
+        f"single eager launch (events) mean {np.mean(durs) * 1e3:.2f} us, p10 {durs[len(durs) // 10] * 1e3:.2f}, "
+        f"p90 {durs[9 * len(durs) // 10] * 1e3:.2f}")
 
     traffic = None
     digest = source_digest()
@@ -219,7 +249,7 @@ def main():
             rec = json.load(open(COUNTERS))
             key = f"{wl.name}/m{m}"
             if rec.get("source_digest") == digest and key in rec.get("per_launch_bytes", {}):
-                traffic = rec["per_launch_bytes"][key]
+                traffic = rec["per_launch_bytes"][key]["total"]
         except (OSError, ValueError):
             traffic = None
 
@@ -253,8 +283,9 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
             "traffic": traffic,
-            "kernel": f"gemv_kernel<{bits}, M-tile {1 if m == 1 else m}>",
+            "kernel": kernel_name(bits, m),
             "kernel_us": round(launch_ms * 1e3, 3),
+            "single_launch_us_mean": round(float(np.mean(durs)) * 1e3, 3),
             "bytes_per_launch": nbytes,
             "source_digest": digest,
         },
