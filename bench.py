@@ -87,8 +87,13 @@ def calibrate_copy(nbytes: int, reps: int) -> None:
           flush=True)
 
 
+PEAK_MFMA_F16_TFLOPS = 2500.0
+
+
 def kernel_name(bits: int, m: int) -> str:
     """The kernel one step launches (the planner's choice for these shapes)."""
+    if m >= 64:
+        return f"gemm_kernel<{bits}> (matrix cores), after rht_kernel per linear"
     if m == 1:
         return f"gemv_ring_kernel<{bits}, true> (LDS-ring weight stream)"
     return f"gemv_stream_kernel<{bits}, {1 if m == 1 else 2 if m == 2 else 4}> (register prefetch)"
@@ -238,6 +243,8 @@ def main():
 
     gbs = nbytes / (ms_per_step * 1e-3) / 1e9
     achieved = nbytes / (launch_ms * 1e-3) / 1e9
+    flops = sum(2 * m * lin.n * lin.k for lin in lins)
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
     log(f"graph: {ms_per_step * 1e3:.2f} us/step = {gbs:.0f} GB/s; eager {eager_ms_per_step * 1e3:.2f} us/step; "
         f"single eager launch (events) mean {np.mean(durs) * 1e3:.2f} us, p10 {durs[len(durs) // 10] * 1e3:.2f}, "
         f"p90 {durs[9 * len(durs) // 10] * 1e3:.2f}")
@@ -283,10 +290,22 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
             "traffic": traffic,
-            "kernel": kernel_name(bits, m),
-            "kernel_us": round(launch_ms * 1e3, 3),
+        } if m < 64 else {
+            # batch >= 64: a dense contraction on the matrix cores; one step is
+            # the seven rotations and GEMMs, so this is per step, not per kernel
+            "bound": "mfma",
+            "achieved": round(tflops, 2),
+            "peak": PEAK_MFMA_F16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_MFMA_F16_TFLOPS, 4),
+            "traffic": None,
+            "flops_per_step": flops,
+        },
+        "kernel": {
+            "name": kernel_name(bits, m),
+            "us_per_step": round(launch_ms * 1e3, 3),
             "single_launch_us_mean": round(float(np.mean(durs)) * 1e3, 3),
-            "bytes_per_launch": nbytes,
+            "bytes_per_step": nbytes,
             "source_digest": digest,
         },
     }

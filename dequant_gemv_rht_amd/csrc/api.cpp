@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <algorithm>
 
 #include "wq_internal.h"
 
@@ -246,8 +247,41 @@ size_t rotated_bytes(const wq_weight &w, int64_t m) {
   return w.rht_signs ? align256((size_t)m * (size_t)rotated_ld(w) * sizeof(uint16_t)) : 0;
 }
 
+// Batch sizes from 64 up run on the matrix cores (uniform code widths); the
+// mixed-width layout stays on the GEMV, in chunks of 16 batch rows.
+bool use_gemm(const wq_weight &w, int64_t m) { return m >= 64 && wq::gemm_available(w.bits); }
+
 size_t gemm_path_workspace(const wq_weight &w, int64_t m) {
   return rotated_bytes(w, m) + wq::gemm_workspace(w, m);
+}
+
+// One validated linear: matrix-core path (rotation into the workspace, then
+// the GEMM) or the GEMV in chunks of 16 batch rows.
+wq_status linear_one(const wq_weight &w, const uint16_t *x, int64_t m, int64_t ldx, void *y, wq_dtype y_dtype,
+                     int64_t ldy, bool rotate, void *workspace, hipStream_t s) {
+  if (use_gemm(w, m)) {
+    const uint16_t *xr = x;
+    int64_t ldr = ldx;
+    char *ws = static_cast<char *>(workspace);
+    if (rotate) {
+      uint16_t *xt = reinterpret_cast<uint16_t *>(ws);
+      ldr = rotated_ld(w);
+      wq_status st = hip_status(wq::launch_rht(x, xt, w.rht_signs, m, w.k, ldx, ldr, s), "wq_linear");
+      if (st != WQ_OK) return st;
+      xr = xt;
+    }
+    ws += rotated_bytes(w, m);
+    return hip_status(wq::launch_gemm(w, xr, m, ldr, y, y_dtype == WQ_F32, ldy, ws, s), "wq_linear");
+  }
+  const size_t esz = y_dtype == WQ_F32 ? 4 : 2;
+  for (int64_t m0 = 0; m0 < m; m0 += 16) {
+    const int64_t mc = (m - m0) < 16 ? (m - m0) : 16;
+    const uint16_t *xc = x + m0 * ldx;
+    void *yc = static_cast<char *>(y) + (size_t)m0 * (size_t)ldy * esz;
+    wq_status st = run_gemv(1, &w, &xc, &ldx, mc, &yc, &y_dtype, &ldy, rotate, s);
+    if (st != WQ_OK) return st;
+  }
+  return WQ_OK;
 }
 
 }  // namespace
@@ -347,7 +381,7 @@ size_t wq_linear_workspace(const wq_weight *w, int64_t m) {
     fail(WQ_E_ARG, "wq_linear_workspace: m must be positive");
     return (size_t)-1;
   }
-  if (m >= 64) return gemm_path_workspace(*w, m);
+  if (use_gemm(*w, m)) return gemm_path_workspace(*w, m);
   return 0;   // the GEMV needs no workspace
 }
 
@@ -360,40 +394,12 @@ wq_status wq_linear(const wq_weight *w, const uint16_t *x, int64_t m, int64_t ld
   st = check_io(*w, x, m, ldx, y, y_dtype, ldy, "wq_linear");
   if (st != WQ_OK) return st;
   if (flags & ~WQ_FUSE_RHT) return fail(WQ_E_ARG, "wq_linear: unknown flags 0x%x", flags);
-  const bool rotate = (flags & WQ_FUSE_RHT) && w->rht_signs;
   const size_t need = wq_linear_workspace(w, m);
   if (need > workspace_bytes || (need && !workspace))
     return fail(WQ_E_WORKSPACE, "wq_linear: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
   if (workspace && !aligned16(workspace)) return fail(WQ_E_ALIGN, "wq_linear: workspace must be 16-byte aligned");
-  hipStream_t s = (hipStream_t)stream;
-  if (m >= 64) {
-    // Matrix-core path: rotate into the workspace first, then the GEMM.
-    if (!wq::gemm_available(w->bits))
-      return fail(WQ_E_UNSUPPORTED, "wq_linear: no matrix-core kernel for bits=%d at m=%lld", w->bits,
-                  (long long)m);
-    const uint16_t *xr = x;
-    int64_t ldr = ldx;
-    char *ws = static_cast<char *>(workspace);
-    if (rotate) {
-      uint16_t *xt = reinterpret_cast<uint16_t *>(ws);
-      ldr = rotated_ld(*w);
-      st = hip_status(wq::launch_rht(x, xt, w->rht_signs, m, w->k, ldx, ldr, s), "wq_linear");
-      if (st != WQ_OK) return st;
-      xr = xt;
-    }
-    ws += rotated_bytes(*w, m);
-    return hip_status(wq::launch_gemm(*w, xr, m, ldr, y, y_dtype == WQ_F32, ldy, ws, s), "wq_linear");
-  }
-  // GEMV, in chunks of 16 batch rows
-  const size_t esz = y_dtype == WQ_F32 ? 4 : 2;
-  for (int64_t m0 = 0; m0 < m; m0 += 16) {
-    const int64_t mc = (m - m0) < 16 ? (m - m0) : 16;
-    const uint16_t *xc = x + m0 * ldx;
-    void *yc = static_cast<char *>(y) + (size_t)m0 * (size_t)ldy * esz;
-    st = run_gemv(1, w, &xc, &ldx, mc, &yc, &y_dtype, &ldy, rotate, s);
-    if (st != WQ_OK) return st;
-  }
-  return WQ_OK;
+  return linear_one(*w, x, m, ldx, y, y_dtype, ldy, (flags & WQ_FUSE_RHT) && w->rht_signs, workspace,
+                    (hipStream_t)stream);
 }
 
 size_t wq_linear_batch_workspace(int32_t count, const wq_weight *w, int64_t m) {
@@ -402,13 +408,16 @@ size_t wq_linear_batch_workspace(int32_t count, const wq_weight *w, int64_t m) {
     fail(WQ_E_ARG, "wq_linear_batch_workspace: count must be 1..%d", WQ_MAX_BATCH);
     return (size_t)-1;
   }
-  if (m <= 0 || m > 16) {
-    fail(WQ_E_UNSUPPORTED, "wq_linear_batch_workspace: m must be 1..16");
+  if (m <= 0) {
+    fail(WQ_E_ARG, "wq_linear_batch_workspace: m must be positive");
     return (size_t)-1;
   }
-  for (int i = 0; i < count; ++i)
+  size_t need = 0;   // m <= 16: one GEMV launch, no workspace; larger m: the linears in turn share it
+  for (int i = 0; i < count; ++i) {
     if (check_weight(&w[i], "wq_linear_batch_workspace") != WQ_OK) return (size_t)-1;
-  return 0;   // the GEMV needs no workspace
+    if (m > 16 && use_gemm(w[i], m)) need = std::max(need, gemm_path_workspace(w[i], m));
+  }
+  return need;
 }
 
 wq_status wq_linear_batch(int32_t count, const wq_weight *w, const uint16_t *const *x, const int64_t *ldx,
@@ -417,7 +426,7 @@ wq_status wq_linear_batch(int32_t count, const wq_weight *w, const uint16_t *con
   clear_err();
   if (count <= 0 || count > WQ_MAX_BATCH) return fail(WQ_E_ARG, "wq_linear_batch: count must be 1..%d", WQ_MAX_BATCH);
   if (!w || !x || !ldx || !y || !y_dtype || !ldy) return fail(WQ_E_ARG, "wq_linear_batch: NULL argument array");
-  if (m <= 0 || m > 16) return fail(WQ_E_UNSUPPORTED, "wq_linear_batch: m must be 1..16");
+  if (m <= 0) return fail(WQ_E_ARG, "wq_linear_batch: m=%lld must be positive", (long long)m);
   if (flags & ~WQ_FUSE_RHT) return fail(WQ_E_ARG, "wq_linear_batch: unknown flags 0x%x", flags);
   for (int i = 0; i < count; ++i) {
     wq_status st = check_weight(&w[i], "wq_linear_batch");
@@ -429,10 +438,21 @@ wq_status wq_linear_batch(int32_t count, const wq_weight *w, const uint16_t *con
     if (((flags & WQ_FUSE_RHT) && w[i].rht_signs) != ((flags & WQ_FUSE_RHT) && w[0].rht_signs))
       return fail(WQ_E_UNSUPPORTED, "wq_linear_batch: rotate all linears or none");
   }
-  (void)workspace;
-  (void)workspace_bytes;
   const bool rotate = (flags & WQ_FUSE_RHT) && w[0].rht_signs;
-  return run_gemv(count, w, x, ldx, m, y, y_dtype, ldy, rotate, (hipStream_t)stream);
+  if (m <= 16) return run_gemv(count, w, x, ldx, m, y, y_dtype, ldy, rotate, (hipStream_t)stream);
+  // larger batches: one linear after another on the stream, sharing the workspace
+  const size_t need = wq_linear_batch_workspace(count, w, m);
+  if (need == (size_t)-1) return WQ_E_ARG;
+  if (need > workspace_bytes || (need && !workspace))
+    return fail(WQ_E_WORKSPACE, "wq_linear_batch: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  if (workspace && !aligned16(workspace))
+    return fail(WQ_E_ALIGN, "wq_linear_batch: workspace must be 16-byte aligned");
+  for (int i = 0; i < count; ++i) {
+    const wq_status st = linear_one(w[i], x[i], m, ldx[i], y[i], y_dtype[i], ldy[i], rotate, workspace,
+                                    (hipStream_t)stream);
+    if (st != WQ_OK) return st;
+  }
+  return WQ_OK;
 }
 
 }  // extern "C"

@@ -177,18 +177,22 @@ size_t wq_linear_workspace(const wq_weight *w, int64_t m);
  *   w          host struct describing the device weight
  *   x          fp16 [m][ldx]
  *   y          out: fp16 or fp32 [m][ldy] (y_dtype)
- *   workspace  device scratch of at least wq_linear_workspace(w, m) bytes.
- *              It must be zero-filled once before its first use; every
- *              call leaves it zero-filled again.
+ *   workspace  device scratch of at least wq_linear_workspace(w, m) bytes
+ *              (caller-owned, 16-byte aligned; NULL when that is 0).  The
+ *              matrix-core path keeps the rotated activations there; its
+ *              contents need no initialisation and are not preserved.
  */
 wq_status wq_linear(const wq_weight *w, const uint16_t *x, int64_t m, int64_t ldx,
                     void *y, wq_dtype y_dtype, int64_t ldy, uint32_t flags,
                     void *workspace, size_t workspace_bytes, void *stream);
 
-/* Several independent linears in one launch (up to WQ_MAX_BATCH), each with
- * its own weight, activations and output, all at the same batch size m
- * (m <= 16).  Same math, layout and workspace rules as wq_linear, applied to
- * each w[i], x[i], y[i].  Arrays of length `count` are host arrays. */
+/* Several independent linears (up to WQ_MAX_BATCH), each with its own
+ * weight, activations and output, all at the same batch size m and code
+ * width.  For m <= 16 they run as one GEMV launch (workspace size 0); for
+ * larger m they run one after another on the stream exactly as wq_linear
+ * would, sharing one workspace of wq_linear_batch_workspace bytes.  Same
+ * math and layout as wq_linear, applied to each w[i], x[i], y[i].  Arrays of
+ * length `count` are host arrays. */
 size_t wq_linear_batch_workspace(int32_t count, const wq_weight *w, int64_t m);
 wq_status wq_linear_batch(int32_t count, const wq_weight *w,
                           const uint16_t *const *x, const int64_t *ldx, int64_t m,

@@ -139,7 +139,25 @@ def test_other_entry_points_reject(lib):
     assert lib.wq_linear_batch(2, arr, xs, lds, 1, ys, dts, ldy, 0, 16, 1 << 20, None) == dq.WQ_E_UNSUPPORTED
     assert "one code width" in lib.wq_last_error().decode()
     assert lib.wq_linear_batch(9, arr, xs, lds, 1, ys, dts, ldy, 0, 16, 1 << 20, None) == dq.WQ_E_ARG
-    assert lib.wq_linear_batch(2, arr, xs, lds, 17, ys, dts, ldy, 0, 16, 1 << 20, None) == dq.WQ_E_UNSUPPORTED
+    assert lib.wq_linear_batch(2, arr, xs, lds, 0, ys, dts, ldy, 0, 16, 1 << 20, None) == dq.WQ_E_ARG
+
+
+def test_batch_workspace_for_large_m(lib):
+    # m <= 16: one GEMV launch, no workspace; m >= 64: the linears run in turn
+    # on the matrix cores and share one workspace sized for the largest
+    sg = dict(rht_signs=16, rht_block=128)
+    arr = (dq.WqWeight * 2)(_weight(n=256, k=2560, **sg), _weight(n=128, k=9728, **sg))
+    assert lib.wq_linear_batch_workspace(2, arr, 16) == 0
+    single = [lib.wq_linear_workspace(ctypes.byref(arr[i]), 512) for i in range(2)]
+    assert min(single) > 0
+    assert lib.wq_linear_batch_workspace(2, arr, 512) == max(single)
+    xs = (ctypes.c_void_p * 2)(16, 16)
+    lds = (ctypes.c_int64 * 2)(2560, 9728)
+    ys = (ctypes.c_void_p * 2)(16, 16)
+    dts = (ctypes.c_int32 * 2)(dq.WQ_F16, dq.WQ_F16)
+    ldy = (ctypes.c_int64 * 2)(256, 128)
+    st = lib.wq_linear_batch(2, arr, xs, lds, 512, ys, dts, ldy, dq.WQ_FUSE_RHT, 16, max(single) - 256, None)
+    assert st == dq.WQ_E_WORKSPACE
 
 
 def test_matrix_core_path_workspace_covers_rotated_activations(lib):

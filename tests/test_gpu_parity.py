@@ -155,6 +155,49 @@ def test_linear_shapes(n, k, rht, out_f32):
     _run_case(n, k, 3, 4, rht, out_f32, n + k)
 
 
+# ---------------------------------------------------------- matrix-core path
+
+@pytest.mark.parametrize("bits", [3, 4, 6, 8])
+@pytest.mark.parametrize("m,n,k", [(64, 256, 512), (100, 200, 384), (256, 130, 1024)])
+def test_gemm_bits_and_ragged_shapes(bits, m, n, k):
+    # M >= 64 runs on MFMA; ragged M and N exercise the partial tiles
+    say(f"gemm bits={bits} m={m} n={n} k={k}")
+    _run_case(n, k, m, bits, True, False, 7000 + 100 * bits + m)
+
+
+@pytest.mark.parametrize("rht,out_f32", [(False, False), (True, True), (False, True)])
+def test_gemm_rotation_and_output(rht, out_f32):
+    say(f"gemm rht={rht} f32={out_f32}")
+    _run_case(192, 640, 128, 4, rht, out_f32, 11 + 2 * rht + out_f32)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_gemm_trained_scales_and_zeros(bits):
+    say(f"gemm trained s,z bits={bits}")
+    n, k, m = 140, 512, 96
+    w, x, signs = _inputs(n, k, m, 300 + bits)
+    q, s, z = OR.prepare(w, signs, bits)
+    s2, z2 = W.trained_scale_zero(s, z, np.random.default_rng(bits + 1), (1 << bits) - 1)
+    ref = OL.linear(q, s2, z2, x, signs)
+    packed, _ = dq.wq_pack(dev(q), bits)
+    qw = dq.QWeight(bits, n, k, packed, dev(s2), dev(z2), dev_u32(signs))
+    check_close(dq.wq_linear(qw, dev(x)).float().cpu().numpy(), ref, "gemm trained s,z")
+
+
+def test_gemm_mixed_width_runs_on_gemv():
+    # the mixed-width layout has no matrix-core kernel: M >= 64 takes the
+    # GEMV in chunks and needs no workspace
+    say("mixed m=64")
+    n, k, m = 192, 512, 64
+    w, x, signs = _inputs(n, k, m, 77)
+    sel = np.array([8, 6, 8], np.uint8)
+    qw = _gpu_weight(w, signs, 0, sel)
+    assert dq.wq_linear_workspace(qw, m) == 0
+    q, s, z = OR.prepare(w, signs, np.repeat(sel, 64))
+    ref = OL.linear(q, s, z, x, signs)
+    check_close(dq.wq_linear(qw, dev(x)).float().cpu().numpy(), ref, "mixed m=64")
+
+
 @pytest.mark.parametrize("m", [17, 40])
 def test_linear_batch_chunks(m):
     say(f"linear chunked m={m}")
