@@ -41,6 +41,8 @@
 // ds_read_b128 hit 16 distinct 4-bank groups.
 #include "wq_internal.h"
 
+#include <type_traits>
+
 namespace wq {
 using namespace dev;
 
@@ -205,7 +207,9 @@ constexpr int kSliceStride = 20;   // u32 per activation slice in LDS (80 bytes,
 
 // Rotate one item into LDS.  Only DPP rows that hold an item do any work
 // (the branch is uniform across the 16 lanes of a row).
-template <int BITS, int MT>
+// With SUMS_IN_SLICE the two slice sums go into the slice's spare bytes
+// (words 16 and 17 of its 20), so one LDS address serves both.
+template <int BITS, int MT, bool SUMS_IN_SLICE = false>
 __device__ __forceinline__ void rotate_item(bool rotate, u32x4 raw, uint32_t sword, int nb, int items, int it,
                                             int jj, uint32_t *xp, float *xs, int S) {
   if (it >= items) return;
@@ -236,8 +240,14 @@ __device__ __forceinline__ void rotate_item(bool rotate, u32x4 raw, uint32_t swo
   const int slice = 4 * b + (jj >> 2);
   *reinterpret_cast<u32x4 *>(&xp[(m * S + slice) * kSliceStride + 4 * (jj & 3)]) = u32x4{o[0], o[1], o[2], o[3]};
   if ((jj & 3) == 0) {
-    xs[2 * (m * S + slice)] = xe;
-    xs[2 * (m * S + slice) + 1] = 1024.0f * xt;
+    if constexpr (SUMS_IN_SLICE) {
+      float *sums = reinterpret_cast<float *>(&xp[(m * S + slice) * kSliceStride + 16]);
+      sums[0] = xe;
+      sums[1] = 1024.0f * xt;
+    } else {
+      xs[2 * (m * S + slice)] = xe;
+      xs[2 * (m * S + slice) + 1] = 1024.0f * xt;
+    }
   }
 }
 
@@ -501,58 +511,51 @@ struct Ring {
   static constexpr int q = 2 * nc + 2;                             // vector loads per wave per step
 };
 
-// Keeps the compiler from turning a select feeding a load's offset into a
-// branch around two copies of the load (which would change the load count).
-__device__ __forceinline__ uint32_t opaque(uint32_t v) {
-  asm volatile("" : "+v"(v));
-  return v;
-}
-
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
 
 // One row's direct loads of a step: chunk c of every lane to its region.
+// `soff` (a scalar offset) selects the row; tasks past the workgroup's rows
+// have offsets past the buffer resource and read zero.
 template <int BITS, int C = 0>
-__device__ __forceinline__ void ring_row_loads(rsrc_t rc, uint8_t *row, bool ok, uint32_t off) {
+__device__ __forceinline__ void ring_row_loads(rsrc_t rc, uint8_t *row, uint32_t off, uint32_t soff) {
   using RS = Ring<BITS>;
 #if defined(__HIP_DEVICE_COMPILE__)   // 16-byte LDS loads exist only in the gfx950 pass
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (lds_ptr_t)(row + 256 * RS::word(C)), RS::size(C),
-                                           opaque(ok ? off + 4 * RS::word(C) : kOOB), 0, 0, kNT);
+                                           off + 4 * RS::word(C), (int)soff, 0, kNT);
 #endif
-  if constexpr (C + 1 < RS::nc) ring_row_loads<BITS, C + 1>(rc, row, ok, off);
+  if constexpr (C + 1 < RS::nc) ring_row_loads<BITS, C + 1>(rc, row, off, soff);
 }
 
 // Load-side position of a 16-lane task row in its workgroup's task list
-// (task lt = (row pair, segment ls)), and the step issue into ring slot d.
-template <int BITS, bool FULL>
+// (task = (row pair, segment ls)), and the step issue into ring slot D.
+// Every lane issues every load: out-of-range slices of a partial last
+// segment read the next row's bytes (or zero), which only feed lanes whose
+// scale is masked to 0.
+template <int BITS>
 struct RingCursor {
   using RS = Ring<BITS>;
   rsrc_t rc, rsc, rz;
   uint8_t *ring;
-  int wave, j, T, S, KS, wpr, ds;
-  uint32_t dco, wco;
-  int dso, wso;
-  int lt, ls;
+  int wave, KS, ds;
+  uint32_t row_bytes, dco, wco, dso, wso;
+  int ls;
   uint32_t lco;   // byte offset of this lane's code words, row 0 of the task
-  int lso;        // byte offset of the scale/zero pair this lane fetches (lanes 0..3)
+  uint32_t lso;   // byte offset of the scale/zero pair this lane fetches (lanes 0..3 of a task)
 
-  __device__ __forceinline__ void issue(int d) {
-    const bool ok = lt < T && (FULL || ls * 16 + j < S);
-    uint8_t *slot = ring + (d * (kStreamThreads / 64) + wave) * RS::slot;
-#pragma unroll
-    for (int r = 0; r < 2; ++r) ring_row_loads<BITS>(rc, slot + r * RS::row, ok, lco + r * wpr * 4);
-    const bool oks = lt < T && j < 4 && (FULL || ls * 16 + 8 * (j & 1) < S);
-    const uint32_t so = opaque(oks ? (uint32_t)lso : kOOB);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsc, (lds_ptr_t)(slot + RS::codes), 4, so, 0, 0, kNT);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rz, (lds_ptr_t)(slot + RS::codes + 256), 4, so, 0, 0, kNT);
-    lt += kRG;
-    lco += dco;
-    lso += dso;
+  template <int D>
+  __device__ __forceinline__ void issue() {
+    uint8_t *slot = ring + (D * (kStreamThreads / 64) + wave) * RS::slot;
+    ring_row_loads<BITS>(rc, slot, lco, 0u);
+    ring_row_loads<BITS>(rc, slot + RS::row, lco, row_bytes);
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsc, (lds_ptr_t)(slot + RS::codes), 4, lso, 0, 0, kNT);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rz, (lds_ptr_t)(slot + RS::codes + 256), 4, lso, 0, 0, kNT);
+#endif
     ls += ds;
-    if (ls >= KS) {
-      ls -= KS;
-      lco += wco;
-      lso += wso;
-    }
+    const bool wrap = ls >= KS;
+    ls = wrap ? ls - KS : ls;
+    lco += wrap ? wco : dco;
+    lso += wrap ? wso : dso;
   }
 };
 
@@ -563,9 +566,9 @@ struct RingLds {
 
 __host__ __device__ inline RingLds ring_lds(int S, int KS, int np, int slot, int depth) {
   RingLds l;
-  l.xs = S * kSliceStride * 4;                      // activations: [S][20] u32
-  l.part = l.xs + S * 8;                            // slice sums: [S][2] f32
-  l.ring = (l.part + 2 * np * KS * 4 + 15) & ~15;   // partials: [2np][KS] f32
+  l.xs = S * kSliceStride * 4;                      // activations: [S][20] u32, sums in words 16, 17
+  l.part = l.xs;                                    // partials: [2np][KS] f32
+  l.ring = (l.part + 2 * np * KS * 4 + 15) & ~15;
   l.total = l.ring + depth * (kStreamThreads / 64) * slot;
   return l;
 }
@@ -595,7 +598,8 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 }
 
 // A task's LDS operands, read in one asm statement that also waits for
-// them: the activation slice (4 x 16 bytes) and its two sums, the scales and
+// them: the activation slice (4 x 16 bytes) and its two sums (bytes 64..71
+// of the slice), the scales and
 // zeros of the lane's group (rows 0, 1), and the lane's code words of both
 // rows from the ring slot.  Keeping these reads out of the compiler's view
 // keeps it from tying them to the ring's direct loads with waits of its own.
@@ -606,14 +610,14 @@ struct TaskOps {
 };
 
 template <int BITS>
-__device__ __forceinline__ void read_task(uint32_t xa, uint32_t xsa, uint32_t sza, uint32_t ca16, uint32_t ca4,
-                                          TaskOps &o, uint32_t (&w)[2][BITS]) {
+__device__ __forceinline__ void read_task(uint32_t xa, uint32_t sza, uint32_t ca16, uint32_t ca4, TaskOps &o,
+                                          uint32_t (&w)[2][BITS]) {
 #define WQ_OPS_READS                    \
   "ds_read_b128 %[x0], %[xa]\n\t"       \
   "ds_read_b128 %[x1], %[xa] offset:16\n\t" \
   "ds_read_b128 %[x2], %[xa] offset:32\n\t" \
   "ds_read_b128 %[x3], %[xa] offset:48\n\t" \
-  "ds_read_b64 %[xq], %[xsa]\n\t"       \
+  "ds_read_b64 %[xq], %[xa] offset:64\n\t" \
   "ds_read_u16 %[s0], %[sza]\n\t"       \
   "ds_read_u16 %[s1], %[sza] offset:8\n\t" \
   "ds_read_u16 %[z0], %[sza] offset:256\n\t" \
@@ -621,7 +625,7 @@ __device__ __forceinline__ void read_task(uint32_t xa, uint32_t xsa, uint32_t sz
 #define WQ_OPS_OUT                                                                                      \
   [x0] "=&v"(o.x[0]), [x1] "=&v"(o.x[1]), [x2] "=&v"(o.x[2]), [x3] "=&v"(o.x[3]), [xq] "=&v"(o.xq),     \
       [s0] "=&v"(o.s0), [s1] "=&v"(o.s1), [z0] "=&v"(o.z0), [z1] "=&v"(o.z1)
-#define WQ_OPS_IN [xa] "v"(xa), [xsa] "v"(xsa), [sza] "v"(sza), [ca16] "v"(ca16), [ca4] "v"(ca4)
+#define WQ_OPS_IN [xa] "v"(xa), [sza] "v"(sza), [ca16] "v"(ca16), [ca4] "v"(ca4)
   if constexpr (BITS == 4) {
     // row r: 16 bytes at r * 1024 + 16 L
     u32x4 c0, c1;
@@ -721,21 +725,48 @@ __device__ __forceinline__ void stream_ring(const LinDesc &L, int r0, int rows, 
   const RingLds lay = ring_lds(S, KS, NP, RS::slot, R);
   uint8_t *lds = reinterpret_cast<uint8_t *>(smem);
   uint32_t *xp = smem;
-  float *xs = reinterpret_cast<float *>(lds + lay.xs);
   float *part = reinterpret_cast<float *>(lds + lay.part);
   uint8_t *ring = lds + lay.ring;
+  const int steps = (T + kRG - 1) / kRG;   // steps of this workgroup (uniform)
 
-  const rsrc_t rc = make_rsrc(L.codes + (size_t)r0 * wpr, (uint32_t)rows * wpr * 4);
-  // scale/zero ranges rounded up to the 4-byte loads: the extra bytes share
-  // the last valid 4-byte granule and only feed lanes that are masked off
-  const uint32_t szb = ((uint32_t)rows * G * 2 + 3u) & ~3u;
-  const rsrc_t rsc = make_rsrc(L.scales + (size_t)r0 * G, szb);
-  const rsrc_t rz = make_rsrc(L.zeros + (size_t)r0 * G, szb);
+  // 1. the first R steps of the weight stream, before anything else.  Task
+  //    tau = rg + 64 i is (row pair tau / KS, segment tau % KS).
+  RingCursor<BITS> cur;
+  {
+    const uint32_t row_bytes = (uint32_t)wpr * 4, pair_bytes = 2 * row_bytes;
+    const uint32_t seg_step = 16 * BITS * 4;
+    const int ds = kRG % KS, dp = kRG / KS;
+    cur.rc = make_rsrc(L.codes + (size_t)r0 * wpr, (uint32_t)rows * row_bytes);
+    // scale/zero ranges rounded up to the 4-byte loads: the extra bytes share
+    // the last valid 4-byte granule and only feed lanes that are masked off
+    const uint32_t szb = ((uint32_t)rows * G * 2 + 3u) & ~3u;
+    cur.rsc = make_rsrc(L.scales + (size_t)r0 * G, szb);
+    cur.rz = make_rsrc(L.zeros + (size_t)r0 * G, szb);
+    cur.ring = ring;
+    cur.wave = wave;
+    cur.KS = KS;
+    cur.ds = ds;
+    cur.row_bytes = row_bytes;
+    cur.dco = (uint32_t)dp * pair_bytes + (uint32_t)ds * seg_step;
+    cur.wco = cur.dco + pair_bytes - (uint32_t)KS * seg_step;
+    cur.dso = (uint32_t)(2 * (2 * dp * G + 4 * ds));
+    cur.wso = cur.dso + (uint32_t)(2 * (2 * G - 4 * KS));
+    cur.ls = rg % KS;
+    cur.lco = (uint32_t)(rg / KS) * pair_bytes + (uint32_t)cur.ls * seg_step + (uint32_t)j * (BITS * 4);
+    // lanes j < 4 fetch the scales/zeros of row 2p + (j >> 1), groups 4s + 2(j & 1) + {0, 1};
+    // the other lanes start past any resource (2^31) and stay there as the offset advances
+    cur.lso = (uint32_t)(2 * (2 * (rg / KS) * G + 4 * cur.ls) + (j >> 1) * 2 * G + (j & 1) * 4);
+    if (j >= 4) cur.lso = kOOB;
+  }
+  if (steps > 0) cur.template issue<0>();
+  if constexpr (R > 1) if (steps > 1) cur.template issue<1>();
+  if constexpr (R > 2) if (steps > 2) cur.template issue<2>();
+  if constexpr (R > 3) if (steps > 3) cur.template issue<3>();
+
+  // 2. activations and signs, then the rotation into LDS
   const rsrc_t rx = make_rsrc(L.x, (uint32_t)K * 2);
   const rsrc_t rsg = make_rsrc(L.signs, L.signs ? (uint32_t)(K / 8) : 0u);
   const bool rotate = L.signs != nullptr;
-
-  // 1. activations and signs first
   const int nb = K / kGroup, items = nb;
   u32x4 xr[XC];
   uint32_t sw[XC];
@@ -746,34 +777,10 @@ __device__ __forceinline__ void stream_ring(const LinDesc &L, int r0, int rows, 
     xr[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, xo, 0, 0));
     sw[q] = rotate ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsg, so, 0, 0) : 0u;
   }
-
-  // 2. the first R steps of the weight stream.  Task tau = rg + 64 i is
-  //    (row pair tau / KS, segment tau % KS); load-side position below.
-  const uint32_t seg_step = 16 * BITS * 4;
-  const uint32_t pair_bytes = (uint32_t)(2 * wpr * 4);
-  const int ds = kRG % KS, dp = kRG / KS;
-  const uint32_t dco = (uint32_t)dp * pair_bytes + (uint32_t)ds * seg_step;
-  const uint32_t wco = pair_bytes - (uint32_t)KS * seg_step;
-  const int dso = 2 * (2 * dp * G + 4 * ds), wso = 2 * (2 * G - 4 * KS);
-  RingCursor<BITS, FULL> cur;
-  cur.rc = rc; cur.rsc = rsc; cur.rz = rz;
-  cur.ring = ring; cur.wave = wave; cur.j = j; cur.T = T; cur.S = S; cur.KS = KS; cur.wpr = wpr;
-  cur.ds = ds; cur.dco = dco; cur.wco = wco; cur.dso = dso; cur.wso = wso;
-  cur.lt = rg;
-  cur.ls = rg % KS;
-  cur.lco = (uint32_t)(rg / KS) * pair_bytes + (uint32_t)cur.ls * seg_step + (uint32_t)j * (BITS * 4);
-  // lanes j < 4 fetch scales/zeros of row 2p + (j >> 1), groups 4s + 2(j & 1) + {0, 1}
-  cur.lso = 2 * (2 * (rg / KS) * G + 4 * cur.ls) + (j >> 1) * 2 * G + (j & 1) * 4;
-  const int steps = (T + kRG - 1) / kRG;   // steps of this workgroup (uniform)
-#pragma unroll
-  for (int d = 0; d < R; ++d)
-    if (d < steps) cur.issue(d);
-
-  // 3. rotation into LDS
 #pragma unroll
   for (int q = 0; q < XC; ++q) {
     consume(xr[q], sw[q]);
-    rotate_item<BITS, 1>(rotate, xr[q], sw[q], nb, items, rg + kRG * q, j, xp, xs, S);
+    rotate_item<BITS, 1, true>(rotate, xr[q], sw[q], nb, items, rg + kRG * q, j, xp, nullptr, S);
   }
   for (int it0 = kRG * XC; it0 < items; it0 += kRG) {
     uint32_t xo, so;
@@ -781,32 +788,42 @@ __device__ __forceinline__ void stream_ring(const LinDesc &L, int r0, int rows, 
     const u32x4 raw = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, xo, 0, 0));
     const uint32_t w1 = rotate ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsg, so, 0, 0) : 0u;
     consume(raw, w1);
-    rotate_item<BITS, 1>(rotate, raw, w1, nb, items, it0 + rg, j, xp, xs, S);
+    rotate_item<BITS, 1, true>(rotate, raw, w1, nb, items, it0 + rg, j, xp, nullptr, S);
   }
   lds_barrier();
 
-  // 4. consume the ring
+  // 3. consume the ring
   const UnpackConsts uc = unpack_consts<BITS>();
-  const uint32_t xa0 = lds_addr(xp), xsa0 = lds_addr(xs), parta0 = lds_addr(part);
-  int cp = rg / KS, cs = rg % KS;   // task being computed
-  for (int i = 0; i < steps; ++i) {
-    const int d = i % R;
+  // Compute-side position of the task: its slice's LDS address xa (slice
+  // 16 cs + j) and, for lanes 0 and 1, the address of row 2 cp + j's partial
+  // for segment cs.  Both advance by a step's (dp pairs, ds segments), with
+  // one compare for the segment wrap.
+  const int ds = kRG % KS, dp = kRG / KS;
+  constexpr uint32_t kSegBytes = 16 * kSliceStride * 4;
+  const int cs0 = rg % KS, cp0 = rg / KS;
+  uint32_t xa = lds_addr(xp) + (uint32_t)(j * kSliceStride * 4) + (uint32_t)cs0 * kSegBytes;
+  const uint32_t xa_end = lds_addr(xp) + (uint32_t)(j * kSliceStride * 4) + (uint32_t)KS * kSegBytes;
+  uint32_t pa = lds_addr(part) + (uint32_t)((((2 * cp0 + (j & 1)) * KS) + cs0) * 4);
+  const uint32_t dxa = (uint32_t)ds * kSegBytes, wxa = (uint32_t)KS * kSegBytes;
+  const uint32_t dpa = (uint32_t)((2 * dp * KS + ds) * 4), wpa = dpa + (uint32_t)(KS * 4);
+  int cs = cs0;   // only needed to mask slices of a partial last segment
+  const uint8_t *slot0 = ring + wave * RS::slot;
+  const uint32_t sza_l = lds_addr(slot0 + RS::codes + (lane & 48) * 4 + (j >> 2) * 2);
+  const uint32_t ca16_l = lds_addr(slot0) + lane * 16, ca4_l = lds_addr(slot0) + lane * 4;
+  constexpr uint32_t kStage = (kStreamThreads / 64) * RS::slot;   // bytes between ring stages
+  // one step i in ring slot D (a compile-time constant, so slot addresses fold)
+  auto step = [&](auto dconst, int i) {
+    constexpr int d = decltype(dconst)::value;
     {
       // wait for step i; the loads of steps i+1 .. min(i+R, steps)-1 may stay in flight
-      const int younger = min(R - 1, steps - 1 - i);
-      wait_vmcnt_younger<R, Q>(younger);
+      wait_vmcnt_younger<R, Q>(min(R - 1, steps - 1 - i));
       if (rg + kRG * i < T) {
-        const uint8_t *slot = ring + (d * (kStreamThreads / 64) + wave) * RS::slot;
-        const int slice = cs * 16 + j;
-        const bool sv = FULL || slice < S;
-        const int sl = sv ? slice : 0;
+        const bool sv = FULL || cs * 16 + j < S;
         TaskOps o;
         uint32_t cw[2][BITS];
         // scales/zeros of this lane's group (rows 0, 1) were fetched by lanes
         // 0..3 of its task: 4 bytes each at task * 64 + 4 * (2 row + group / 2)
-        read_task<BITS>(xa0 + sl * (kSliceStride * 4), xsa0 + sl * 8,
-                        lds_addr(slot + RS::codes + (lane & 48) * 4 + (j >> 2) * 2), lds_addr(slot) + lane * 16,
-                        lds_addr(slot) + lane * 4, o, cw);
+        read_task<BITS>(sv ? xa : lds_addr(xp), sza_l + d * kStage, ca16_l + d * kStage, ca4_l + d * kStage, o, cw);
         uint32_t xv[16];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -824,7 +841,7 @@ __device__ __forceinline__ void stream_ring(const LinDesc &L, int r0, int rows, 
           float dd = fmaf(-zc[r], xsum, -xoff);
 #pragma unroll
           for (int q = 0; q < 16; ++q) dd = dot2(pr[q], xv[q], dd);
-          a[r] = (sv ? sc[r] : 0.f) * dd;
+          a[r] = fmaf(sv ? sc[r] : 0.f, dd, 0.0f);   // one v_fma_mix with the fp16 scale
         }
         // both rows summed over the 16 lanes at once: after the first
         // exchange, even lanes carry row 0 and odd lanes row 1
@@ -833,22 +850,27 @@ __device__ __forceinline__ void stream_ring(const LinDesc &L, int r0, int rows, 
         v += dpp<kQuadXor2>(v);
         v += dpp<kRowRor4>(v);
         v += dpp<kRowRor8>(v);
-        if (j < 2) lds_store(parta0 + ((2 * cp + j) * KS + cs) * 4, v);
-        cs += ds;
-        cp += dp;
-        if (cs >= KS) {
-          cs -= KS;
-          ++cp;
-        }
+        if (j < 2) lds_store(pa, v);
+        xa += dxa;
+        const bool wrap = xa >= xa_end;
+        xa = wrap ? xa - wxa : xa;
+        pa += wrap ? wpa : dpa;
+        if constexpr (!FULL) cs = wrap ? cs + ds - KS : cs + ds;
       }
       wait_lgkm0();   // this slot's bytes are in registers before it is refilled
-      if (i + R < steps) cur.issue(d);
+      if (i + R < steps) cur.template issue<d>();
     }
+  };
+  for (int i0 = 0; i0 < steps; i0 += R) {
+    step(std::integral_constant<int, 0>{}, i0);
+    if constexpr (R > 1) if (i0 + 1 < steps) step(std::integral_constant<int, 1>{}, i0 + 1);
+    if constexpr (R > 2) if (i0 + 2 < steps) step(std::integral_constant<int, 2>{}, i0 + 2);
+    if constexpr (R > 3) if (i0 + 3 < steps) step(std::integral_constant<int, 3>{}, i0 + 3);
   }
   wait_vmcnt<0>();    // no load may still be writing LDS when the workgroup ends
   __syncthreads();
 
-  // 5. add each row's partials in segment order, store
+  // 4. add each row's partials in segment order, store
   for (int e = t; e < rows; e += kStreamThreads) {
     float sum = 0.f;
     for (int s = 0; s < KS; ++s) sum += part[e * KS + s];
