@@ -205,6 +205,18 @@ __device__ __forceinline__ void item_offsets(const LinDesc &L, int nb, int items
 
 constexpr int kSliceStride = 20;   // u32 per activation slice in LDS (80 bytes, 64 used)
 
+// fp16 values e0 .. e0 + 7 of a resource holding n of them, zero from n on.
+// A load that reaches past the end of its range returns zero as a whole, so
+// the group of eight that holds the end is read one value at a time.
+__device__ __forceinline__ u32x4 load8_h(rsrc_t rs, int e0, int n) {
+  if (e0 + 8 <= n) return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)e0 * 2, 0, 0));
+  uint32_t h[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    h[e] = e0 + e < n ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, (uint32_t)(e0 + e) * 2, 0, 0) : 0u;
+  return u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+}
+
 // Rotate one item into LDS.  Only DPP rows that hold an item do any work
 // (the branch is uniform across the 16 lanes of a row).
 // With SUMS_IN_SLICE the two slice sums go into the slice's spare bytes
@@ -293,11 +305,9 @@ __device__ __forceinline__ void stream_rows(const LinDesc &L, int m_valid, int r
   float *szl = reinterpret_cast<float *>(smem + lay.szl);
 
   const rsrc_t rc = make_rsrc(L.codes + (size_t)r0 * wpr, (uint32_t)rows * wpr * 4);
-  // scale/zero ranges rounded up to the 16-byte loads: the extra bytes share
-  // the last valid 16-byte granule and only feed rows past the matrix
-  const uint32_t szb = ((uint32_t)rows * G * 2 + 15u) & ~15u;
-  const rsrc_t rsc = make_rsrc(L.scales + (size_t)r0 * G, szb);
-  const rsrc_t rz = make_rsrc(L.zeros + (size_t)r0 * G, szb);
+  const int nszv = rows * G;                 // scale (zero) values of the workgroup's rows
+  const rsrc_t rsc = make_rsrc(L.scales + (size_t)r0 * G, (uint32_t)nszv * 2);
+  const rsrc_t rz = make_rsrc(L.zeros + (size_t)r0 * G, (uint32_t)nszv * 2);
   const rsrc_t rx = make_rsrc(L.x, (uint32_t)(((size_t)(m_valid - 1) * L.ldx + K) * 2));
   const rsrc_t rsg = make_rsrc(L.signs, L.signs ? (uint32_t)(K / 8) : 0u);
   const bool rotate = L.signs != nullptr;
@@ -320,9 +330,8 @@ __device__ __forceinline__ void stream_rows(const LinDesc &L, int m_valid, int r
 #pragma unroll
   for (int q = 0; q < ZL; ++q) {
     const int e0 = 8 * (t + kStreamThreads * q);
-    const uint32_t off = e0 < nsz ? (uint32_t)e0 * 2 : kOOB;
-    sr[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsc, off, 0, 0));
-    zr[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rz, off, 0, 0));
+    sr[q] = load8_h(rsc, e0, nszv);
+    zr[q] = load8_h(rz, e0, nszv);
   }
 
   // 2. the first D steps of this DPP row's tasks: task = rg + 64 i
@@ -359,8 +368,8 @@ __device__ __forceinline__ void stream_rows(const LinDesc &L, int m_valid, int r
     }
   }
   for (int e0 = 8 * (t + kStreamThreads * ZL); e0 < nsz; e0 += 8 * kStreamThreads) {
-    const u32x4 a = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsc, (uint32_t)e0 * 2, 0, 0));
-    const u32x4 b = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rz, (uint32_t)e0 * 2, 0, 0));
+    const u32x4 a = load8_h(rsc, e0, nszv);
+    const u32x4 b = load8_h(rz, e0, nszv);
     const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
     for (int h = 0; h < 4; ++h)
@@ -514,16 +523,17 @@ struct Ring {
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
 
 // One row's direct loads of a step: chunk c of every lane to its region.
-// `soff` (a scalar offset) selects the row; tasks past the workgroup's rows
-// have offsets past the buffer resource and read zero.
+// Tasks past the workgroup's rows have offsets past the buffer resource and
+// read zero.  The whole offset is in the vector operand: the range check of
+// a raw buffer load does not include the scalar offset.
 template <int BITS, int C = 0>
-__device__ __forceinline__ void ring_row_loads(rsrc_t rc, uint8_t *row, uint32_t off, uint32_t soff) {
+__device__ __forceinline__ void ring_row_loads(rsrc_t rc, uint8_t *row, uint32_t off) {
   using RS = Ring<BITS>;
 #if defined(__HIP_DEVICE_COMPILE__)   // 16-byte LDS loads exist only in the gfx950 pass
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (lds_ptr_t)(row + 256 * RS::word(C)), RS::size(C),
-                                           off + 4 * RS::word(C), (int)soff, 0, kNT);
+                                           off + 4 * RS::word(C), 0, 0, kNT);
 #endif
-  if constexpr (C + 1 < RS::nc) ring_row_loads<BITS, C + 1>(rc, row, off, soff);
+  if constexpr (C + 1 < RS::nc) ring_row_loads<BITS, C + 1>(rc, row, off);
 }
 
 // Load-side position of a 16-lane task row in its workgroup's task list
@@ -534,22 +544,27 @@ __device__ __forceinline__ void ring_row_loads(rsrc_t rc, uint8_t *row, uint32_t
 template <int BITS>
 struct RingCursor {
   using RS = Ring<BITS>;
-  rsrc_t rc, rsc, rz;
+  rsrc_t rc, rc1, rsc, rz;   // rc1: the codes from the workgroup's second row on
   uint8_t *ring;
   int wave, KS, ds;
-  uint32_t row_bytes, dco, wco, dso, wso;
+  uint32_t dco, wco, dso, wso;
   int ls;
   uint32_t lco;   // byte offset of this lane's code words, row 0 of the task
-  uint32_t lso;   // byte offset of the scale/zero pair this lane fetches (lanes 0..3 of a task)
+  uint32_t lso;   // byte offset of the scale/zero this lane fetches (lanes 0..7 of a task)
 
   template <int D>
   __device__ __forceinline__ void issue() {
     uint8_t *slot = ring + (D * (kStreamThreads / 64) + wave) * RS::slot;
-    ring_row_loads<BITS>(rc, slot, lco, 0u);
-    ring_row_loads<BITS>(rc, slot + RS::row, lco, row_bytes);
+    // row 2p + 1 at the same offset from the second row: past the last row
+    // (an odd row count) it is out of range and reads zero
+    ring_row_loads<BITS>(rc, slot, lco);
+    ring_row_loads<BITS>(rc1, slot + RS::row, lco);
 #if defined(__HIP_DEVICE_COMPILE__)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsc, (lds_ptr_t)(slot + RS::codes), 4, lso, 0, 0, kNT);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rz, (lds_ptr_t)(slot + RS::codes + 256), 4, lso, 0, 0, kNT);
+    // one fp16 per lane, zero-extended to 4 bytes at slot + 4 L: a 2-byte
+    // load never reaches past the end of its range (a load that does
+    // returns zero as a whole)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsc, (lds_ptr_t)(slot + RS::codes), 2, lso, 0, 0, kNT);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rz, (lds_ptr_t)(slot + RS::codes + 256), 2, lso, 0, 0, kNT);
 #endif
     ls += ds;
     const bool wrap = ls >= KS;
@@ -619,9 +634,9 @@ __device__ __forceinline__ void read_task(uint32_t xa, uint32_t sza, uint32_t ca
   "ds_read_b128 %[x3], %[xa] offset:48\n\t" \
   "ds_read_b64 %[xq], %[xa] offset:64\n\t" \
   "ds_read_u16 %[s0], %[sza]\n\t"       \
-  "ds_read_u16 %[s1], %[sza] offset:8\n\t" \
+  "ds_read_u16 %[s1], %[sza] offset:16\n\t" \
   "ds_read_u16 %[z0], %[sza] offset:256\n\t" \
-  "ds_read_u16 %[z1], %[sza] offset:264\n\t"
+  "ds_read_u16 %[z1], %[sza] offset:272\n\t"
 #define WQ_OPS_OUT                                                                                      \
   [x0] "=&v"(o.x[0]), [x1] "=&v"(o.x[1]), [x2] "=&v"(o.x[2]), [x3] "=&v"(o.x[3]), [xq] "=&v"(o.xq),     \
       [s0] "=&v"(o.s0), [s1] "=&v"(o.s1), [z0] "=&v"(o.z0), [z1] "=&v"(o.z1)
@@ -729,41 +744,40 @@ __device__ __forceinline__ void stream_ring(const LinDesc &L, int r0, int rows, 
   uint8_t *ring = lds + lay.ring;
   const int steps = (T + kRG - 1) / kRG;   // steps of this workgroup (uniform)
 
-  // 1. the first R steps of the weight stream, before anything else.  Task
-  //    tau = rg + 64 i is (row pair tau / KS, segment tau % KS).
+  // 1. the weight stream's cursor.  Task tau = rg + 64 i is (row pair
+  //    tau / KS, segment tau % KS).
   RingCursor<BITS> cur;
   {
     const uint32_t row_bytes = (uint32_t)wpr * 4, pair_bytes = 2 * row_bytes;
     const uint32_t seg_step = 16 * BITS * 4;
     const int ds = kRG % KS, dp = kRG / KS;
     cur.rc = make_rsrc(L.codes + (size_t)r0 * wpr, (uint32_t)rows * row_bytes);
-    // scale/zero ranges rounded up to the 4-byte loads: the extra bytes share
-    // the last valid 4-byte granule and only feed lanes that are masked off
-    const uint32_t szb = ((uint32_t)rows * G * 2 + 3u) & ~3u;
+    cur.rc1 = make_rsrc(L.codes + (size_t)(r0 + 1) * wpr, (uint32_t)(rows - 1) * row_bytes);
+    const uint32_t szb = (uint32_t)rows * G * 2;
     cur.rsc = make_rsrc(L.scales + (size_t)r0 * G, szb);
     cur.rz = make_rsrc(L.zeros + (size_t)r0 * G, szb);
     cur.ring = ring;
     cur.wave = wave;
     cur.KS = KS;
     cur.ds = ds;
-    cur.row_bytes = row_bytes;
     cur.dco = (uint32_t)dp * pair_bytes + (uint32_t)ds * seg_step;
     cur.wco = cur.dco + pair_bytes - (uint32_t)KS * seg_step;
     cur.dso = (uint32_t)(2 * (2 * dp * G + 4 * ds));
     cur.wso = cur.dso + (uint32_t)(2 * (2 * G - 4 * KS));
     cur.ls = rg % KS;
     cur.lco = (uint32_t)(rg / KS) * pair_bytes + (uint32_t)cur.ls * seg_step + (uint32_t)j * (BITS * 4);
-    // lanes j < 4 fetch the scales/zeros of row 2p + (j >> 1), groups 4s + 2(j & 1) + {0, 1};
+    // lanes j < 8 fetch the scale/zero of row 2p + (j >> 2), group 4s + (j & 3);
     // the other lanes start past any resource (2^31) and stay there as the offset advances
-    cur.lso = (uint32_t)(2 * (2 * (rg / KS) * G + 4 * cur.ls) + (j >> 1) * 2 * G + (j & 1) * 4);
-    if (j >= 4) cur.lso = kOOB;
+    cur.lso = (uint32_t)(2 * (2 * (rg / KS) * G + 4 * cur.ls) + (j >> 2) * 2 * G + (j & 3) * 2);
+    if (j >= 8) cur.lso = kOOB;
   }
-  if (steps > 0) cur.template issue<0>();
-  if constexpr (R > 1) if (steps > 1) cur.template issue<1>();
-  if constexpr (R > 2) if (steps > 2) cur.template issue<2>();
-  if constexpr (R > 3) if (steps > 3) cur.template issue<3>();
 
-  // 2. activations and signs, then the rotation into LDS
+  // 2. activations and signs first: the loads complete in order, so
+  //    activations requested after the weight stream would wait for it.
+  //    Then the first R steps of the weight stream, issued unconditionally
+  //    (a slot past the workgroup's steps reads out of range: zeros, no
+  //    traffic), which keeps the compiler's wait for the activations exact
+  //    (it counts the stream's loads as younger), then the rotation into LDS.
   const rsrc_t rx = make_rsrc(L.x, (uint32_t)K * 2);
   const rsrc_t rsg = make_rsrc(L.signs, L.signs ? (uint32_t)(K / 8) : 0u);
   const bool rotate = L.signs != nullptr;
@@ -777,6 +791,10 @@ __device__ __forceinline__ void stream_ring(const LinDesc &L, int r0, int rows, 
     xr[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, xo, 0, 0));
     sw[q] = rotate ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsg, so, 0, 0) : 0u;
   }
+  cur.template issue<0>();
+  if constexpr (R > 1) cur.template issue<1>();
+  if constexpr (R > 2) cur.template issue<2>();
+  if constexpr (R > 3) cur.template issue<3>();
 #pragma unroll
   for (int q = 0; q < XC; ++q) {
     consume(xr[q], sw[q]);
@@ -808,7 +826,7 @@ __device__ __forceinline__ void stream_ring(const LinDesc &L, int r0, int rows, 
   const uint32_t dpa = (uint32_t)((2 * dp * KS + ds) * 4), wpa = dpa + (uint32_t)(KS * 4);
   int cs = cs0;   // only needed to mask slices of a partial last segment
   const uint8_t *slot0 = ring + wave * RS::slot;
-  const uint32_t sza_l = lds_addr(slot0 + RS::codes + (lane & 48) * 4 + (j >> 2) * 2);
+  const uint32_t sza_l = lds_addr(slot0 + RS::codes + (lane & 48) * 4 + (j >> 2) * 4);
   const uint32_t ca16_l = lds_addr(slot0) + lane * 16, ca4_l = lds_addr(slot0) + lane * 4;
   constexpr uint32_t kStage = (kStreamThreads / 64) * RS::slot;   // bytes between ring stages
   // one step i in ring slot D (a compile-time constant, so slot addresses fold)
@@ -822,7 +840,7 @@ __device__ __forceinline__ void stream_ring(const LinDesc &L, int r0, int rows, 
         TaskOps o;
         uint32_t cw[2][BITS];
         // scales/zeros of this lane's group (rows 0, 1) were fetched by lanes
-        // 0..3 of its task: 4 bytes each at task * 64 + 4 * (2 row + group / 2)
+        // 0..7 of its task: 4 bytes each at task * 64 + 4 * (4 row + group)
         read_task<BITS>(sv ? xa : lds_addr(xp), sza_l + d * kStage, ca16_l + d * kStage, ca4_l + d * kStage, o, cw);
         uint32_t xv[16];
 #pragma unroll

@@ -150,9 +150,11 @@ def test_linear_bits_by_batch(bits, m):
 @pytest.mark.parametrize("n,k", [(1, 128), (17, 384), (130, 2560), (64, 9728), (300, 640)])
 @pytest.mark.parametrize("rht", [True, False])
 @pytest.mark.parametrize("out_f32", [False, True])
-def test_linear_shapes(n, k, rht, out_f32):
-    say(f"linear n={n} k={k} rht={rht} f32={out_f32}")
-    _run_case(n, k, 3, 4, rht, out_f32, n + k)
+@pytest.mark.parametrize("m", [1, 3])
+def test_linear_shapes(n, k, rht, out_f32, m):
+    # m = 1 runs the LDS-ring kernel: odd n leaves a row pair with one row
+    say(f"linear n={n} k={k} m={m} rht={rht} f32={out_f32}")
+    _run_case(n, k, m, 4, rht, out_f32, n + k + m)
 
 
 # ---------------------------------------------------------- matrix-core path
