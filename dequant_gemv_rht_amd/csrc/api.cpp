@@ -169,6 +169,7 @@ wq_status run_gemv(int count, const wq_weight *w, const uint16_t *const *x, cons
                    bool rotate, hipStream_t s) {
   wq::GemvArgs a;
   memset(&a, 0, sizeof a);
+  for (int i = 0; i < wq::kMaxBatch; ++i) a.first_tile[i] = INT32_MAX;
   a.count = count;
   a.m = (int32_t)m;
   // longest rows first, so the longest workgroups start first
@@ -207,7 +208,12 @@ wq_status run_gemv(int count, const wq_weight *w, const uint16_t *const *x, cons
     L.mode = p.mode;
     L.row_blocks = p.row_blocks;
     L.out_f32 = ydt[i] == WQ_F32;
+    {
+      const int64_t ks = (w[i].k + wq::kSeg - 1) / wq::kSeg;
+      L.ks_inv = (int32_t)((65536 + ks - 1) / ks);
+    }
     L.tile_begin = (int32_t)tiles;
+    a.first_tile[o] = (int32_t)tiles;
     if (stream) {
       L.rows_per_wg = rpw[o];
       tiles += wg[o];

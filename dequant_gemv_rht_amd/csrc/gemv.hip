@@ -131,14 +131,6 @@ __device__ __forceinline__ void pairs_in_dot_order(const float (&v)[8], uint32_t
 }
 
 
-template <typename T>
-__device__ __forceinline__ T select_desc(const GemvArgs &a, int l) {
-  T L = a.lin[0];
-#pragma unroll
-  for (int i = 1; i < kMaxBatch; ++i)
-    if (i == l) L = a.lin[i];
-  return L;
-}
 
 __device__ __forceinline__ void store_out(const LinDesc &L, int m, int row, float v) {
   if (L.out_f32) {
@@ -424,11 +416,7 @@ template <int BITS, int MT>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
   extern __shared__ uint32_t smem[];
   const int tile = blockIdx.x;
-  int l = 0;
-#pragma unroll
-  for (int i = 1; i < kMaxBatch; ++i)
-    if (i < a.count && tile >= a.lin[i].tile_begin) l = i;
-  const LinDesc L = select_desc<LinDesc>(a, l);
+  const LinDesc L = fetch_desc(a, tile);
   const int rb = tile - L.tile_begin;
   const size_t wpr = (size_t)(L.k / kSlice) * BITS;
   using Sh = Shape<BITS, MT>;
@@ -444,11 +432,7 @@ template <int MT>
 __global__ __launch_bounds__(kThreads) void gemv_mixed_kernel(GemvArgs a) {
   extern __shared__ uint32_t smem[];
   const int tile = blockIdx.x;
-  int l = 0;
-#pragma unroll
-  for (int i = 1; i < kMaxBatch; ++i)
-    if (i < a.count && tile >= a.lin[i].tile_begin) l = i;
-  const LinDesc L = select_desc<LinDesc>(a, l);
+  const LinDesc L = fetch_desc(a, tile);
   const int rb = tile - L.tile_begin;            // 16-row tile
   const int blk = rb >> 2;                        // 64-row block
   const int bits = L.block_bits[blk];

@@ -160,14 +160,6 @@ __device__ __forceinline__ void pairs_in_dot_order(const float (&v)[8], uint32_t
   }
 }
 
-template <typename T>
-__device__ __forceinline__ T select_desc(const GemvArgs &a, int l) {
-  T L = a.lin[0];
-#pragma unroll
-  for (int i = 1; i < kMaxBatch; ++i)
-    if (i == l) L = a.lin[i];
-  return L;
-}
 
 __device__ __forceinline__ void store_out(const LinDesc &L, int m, int row, float v) {
   if (L.out_f32) {
@@ -527,7 +519,7 @@ typedef __attribute__((address_space(3))) void *lds_ptr_t;
 // read zero.  The whole offset is in the vector operand: the range check of
 // a raw buffer load does not include the scalar offset.
 template <int BITS, int C = 0>
-__device__ __forceinline__ void ring_row_loads(rsrc_t rc, uint8_t *row, uint32_t off) {
+__device__ __forceinline__ void ring_row_loads(rsrc_t rc, uint32_t row, uint32_t off) {
   using RS = Ring<BITS>;
 #if defined(__HIP_DEVICE_COMPILE__)   // 16-byte LDS loads exist only in the gfx950 pass
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (lds_ptr_t)(row + 256 * RS::word(C)), RS::size(C),
@@ -545,8 +537,8 @@ template <int BITS>
 struct RingCursor {
   using RS = Ring<BITS>;
   rsrc_t rc, rc1, rsc, rz;   // rc1: the codes from the workgroup's second row on
-  uint8_t *ring;
-  int wave, KS, ds;
+  uint32_t slot0;            // LDS address of the wave's slot in stage 0
+  int KS, ds;
   uint32_t dco, wco, dso, wso;
   int ls;
   uint32_t lco;   // byte offset of this lane's code words, row 0 of the task
@@ -554,7 +546,7 @@ struct RingCursor {
 
   template <int D>
   __device__ __forceinline__ void issue() {
-    uint8_t *slot = ring + (D * (kStreamThreads / 64) + wave) * RS::slot;
+    const uint32_t slot = slot0 + D * (kStreamThreads / 64) * RS::slot;
     // row 2p + 1 at the same offset from the second row: past the last row
     // (an odd row count) it is out of range and reads zero
     ring_row_loads<BITS>(rc, slot, lco);
@@ -741,70 +733,73 @@ __device__ __forceinline__ void stream_ring(const LinDesc &L, int r0, int rows, 
   uint8_t *lds = reinterpret_cast<uint8_t *>(smem);
   uint32_t *xp = smem;
   float *part = reinterpret_cast<float *>(lds + lay.part);
-  uint8_t *ring = lds + lay.ring;
   const int steps = (T + kRG - 1) / kRG;   // steps of this workgroup (uniform)
+  const int nb = K / kGroup, items = nb;
 
-  // 1. the weight stream's cursor.  Task tau = rg + 64 i is (row pair
-  //    tau / KS, segment tau % KS).
+  // 1. activations and signs first: loads complete in order, so activations
+  //    requested after the weight stream would wait for it.  Item it = rg +
+  //    64 q is rotation block it; lane j holds its elements 8j .. 8j + 7.
+  //    Without signs the sign range is empty and the loads read zero.
+  const rsrc_t rx = make_rsrc(L.x, (uint32_t)K * 2);
+  const rsrc_t rsg = make_rsrc(L.signs, L.signs ? (uint32_t)(K / 8) : 0u);
+  const bool rotate = L.signs != nullptr;
+  u32x4 xr[XC];
+  uint32_t sw[XC];
+#pragma unroll
+  for (int q = 0; q < XC; ++q) {
+    const int it = rg + kRG * q;
+    const bool ok = it < items;
+    xr[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, ok ? (uint32_t)(256 * it + 16 * j) : kOOB, 0, 0));
+    sw[q] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsg, ok ? (uint32_t)(16 * it + 4 * (j >> 2)) : kOOB, 0, 0);
+  }
+
+  // 2. the weight stream's cursor.  Task tau = rg + 64 i is (row pair
+  //    tau / KS, segment tau % KS); quotients by KS of numbers up to 64 are
+  //    (x * ks_inv) >> 16 exactly.  The first R steps are issued
+  //    unconditionally (a slot past the workgroup's steps reads out of range:
+  //    zeros, no traffic), which keeps the compiler's wait for the
+  //    activations exact (it counts the stream's loads as younger).
+  const int cp0 = (int)(__umul24((uint32_t)rg, (uint32_t)L.ks_inv) >> 16), cs0 = rg - cp0 * KS;
+  const int dp = (kRG * L.ks_inv) >> 16, ds = kRG - dp * KS;
   RingCursor<BITS> cur;
   {
     const uint32_t row_bytes = (uint32_t)wpr * 4, pair_bytes = 2 * row_bytes;
     const uint32_t seg_step = 16 * BITS * 4;
-    const int ds = kRG % KS, dp = kRG / KS;
     cur.rc = make_rsrc(L.codes + (size_t)r0 * wpr, (uint32_t)rows * row_bytes);
     cur.rc1 = make_rsrc(L.codes + (size_t)(r0 + 1) * wpr, (uint32_t)(rows - 1) * row_bytes);
     const uint32_t szb = (uint32_t)rows * G * 2;
     cur.rsc = make_rsrc(L.scales + (size_t)r0 * G, szb);
     cur.rz = make_rsrc(L.zeros + (size_t)r0 * G, szb);
-    cur.ring = ring;
-    cur.wave = wave;
+    cur.slot0 = lds_addr(lds + lay.ring) + (uint32_t)(wave * RS::slot);
     cur.KS = KS;
     cur.ds = ds;
     cur.dco = (uint32_t)dp * pair_bytes + (uint32_t)ds * seg_step;
     cur.wco = cur.dco + pair_bytes - (uint32_t)KS * seg_step;
     cur.dso = (uint32_t)(2 * (2 * dp * G + 4 * ds));
     cur.wso = cur.dso + (uint32_t)(2 * (2 * G - 4 * KS));
-    cur.ls = rg % KS;
-    cur.lco = (uint32_t)(rg / KS) * pair_bytes + (uint32_t)cur.ls * seg_step + (uint32_t)j * (BITS * 4);
+    cur.ls = cs0;
+    cur.lco = __umul24((uint32_t)cp0, pair_bytes) + (uint32_t)cs0 * seg_step + (uint32_t)j * (BITS * 4);
     // lanes j < 8 fetch the scale/zero of row 2p + (j >> 2), group 4s + (j & 3);
-    // the other lanes start past any resource (2^31) and stay there as the offset advances
-    cur.lso = (uint32_t)(2 * (2 * (rg / KS) * G + 4 * cur.ls) + (j >> 2) * 2 * G + (j & 3) * 2);
-    if (j >= 8) cur.lso = kOOB;
-  }
-
-  // 2. activations and signs first: the loads complete in order, so
-  //    activations requested after the weight stream would wait for it.
-  //    Then the first R steps of the weight stream, issued unconditionally
-  //    (a slot past the workgroup's steps reads out of range: zeros, no
-  //    traffic), which keeps the compiler's wait for the activations exact
-  //    (it counts the stream's loads as younger), then the rotation into LDS.
-  const rsrc_t rx = make_rsrc(L.x, (uint32_t)K * 2);
-  const rsrc_t rsg = make_rsrc(L.signs, L.signs ? (uint32_t)(K / 8) : 0u);
-  const bool rotate = L.signs != nullptr;
-  const int nb = K / kGroup, items = nb;
-  u32x4 xr[XC];
-  uint32_t sw[XC];
-#pragma unroll
-  for (int q = 0; q < XC; ++q) {
-    uint32_t xo, so;
-    item_offsets<1>(L, nb, items, rg + kRG * q, j, xo, so);
-    xr[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, xo, 0, 0));
-    sw[q] = rotate ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsg, so, 0, 0) : 0u;
+    // the other lanes start past any resource (bit 31 set) and stay there as the offset advances
+    cur.lso = (__umul24((uint32_t)(2 * cp0 + (j >> 2)), (uint32_t)(2 * G)) + (uint32_t)(8 * cs0 + 2 * (j & 3))) |
+              (j < 8 ? 0u : kOOB);
   }
   cur.template issue<0>();
   if constexpr (R > 1) cur.template issue<1>();
   if constexpr (R > 2) cur.template issue<2>();
   if constexpr (R > 3) cur.template issue<3>();
+
+  // 3. the rotation into LDS
 #pragma unroll
   for (int q = 0; q < XC; ++q) {
     consume(xr[q], sw[q]);
     rotate_item<BITS, 1, true>(rotate, xr[q], sw[q], nb, items, rg + kRG * q, j, xp, nullptr, S);
   }
   for (int it0 = kRG * XC; it0 < items; it0 += kRG) {
-    uint32_t xo, so;
-    item_offsets<1>(L, nb, items, it0 + rg, j, xo, so);
-    const u32x4 raw = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, xo, 0, 0));
-    const uint32_t w1 = rotate ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsg, so, 0, 0) : 0u;
+    const int it = it0 + rg;
+    const bool ok = it < items;
+    const u32x4 raw = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, ok ? (uint32_t)(256 * it + 16 * j) : kOOB, 0, 0));
+    const uint32_t w1 = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsg, ok ? (uint32_t)(16 * it + 4 * (j >> 2)) : kOOB, 0, 0);
     consume(raw, w1);
     rotate_item<BITS, 1, true>(rotate, raw, w1, nb, items, it0 + rg, j, xp, nullptr, S);
   }
@@ -816,18 +811,15 @@ __device__ __forceinline__ void stream_ring(const LinDesc &L, int r0, int rows, 
   // 16 cs + j) and, for lanes 0 and 1, the address of row 2 cp + j's partial
   // for segment cs.  Both advance by a step's (dp pairs, ds segments), with
   // one compare for the segment wrap.
-  const int ds = kRG % KS, dp = kRG / KS;
   constexpr uint32_t kSegBytes = 16 * kSliceStride * 4;
-  const int cs0 = rg % KS, cp0 = rg / KS;
   uint32_t xa = lds_addr(xp) + (uint32_t)(j * kSliceStride * 4) + (uint32_t)cs0 * kSegBytes;
   const uint32_t xa_end = lds_addr(xp) + (uint32_t)(j * kSliceStride * 4) + (uint32_t)KS * kSegBytes;
   uint32_t pa = lds_addr(part) + (uint32_t)((((2 * cp0 + (j & 1)) * KS) + cs0) * 4);
   const uint32_t dxa = (uint32_t)ds * kSegBytes, wxa = (uint32_t)KS * kSegBytes;
   const uint32_t dpa = (uint32_t)((2 * dp * KS + ds) * 4), wpa = dpa + (uint32_t)(KS * 4);
   int cs = cs0;   // only needed to mask slices of a partial last segment
-  const uint8_t *slot0 = ring + wave * RS::slot;
-  const uint32_t sza_l = lds_addr(slot0 + RS::codes + (lane & 48) * 4 + (j >> 2) * 4);
-  const uint32_t ca16_l = lds_addr(slot0) + lane * 16, ca4_l = lds_addr(slot0) + lane * 4;
+  const uint32_t sza_l = cur.slot0 + RS::codes + (lane & 48) * 4 + (j >> 2) * 4;
+  const uint32_t ca16_l = cur.slot0 + lane * 16, ca4_l = cur.slot0 + lane * 4;
   constexpr uint32_t kStage = (kStreamThreads / 64) * RS::slot;   // bytes between ring stages
   // one step i in ring slot D (a compile-time constant, so slot addresses fold)
   auto step = [&](auto dconst, int i) {
@@ -900,11 +892,7 @@ template <int BITS, bool FULL>
 __global__ __launch_bounds__(kStreamThreads) void gemv_ring_kernel(GemvArgs a) {
   extern __shared__ uint32_t smem[];
   const int w = blockIdx.x;
-  int l = 0;
-#pragma unroll
-  for (int i = 1; i < kMaxBatch; ++i)
-    if (i < a.count && w >= a.lin[i].tile_begin) l = i;
-  const LinDesc L = select_desc<LinDesc>(a, l);
+  const LinDesc L = fetch_desc(a, w);
   const int r0 = (w - L.tile_begin) * L.rows_per_wg;
   if (r0 >= L.n) return;
   stream_ring<BITS, FULL>(L, r0, min(L.rows_per_wg, L.n - r0), smem);
@@ -923,11 +911,7 @@ template <int BITS, int MT>
 __global__ __launch_bounds__(kStreamThreads) void gemv_stream_kernel(GemvArgs a) {
   extern __shared__ uint32_t smem[];
   const int w = blockIdx.x;
-  int l = 0;
-#pragma unroll
-  for (int i = 1; i < kMaxBatch; ++i)
-    if (i < a.count && w >= a.lin[i].tile_begin) l = i;
-  const LinDesc L = select_desc<LinDesc>(a, l);
+  const LinDesc L = fetch_desc(a, w);
   const int r0 = (w - L.tile_begin) * L.rows_per_wg;
   if (r0 >= L.n) return;
   const int rows = min(L.rows_per_wg, L.n - r0);

@@ -37,9 +37,11 @@ struct LinDesc {
   int32_t row_blocks;
   int32_t tile_begin;           // first workgroup of this linear in the grid
   int32_t out_f32;
+  int32_t ks_inv;               // ceil(2^16 / KS), KS = ceil(k / 512): x / KS = (x * ks_inv) >> 16 for x <= 64
 };
 
 struct GemvArgs {
+  int32_t first_tile[kMaxBatch];  // lin[i].tile_begin, packed; INT32_MAX past count
   LinDesc lin[kMaxBatch];
   int32_t count;
   int32_t m;                    // batch rows actually present (<= MT)
@@ -224,6 +226,21 @@ __device__ __forceinline__ uint32_t pack_half2(float lo, float hi) {
 
 __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+// The descriptor of the linear that workgroup (or tile) w belongs to.  Its
+// fields are all read in one round of scalar loads: read where first used,
+// each would wait for its own round trip to the argument block, and the
+// first weight load waits for the pointers.
+__device__ __forceinline__ LinDesc fetch_desc(const GemvArgs &a, int w) {
+  int l = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxBatch; ++i)
+    if (w >= a.first_tile[i]) l = i;
+  const LinDesc L = a.lin[l];
+  asm volatile("" ::"s"(L.codes), "s"(L.scales), "s"(L.zeros), "s"(L.signs), "s"(L.x), "s"(L.y), "s"(L.ldx),
+               "s"(L.ldy), "s"(L.n), "s"(L.k), "s"(L.rows_per_wg), "s"(L.tile_begin), "s"(L.out_f32));
+  return L;
 }
 
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
