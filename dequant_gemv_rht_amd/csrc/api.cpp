@@ -104,46 +104,43 @@ int device_cus() {
 constexpr int kMaxLds = 160 * 1024;
 
 // Persistent stream kernel plan: workgroups (one per CU) split among the
-// linears in proportion to their bytes; each gets an even number of rows.
-bool plan_stream(int count, const wq_weight *w, int64_t m, int *wg, int *rows_per_wg, int *lds, bool *ring) {
+// linears so that their estimated times match; each gets an even number of
+// rows.  A workgroup's time is its weight bytes plus its activation
+// preparation, which it does before any weight can be used: each SIMD
+// (4 waves of 4 16-lane rows) takes ceil(items / 16) rounds over the
+// linear's 128-blocks (times the batch tile), about 0.25 us per round with
+// the rotation (~185 vector instructions per block), which is what a CU
+// streams of weights in that time (~32 KB/us): 8 KB per round; without the
+// rotation ~70 instructions, 3 KB.
+bool plan_stream(int count, const wq_weight *w, int64_t m, bool rotate, int *wg, int *rows_per_wg, int *lds,
+                 bool *ring) {
   const int mt = mtile(m);
   if (w[0].bits == 0 || mt > 4) return false;
   const int ncu = device_cus();
   if (count > ncu) return false;
-  double bytes[WQ_MAX_BATCH], total = 0;
+  const double round_bytes = rotate ? 8192.0 : 3072.0;
+  double bytes[WQ_MAX_BATCH], prep[WQ_MAX_BATCH];
   int64_t maxwg[WQ_MAX_BATCH];
   for (int i = 0; i < count; ++i) {
     bytes[i] = (double)w[i].n * (double)w[i].k * (w[i].bits / 8.0 + 4.0 / 128.0);
-    total += bytes[i];
+    const int64_t items = mt * (w[i].k / wq::kGroup);
+    prep[i] = round_bytes * (double)((items + 15) / 16);
     maxwg[i] = (w[i].n + 1) / 2;
+    wg[i] = 1;
   }
-  int sum = 0;
-  for (int i = 0; i < count; ++i) {
-    int64_t g = (int64_t)(ncu * bytes[i] / total);
-    if (g < 1) g = 1;
-    if (g > maxwg[i]) g = maxwg[i];
-    wg[i] = (int)g;
-    sum += wg[i];
-  }
-  while (sum > ncu) {            // shrink the largest share
-    int b = 0;
-    for (int i = 1; i < count; ++i)
-      if (wg[i] > wg[b]) b = i;
-    if (wg[b] <= 1) return false;
-    --wg[b];
-    --sum;
-  }
-  while (sum < ncu) {            // give spare CUs to the most loaded linear
+  // hand out the CUs one at a time to the linear with the longest estimate
+  for (int sum = count; sum < ncu; ++sum) {
     int b = -1;
-    double best = 0;
-    for (int i = 0; i < count; ++i)
-      if (wg[i] < maxwg[i] && bytes[i] / wg[i] > best) {
-        best = bytes[i] / wg[i];
+    double worst = 0;
+    for (int i = 0; i < count; ++i) {
+      const double est = bytes[i] / wg[i] + prep[i];
+      if (wg[i] < maxwg[i] && est > worst) {
+        worst = est;
         b = i;
       }
+    }
     if (b < 0) break;
     ++wg[b];
-    ++sum;
   }
   *lds = 0;
   int ring_lds = 0;
@@ -185,7 +182,7 @@ wq_status run_gemv(int count, const wq_weight *w, const uint16_t *const *x, cons
   for (int o = 0; o < count; ++o) ws[o] = w[order[o]];
   int wg[WQ_MAX_BATCH], rpw[WQ_MAX_BATCH], slds = 0;
   bool ring = false;
-  const bool stream = plan_stream(count, ws, m, wg, rpw, &slds, &ring);
+  const bool stream = plan_stream(count, ws, m, rotate, wg, rpw, &slds, &ring);
   int64_t tiles = 0;
   int lds = 0;
   for (int o = 0; o < count; ++o) {
