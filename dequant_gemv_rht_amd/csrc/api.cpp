@@ -254,28 +254,82 @@ size_t rotated_bytes(const wq_weight &w, int64_t m) {
 // mixed-width layout stays on the GEMV, in chunks of 16 batch rows.
 bool use_gemm(const wq_weight &w, int64_t m) { return m >= 64 && wq::gemm_available(w.bits); }
 
-size_t gemm_path_workspace(const wq_weight &w, int64_t m) {
-  return rotated_bytes(w, m) + wq::gemm_workspace(w, m);
+// Workspace of a matrix-core launch over `count` linears: each linear's
+// rotated activations (when rotating), then each split linear's fp32
+// partial sums, every part 256-byte aligned.
+struct GemmLayout {
+  size_t rot[WQ_MAX_BATCH], part[WQ_MAX_BATCH], total;
+  int ksplit[WQ_MAX_BATCH];
+};
+
+GemmLayout gemm_layout(int count, const wq_weight *w, int64_t m, bool rotate) {
+  GemmLayout g;
+  wq::gemm_plan(count, w, m, g.ksplit);
+  size_t off = 0;
+  for (int i = 0; i < count; ++i) {
+    g.rot[i] = off;
+    if (rotate && w[i].rht_signs) off += rotated_bytes(w[i], m);
+  }
+  for (int i = 0; i < count; ++i) {
+    g.part[i] = off;
+    off += align256(wq::gemm_partial_bytes(w[i], m, g.ksplit[i]));
+  }
+  g.total = off;
+  return g;
 }
 
-// One validated linear: matrix-core path (rotation into the workspace, then
-// the GEMM) or the GEMV in chunks of 16 batch rows.
+size_t gemm_path_workspace(const wq_weight &w, int64_t m) { return gemm_layout(1, &w, m, true).total; }
+
+// Validated linears on the matrix cores: rotations into the workspace, then
+// one GEMM launch for all of them (plus one launch adding K-split partials).
+wq_status run_gemm(int count, const wq_weight *w, const uint16_t *const *x, const int64_t *ldx, int64_t m,
+                   void *const *y, const wq_dtype *ydt, const int64_t *ldy, bool rotate, void *workspace,
+                   hipStream_t s, const char *who) {
+  const GemmLayout g = gemm_layout(count, w, m, rotate);
+  char *ws = static_cast<char *>(workspace);
+  const uint16_t *xr[WQ_MAX_BATCH];
+  int64_t ldr[WQ_MAX_BATCH], ldo[WQ_MAX_BATCH];
+  int f32[WQ_MAX_BATCH];
+  float *part[WQ_MAX_BATCH];
+  void *yo[WQ_MAX_BATCH];
+  // the rotations of all linears in one launch
+  int nr = 0;
+  const uint16_t *rx[WQ_MAX_BATCH];
+  uint16_t *ry[WQ_MAX_BATCH];
+  const uint32_t *rs[WQ_MAX_BATCH];
+  int64_t rk[WQ_MAX_BATCH], rlx[WQ_MAX_BATCH], rly[WQ_MAX_BATCH];
+  for (int i = 0; i < count; ++i) {
+    xr[i] = x[i];
+    ldr[i] = ldx[i];
+    if (rotate && w[i].rht_signs) {
+      uint16_t *xt = reinterpret_cast<uint16_t *>(ws + g.rot[i]);
+      ldr[i] = rotated_ld(w[i]);
+      rx[nr] = x[i];
+      ry[nr] = xt;
+      rs[nr] = w[i].rht_signs;
+      rk[nr] = w[i].k;
+      rlx[nr] = ldx[i];
+      rly[nr] = ldr[i];
+      ++nr;
+      xr[i] = xt;
+    }
+    part[i] = g.ksplit[i] > 1 ? reinterpret_cast<float *>(ws + g.part[i]) : nullptr;
+    f32[i] = ydt[i] == WQ_F32;
+    ldo[i] = ldy[i];
+    yo[i] = y[i];
+  }
+  if (nr) {
+    const wq_status st = hip_status(wq::launch_rht_batch(nr, rx, ry, rs, m, rk, rlx, rly, s), who);
+    if (st != WQ_OK) return st;
+  }
+  return hip_status(wq::launch_gemm_batch(count, w, xr, ldr, m, yo, f32, ldo, g.ksplit, part, s), who);
+}
+
+// One validated linear: matrix-core path or the GEMV in chunks of 16 batch
+// rows.
 wq_status linear_one(const wq_weight &w, const uint16_t *x, int64_t m, int64_t ldx, void *y, wq_dtype y_dtype,
                      int64_t ldy, bool rotate, void *workspace, hipStream_t s) {
-  if (use_gemm(w, m)) {
-    const uint16_t *xr = x;
-    int64_t ldr = ldx;
-    char *ws = static_cast<char *>(workspace);
-    if (rotate) {
-      uint16_t *xt = reinterpret_cast<uint16_t *>(ws);
-      ldr = rotated_ld(w);
-      wq_status st = hip_status(wq::launch_rht(x, xt, w.rht_signs, m, w.k, ldx, ldr, s), "wq_linear");
-      if (st != WQ_OK) return st;
-      xr = xt;
-    }
-    ws += rotated_bytes(w, m);
-    return hip_status(wq::launch_gemm(w, xr, m, ldr, y, y_dtype == WQ_F32, ldy, ws, s), "wq_linear");
-  }
+  if (use_gemm(w, m)) return run_gemm(1, &w, &x, &ldx, m, &y, &y_dtype, &ldy, rotate, workspace, s, "wq_linear");
   const size_t esz = y_dtype == WQ_F32 ? 4 : 2;
   for (int64_t m0 = 0; m0 < m; m0 += 16) {
     const int64_t mc = (m - m0) < 16 ? (m - m0) : 16;
@@ -415,12 +469,14 @@ size_t wq_linear_batch_workspace(int32_t count, const wq_weight *w, int64_t m) {
     fail(WQ_E_ARG, "wq_linear_batch_workspace: m must be positive");
     return (size_t)-1;
   }
-  size_t need = 0;   // m <= 16: one GEMV launch, no workspace; larger m: the linears in turn share it
+  bool gemm = m > 16;   // m <= 16: one GEMV launch, no workspace
   for (int i = 0; i < count; ++i) {
     if (check_weight(&w[i], "wq_linear_batch_workspace") != WQ_OK) return (size_t)-1;
-    if (m > 16 && use_gemm(w[i], m)) need = std::max(need, gemm_path_workspace(w[i], m));
+    gemm = gemm && use_gemm(w[i], m) && w[i].bits == w[0].bits;
   }
-  return need;
+  // m >= 64 with one uniform width: one matrix-core launch over all of them;
+  // otherwise the GEMV in chunks of 16 rows, one linear after another
+  return gemm ? gemm_layout(count, w, m, true).total : 0;
 }
 
 wq_status wq_linear_batch(int32_t count, const wq_weight *w, const uint16_t *const *x, const int64_t *ldx,
@@ -443,14 +499,16 @@ wq_status wq_linear_batch(int32_t count, const wq_weight *w, const uint16_t *con
   }
   const bool rotate = (flags & WQ_FUSE_RHT) && w[0].rht_signs;
   if (m <= 16) return run_gemv(count, w, x, ldx, m, y, y_dtype, ldy, rotate, (hipStream_t)stream);
-  // larger batches: one linear after another on the stream, sharing the workspace
   const size_t need = wq_linear_batch_workspace(count, w, m);
   if (need == (size_t)-1) return WQ_E_ARG;
   if (need > workspace_bytes || (need && !workspace))
     return fail(WQ_E_WORKSPACE, "wq_linear_batch: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
   if (workspace && !aligned16(workspace))
     return fail(WQ_E_ALIGN, "wq_linear_batch: workspace must be 16-byte aligned");
-  for (int i = 0; i < count; ++i) {
+  if (use_gemm(w[0], m))   // one width (checked above): all on the matrix cores in one launch
+    return run_gemm(count, w, x, ldx, m, y, y_dtype, ldy, rotate, workspace, (hipStream_t)stream,
+                    "wq_linear_batch");
+  for (int i = 0; i < count; ++i) {   // mixed width: the GEMV, one linear after another
     const wq_status st = linear_one(w[i], x[i], m, ldx[i], y[i], y_dtype[i], ldy[i], rotate, workspace,
                                     (hipStream_t)stream);
     if (st != WQ_OK) return st;

@@ -1,5 +1,5 @@
 // Matrix-core path for batch sizes M >= 64 (gfx950): y = x' . W^T with the
-// weight dequantised tile by tile into LDS and multiplied on MFMA
+// weight dequantised in registers and multiplied on MFMA
 // (v_mfma_f32_32x32x16_f16, fp32 accumulate).  Same layer as the GEMV:
 // w = (q - z) s per group of 128 along K (model card "24B0978 - Week 01 -
 // Track 2, 20% target", section "How these techniques accelerate inference
@@ -7,31 +7,42 @@
 // rotated by the block Hadamard transform (the caller runs rht_apply's
 // kernel into the workspace first).
 //
-// Tiling.  A workgroup of 256 threads owns a 128 x 128 tile of y (128 batch
-// rows x 128 output columns) and walks K in steps of 64 (half a group, so a
-// step never straddles two scales).  Per step every thread
-//   - loads 32 activations of one batch row and the 32-code slice of one
-//     weight row (plus that row's scale and zero), one step ahead, into
-//     registers;
-//   - writes them to LDS: the weight slice dequantised to fp16, the
-//     activations permuted into the same k order (below);
-// and each wave multiplies a 64 x 64 sub-tile: 2 x 2 MFMA blocks, 4 k-steps
-// of 16.
+// One launch serves every linear of a batch: workgroups are dealt to the
+// linears by a packed table of first tiles, like the GEMV.
 //
-// Dequantisation.  A code pair is unpacked to two fp16 values 1024 + q (the
-// GEMV's magic-number unpack, one v_and_or_b32), then q = h - 1024 (or
-// h / 16 - 64 for int4 nibbles read in place from bits 4..7), q - z (exact
-// in fp16: |q - z| < 256 and z's ulp keeps the difference within 11
-// significant bits), and (q - z) * s rounded once to fp16.  The pairs come
-// out in the unpacker's order -- int4: codes (0,4) (1,5) (2,6) (3,7) of each
-// word; int8: (0,2) (1,3) of each word; int3 and int6: natural -- so the
-// activations are stored in LDS in the same k order; a dot product does not
-// depend on the order of its terms.
+// Tiling.  A workgroup of 4 waves owns a 128 (batch rows) x 256 (outputs)
+// tile of y and a range of K in steps of 64 (half a group, so a step never
+// straddles two scales); each wave owns 128 x 64 of the tile: 4 x 2 blocks
+// of 32 x 32, 128 fp32 accumulators per lane.  A long K is split over
+// several workgroups whose fp32 partial tiles a second kernel adds.
+//
+// Activations (A operand) travel HBM -> LDS by direct buffer-to-LDS loads,
+// kAhead steps in flight; every wave loads 32 of the tile's 128 rows and a
+// barrier per step publishes them.  In LDS a row is 128 bytes (64 fp16) in
+// eight 16-byte chunks, chunk c of row r stored at slot c ^ (r & 7): the 32
+// lanes reading one chunk of 32 rows then spread over all banks.
+//
+// Weights (B operand) never pass through LDS.  The MFMA wants lane l to hold
+// B[k = 8 (l / 32) .. +8][n = l % 32] of each 16-k block; the four blocks of
+// a 64-k step are free to take any k of the step as long as the activations
+// use the same ones, so lane l takes the step's k = 32 (l / 32) .. +32: the
+// 32-code slice of row n the packing already keeps contiguous (int4: one
+// 16-byte load).  Codes become fp16 in natural k order -- int4: v_perm_b32
+// puts a code byte into both halves, one v_and_or_b32 masks the low nibble
+// into the low half and the high nibble into bits 4..7 of the high half, each
+// over 1024.0's bit pattern (1024 + q, 1024 + 16 q); int8: v_perm_b32 places
+// two bytes next to 0x64 bytes; int3/int6: bit fields spread over the two
+// halves -- then q exactly with one packed fma, q - z and times s in fp16.
 //
 // MFMA operand layout (checked on the device): lane l holds A[l % 32][8 (l /
 // 32) .. +8] and B[8 (l / 32) .. +8][l % 32]; accumulator register v of lane
 // l is C[8 (v / 4) + 4 (l / 32) + v % 4][l % 32].
 #include "wq_internal.h"
+
+#include <algorithm>
+#include <climits>
+#include <cstring>
+#include <type_traits>
 
 namespace wq {
 using namespace dev;
@@ -41,29 +52,73 @@ namespace {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
 
-constexpr int kBM = 128, kBN = 128, kBK = 64;
-constexpr int kLdk = kBK + 8;              // halfs per LDS row (144 bytes: spreads the 32 rows over the banks)
-constexpr int kGemmThreads = 256;
-constexpr uint32_t kMagic = 0x64006400u;   // two fp16 1024.0
+constexpr int kTM = 128, kTN = 256, kBK = 64;
+constexpr int kWaves = 4, kGemmThreads = 64 * kWaves;
+constexpr int kStages = 3;                    // steps in flight + 1: activation stages in LDS, weight register sets
+constexpr int kAhead = kStages - 1;           // steps loaded ahead of the one computed
 
+// LDS slot of 16-byte chunk c of activation row r
+__device__ __forceinline__ int a_slot(int c, int r) { return c ^ (r & 7); }
+constexpr int kAStage = kTM * kBK * 2;        // 16 KB per step
+constexpr uint32_t kMagic = 0x64006400u;      // two fp16 1024.0
+
+struct GemmLin {
+  const uint32_t *codes;
+  const uint16_t *scales, *zeros;
+  const uint16_t *x;     // rotated activations [m][ldx]
+  void *y;
+  float *part;           // ksplit > 1: fp32 partial tiles [ksplit][m][n]
+  int64_t ldx, ldy;
+  int32_t m, n, k, out_f32;
+  int32_t mtiles, ntiles, ksplit, ksteps;   // ksteps: 64-k steps per split
+  int32_t tile_begin;
+};
+
+struct GemmBatch {
+  int32_t first_tile[kMaxBatch];   // lin[i].tile_begin, packed; INT32_MAX past count
+  GemmLin lin[kMaxBatch];
+  int32_t count, tiles;
+};
+
+__device__ __forceinline__ half2v as_h2(uint32_t v) { return __builtin_bit_cast(half2v, v); }
+__device__ __forceinline__ uint32_t as_u32(half2v v) { return __builtin_bit_cast(uint32_t, v); }
+
+// A lane's 32-code slice (BITS words) of one weight row: vector offset
+// `off` (the row, range checked), scalar offset `so` (the slice in the row).
 template <int BITS>
-__device__ __forceinline__ void load_codes(rsrc_t rs, uint32_t off, uint32_t (&w)[BITS]) {
+__device__ __forceinline__ void load_slice(rsrc_t rs, uint32_t off, uint32_t so, uint32_t (&w)[BITS]) {
   if constexpr (BITS == 4) {
-    const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+    const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, so, 0));
     w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
   } else if constexpr (BITS == 8) {
-    const u32x4 a = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
-    const u32x4 b = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16, 0, 0));
+    const u32x4 a = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, so, 0));
+    const u32x4 b = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16, so, 0));
     w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w; w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
   } else if constexpr (BITS == 6) {
-    const u32x4 a = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
-    const u32x2 b = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, off + 16, 0, 0));
+    const u32x4 a = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, so, 0));
+    const u32x2 b = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, off + 16, so, 0));
     w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w; w[4] = b.x; w[5] = b.y;
   } else {
-    const u32x3 v = __builtin_bit_cast(u32x3, __builtin_amdgcn_raw_buffer_load_b96(rs, off, 0, 0));
+    const u32x3 v = __builtin_bit_cast(u32x3, __builtin_amdgcn_raw_buffer_load_b96(rs, off, so, 0));
     w[0] = v.x; w[1] = v.y; w[2] = v.z;
   }
+}
+
+// Mask and bias of the unpack, held in VGPRs so that one v_and_or_b32 takes
+// both (a VOP3 instruction encodes at most one literal).
+struct PairConsts {
+  uint32_t mask, bias;
+};
+
+template <int BITS>
+__device__ __forceinline__ PairConsts pair_consts() {
+  constexpr uint32_t m = BITS == 4 ? 0x00F0000Fu : BITS == 3 ? 0x00070007u : 0x003F003Fu;
+  PairConsts c;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(c.mask) : "i"(m));
+  asm volatile("v_mov_b32 %0, %1" : "=v"(c.bias) : "i"(kMagic));
+  return c;
 }
 
 template <int BIT, int WIDTH, int N>
@@ -76,227 +131,372 @@ __device__ __forceinline__ uint32_t bits_at(const uint32_t (&w)[N]) {
   }
 }
 
-// Code pair P of a 32-code slice as two fp16 values 1024 + q (int4 pairs
-// with P % 4 odd: 1024 + 16 q).
+// Codes 2P and 2P + 1 of the slice as two fp16 values over 1024: (1024 +
+// q0, 1024 + q1), int4: (1024 + q0, 1024 + 16 q1).
 template <int BITS, int P>
-__device__ __forceinline__ uint32_t code_pair(const uint32_t (&w)[BITS]) {
+__device__ __forceinline__ uint32_t code_pair(const uint32_t (&w)[BITS], PairConsts k) {
   if constexpr (BITS == 4) {
-    constexpr int wi = P / 4, r = P % 4;
-    const uint32_t v = (r < 2) ? w[wi] : (w[wi] >> 8);
-    return (r & 1) ? ((v & 0x00F000F0u) | kMagic) : ((v & 0x000F000Fu) | kMagic);
+    constexpr int wi = P / 4, b = P % 4;    // byte b of word wi holds codes 2P (low nibble), 2P + 1
+    const uint32_t t = __builtin_amdgcn_perm(w[wi], w[wi], (uint32_t)(b | (b << 8) | (b << 16) | (b << 24)));
+    return (t & k.mask) | k.bias;
   } else if constexpr (BITS == 8) {
-    constexpr int wi = P / 2, r = P % 2;
-    return __builtin_amdgcn_perm(0x64646464u, w[wi], r ? 0x04030401u : 0x04020400u);
+    // bytes b, b + 1 of word wi next to byte 1 of the bias (0x64); selectors
+    // 0..3 take bytes of the second operand, 4..7 of the first
+    constexpr int wi = P / 2, b = 2 * (P % 2);
+    return __builtin_amdgcn_perm(k.bias, w[wi], (uint32_t)(b | (5 << 8) | ((b + 1) << 16) | (5 << 24)));
   } else if constexpr (BITS == 3) {
     const uint32_t t = bits_at<6 * P, 6>(w);
-    return ((t | (t << 13)) & 0x00070007u) | kMagic;
+    return ((t | (t << 13)) & k.mask) | k.bias;
   } else {
-    constexpr int run = P / 8, q = P % 8;
+    constexpr int run = P / 8, q = P % 8;    // two 96-bit runs of 16 codes
     const uint32_t t = (run == 0) ? bits_at<12 * q, 12>(w) : bits_at<96 + 12 * q, 12>(w);
-    return ((t | (t << 10)) & 0x003F003Fu) | kMagic;
+    return ((t | (t << 10)) & k.mask) | k.bias;
   }
 }
 
-__device__ __forceinline__ half2v as_h2(uint32_t v) { return __builtin_bit_cast(half2v, v); }
-__device__ __forceinline__ uint32_t as_u32(half2v v) { return __builtin_bit_cast(uint32_t, v); }
-
-// Dequantise pair P: (q - z) * s, fp16.
-template <int BITS, int P>
-__device__ __forceinline__ uint32_t dequant_pair(const uint32_t (&w)[BITS], half2v z, half2v s) {
-  const half2v h = as_h2(code_pair<BITS, P>(w));
-  half2v q;
-  if constexpr (BITS == 4 && (P % 2) == 1) {
-    const half2v k16 = {(_Float16)0.0625f, (_Float16)0.0625f}, m64 = {(_Float16)-64.0f, (_Float16)-64.0f};
-    q = __builtin_elementwise_fma(h, k16, m64);
-  } else {
-    const half2v m1024 = {(_Float16)-1024.0f, (_Float16)-1024.0f};
-    q = h + m1024;
+// The lane's B operand of 16-k block kk: codes 8 kk .. 8 kk + 7 of its slice,
+// dequantised: q = h c + d exactly (c, d per half remove the 1024 offset and
+// the int4 factor 16), then (q - z) s.
+template <int BITS, int KK>
+__device__ __forceinline__ half8 b_operand(const uint32_t (&w)[BITS], PairConsts k, half2v c, half2v d, half2v z,
+                                           half2v s) {
+  uint32_t p[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t h;
+    switch (i) {
+      case 0: h = code_pair<BITS, 4 * KK + 0>(w, k); break;
+      case 1: h = code_pair<BITS, 4 * KK + 1>(w, k); break;
+      case 2: h = code_pair<BITS, 4 * KK + 2>(w, k); break;
+      default: h = code_pair<BITS, 4 * KK + 3>(w, k); break;
+    }
+    const half2v q = __builtin_elementwise_fma(as_h2(h), c, d);
+    p[i] = as_u32((q - z) * s);
   }
-  return as_u32((q - z) * s);
+  return __builtin_bit_cast(half8, u32x4{p[0], p[1], p[2], p[3]});
 }
 
-// Four u32 of natural-order activations (k, k+1), (k+2, k+3), ... permuted
-// into the order the weight pairs of the same 8 codes come out in.
-template <int BITS>
-__device__ __forceinline__ u32x4 permute_acts(u32x4 a) {
-  if constexpr (BITS == 4) {
-    // halves 0..7 -> 0 4 1 5 2 6 3 7
-    return u32x4{__builtin_amdgcn_perm(a.z, a.x, 0x05040100u), __builtin_amdgcn_perm(a.z, a.x, 0x07060302u),
-                 __builtin_amdgcn_perm(a.w, a.y, 0x05040100u), __builtin_amdgcn_perm(a.w, a.y, 0x07060302u)};
-  } else if constexpr (BITS == 8) {
-    // halves 0..7 -> 0 2 1 3 4 6 5 7
-    return u32x4{__builtin_amdgcn_perm(a.y, a.x, 0x05040100u), __builtin_amdgcn_perm(a.y, a.x, 0x07060302u),
-                 __builtin_amdgcn_perm(a.w, a.z, 0x05040100u), __builtin_amdgcn_perm(a.w, a.z, 0x07060302u)};
-  } else {
-    return a;
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// The same wait, also taking a step's weight registers as operands, so that
+// no arithmetic on them is scheduled above it.
+template <int N, int BITS>
+__device__ __forceinline__ void wait_vmcnt_regs(uint32_t (&w)[2][BITS], uint32_t (&sr)[2], uint32_t (&zr)[2]) {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+#pragma unroll
+    for (int e = 0; e < BITS; ++e) asm volatile("" : "+v"(w[j][e]));
+    asm volatile("" : "+v"(sr[j]), "+v"(zr[j]));
   }
 }
 
-struct GemmArgs {
-  const uint32_t *codes;
-  const uint16_t *scales, *zeros;
-  const uint16_t *x;   // rotated activations [m][ldx]
-  void *y;
-  int64_t ldx, ldy;
-  int32_t m, n, k;
-  int32_t mtiles, ntiles;
-  int32_t out_f32;
-};
+__device__ __forceinline__ uint32_t lds_addr(const void *p) { return (uint32_t)(uintptr_t)(lds_ptr_t)p; }
 
-// blockIdx -> (m tile, n tile).  Workgroups are dealt to the 8 XCDs round
-// robin; the mapping puts runs of consecutive tiles (the m tiles of one n
-// tile, which dequantise the same weights) on one XCD so they share its L2.
-__device__ __forceinline__ void tile_of(const GemmArgs &a, int &mt, int &nt) {
-  const int nb = a.mtiles * a.ntiles, b = blockIdx.x;
+// The A operands of one 16-k block for the 4 m blocks (32 rows apart, 4096
+// bytes) of stage ST, read and waited for in one statement.  Reading the
+// direct-loaded tile in asm keeps the compiler from tying these reads to the
+// outstanding direct loads of other stages with waits of its own.
+template <int ST>
+__device__ __forceinline__ void read_a(uint32_t addr, half8 (&a)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %4 offset:%5\n\t"
+      "ds_read_b128 %1, %4 offset:%6\n\t"
+      "ds_read_b128 %2, %4 offset:%7\n\t"
+      "ds_read_b128 %3, %4 offset:%8\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3])
+      : "v"(addr), "i"(ST * kAStage), "i"(ST * kAStage + 4096), "i"(ST * kAStage + 8192),
+        "i"(ST * kAStage + 12288)
+      : "memory");
+}
+
+// Logical tile of workgroup b: runs of consecutive tiles (the m tiles of one
+// n tile and K split, which read the same weights) on one XCD, so they share
+// its L2; workgroups are dealt to the 8 XCDs round robin.
+__device__ __forceinline__ int logical_tile(int b, int nb) {
   const int xcd = b % 8, slot = b / 8, q = nb / 8, rem = nb % 8;
-  const int logical = (xcd < rem ? xcd * (q + 1) : rem * (q + 1) + (xcd - rem) * q) + slot;
-  nt = logical / a.mtiles;
-  mt = logical - nt * a.mtiles;
+  return (xcd < rem ? xcd * (q + 1) : rem * (q + 1) + (xcd - rem) * q) + slot;
 }
 
 template <int BITS>
-__global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[kBM * kLdk];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[kBN * kLdk];
-  int mt, nt;
-  tile_of(a, mt, nt);
-  const int m0 = mt * kBM, n0 = nt * kBN;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int S = a.k / kSlice, G = a.k / kGroup, wpr = S * BITS;
+__global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmBatch a) {
+  __shared__ __attribute__((aligned(16))) uint8_t As[kStages * kAStage];
+  const int tile = logical_tile(blockIdx.x, a.tiles);
+  int l = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxBatch; ++i)
+    if (tile >= a.first_tile[i]) l = i;
+  const GemmLin L = a.lin[l];
+  int local = tile - L.tile_begin;
+  const int mt = local % L.mtiles;
+  local /= L.mtiles;
+  const int nt = local % L.ntiles, ks = local / L.ntiles;
+  const int m0 = mt * kTM, n0 = nt * kTN;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int S = L.k / kSlice, G = L.k / kGroup, wpr = S * BITS;
+  const int kt0 = ks * L.ksteps, T = min(L.ksteps, L.k / kBK - kt0);
 
-  // per-thread load roles: row t / 2 of the tile, 32-wide k half t & 1
-  const int lr = t >> 1, lh = t & 1;
-  const rsrc_t rx = make_rsrc(a.x + (size_t)m0 * a.ldx, (uint32_t)((size_t)min(kBM, a.m - m0) * a.ldx * 2));
-  const int nrows = min(kBN, a.n - n0);
-  const rsrc_t rc = make_rsrc(a.codes + (size_t)n0 * wpr, (uint32_t)nrows * wpr * 4);
-  const rsrc_t rs = make_rsrc(a.scales + (size_t)n0 * G, (uint32_t)nrows * G * 2);
-  const rsrc_t rz = make_rsrc(a.zeros + (size_t)n0 * G, (uint32_t)nrows * G * 2);
+  // Each lane's offsets are fixed for the whole K range (the vector offset,
+  // which the range check covers: rows past M or N read zero); a step's
+  // position goes in the scalar offset, which never takes a load past its
+  // row's end.  Steps past the range reload the range's last step, so every
+  // step issues the same loads and the counts waited on are constants.
+  //
+  // activations: rows m0 .. m0 + 127; this wave loads rows 32 wave + 8 i +
+  // lane / 8 (i = 0..3), chunk slot lane % 8
+  const rsrc_t rx = make_rsrc(L.x + (size_t)m0 * L.ldx, (uint32_t)((size_t)min(kTM, L.m - m0) * L.ldx * 2));
+  const int arow = 32 * wave + (lane >> 3), aslot = lane & 7;
+  uint32_t a_vo[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    a_vo[i] = (uint32_t)((size_t)(arow + 8 * i) * L.ldx * 2) + (uint32_t)(a_slot(aslot, arow + 8 * i) * 16);
+  const uint32_t as0 = lds_addr(As) + (uint32_t)(wave * 4 * 1024);
+  // weights: rows nw0 + 32 j + lane % 32, slice 2 kt + lane / 32 of the row
+  const int nw0 = n0 + 64 * wave;
+  // (uniform: a clamp would otherwise become a vector med3 and the resources divergent)
+  const int nrows = __builtin_amdgcn_readfirstlane(max(0, min(64, L.n - nw0)));
+  const rsrc_t rc = make_rsrc(L.codes + (size_t)nw0 * wpr, (uint32_t)nrows * wpr * 4);
+  const rsrc_t rs = make_rsrc(L.scales + (size_t)nw0 * G, (uint32_t)nrows * G * 2);
+  const rsrc_t rz = make_rsrc(L.zeros + (size_t)nw0 * G, (uint32_t)nrows * G * 2);
+  const int bn = lane & 31, bh = lane >> 5;
+  const uint32_t b_vo0 = (uint32_t)(bn * wpr * 4 + bh * BITS * 4), b_vo1 = b_vo0 + (uint32_t)(32 * wpr * 4);
+  const uint32_t s_vo0 = (uint32_t)(bn * G * 2), s_vo1 = s_vo0 + (uint32_t)(32 * G * 2);
 
-  u32x4 xa[4];
-  uint32_t cw[BITS];
-  uint32_t sraw, zraw;
-  auto load = [&](int kt) {
-    const int k0 = kt * kBK + 32 * lh;
-    const uint32_t xo = (uint32_t)(((size_t)lr * a.ldx + k0) * 2);
+  uint32_t cw[kStages][2][BITS];
+  uint32_t sr[kStages][2], zr[kStages][2];
+  auto issue = [&](auto sconst, int kt) {
+    constexpr int st = decltype(sconst)::value;
+    const int kc = min(kt, kt0 + T - 1);
+    const uint32_t so_a = (uint32_t)kc * (kBK * 2), so_b = (uint32_t)kc * (2 * BITS * 4), so_s = (uint32_t)(kc >> 1) * 2;
+#if defined(__HIP_DEVICE_COMPILE__)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      xa[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, xo + 16 * i, 0, 0));
-    load_codes<BITS>(rc, (uint32_t)((lr * wpr + (k0 / kSlice) * BITS) * 4), cw);
-    const uint32_t so = (uint32_t)((lr * G + k0 / kGroup) * 2);
-    sraw = __builtin_amdgcn_raw_buffer_load_b16(rs, so, 0, 0);
-    zraw = __builtin_amdgcn_raw_buffer_load_b16(rz, so, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr_t)(as0 + st * kAStage + i * 1024), 16, a_vo[i], so_a, 0, 0);
+#endif
+    load_slice<BITS>(rc, b_vo0, so_b, cw[st][0]);
+    load_slice<BITS>(rc, b_vo1, so_b, cw[st][1]);
+    sr[st][0] = __builtin_amdgcn_raw_buffer_load_b16(rs, s_vo0, so_s, 0);
+    sr[st][1] = __builtin_amdgcn_raw_buffer_load_b16(rs, s_vo1, so_s, 0);
+    zr[st][0] = __builtin_amdgcn_raw_buffer_load_b16(rz, s_vo0, so_s, 0);
+    zr[st][1] = __builtin_amdgcn_raw_buffer_load_b16(rz, s_vo1, so_s, 0);
   };
+  // vector-memory operations of one issue, the count waited on
+  constexpr int kLoadsB = BITS == 3 || BITS == 4 ? 1 : 2;
+  constexpr int kIssue = 4 + 2 * kLoadsB + 4;
 
-  f32x16 acc[2][2];
+  f32x16 acc[4][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
-  const int wm = (wave & 1) * 64, wn = (wave >> 1) * 64;
-  const int KT = a.k / kBK;
-  load(0);
-  for (int kt = 0; kt < KT; ++kt) {
-    // registers -> LDS: activations permuted, weights dequantised
-    {
-      u32x4 *dst = reinterpret_cast<u32x4 *>(&As[lr * kLdk + 32 * lh]);
+  // A fragment of m block i, 16-k block kk: row 32 i + lane % 32, k 32 (lane / 32) + 8 kk,
+  // i.e. chunk 4 (lane / 32) + kk of the row at slot chunk ^ (row & 7)
+  const int ar = lane & 31;
+  uint32_t a_rd[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dst[i] = permute_acts<BITS>(xa[i]);
-      const half2v s2 = as_h2((sraw & 0xFFFFu) * 0x10001u), z2 = as_h2((zraw & 0xFFFFu) * 0x10001u);
-      uint32_t p[16];
-      p[0] = dequant_pair<BITS, 0>(cw, z2, s2);   p[1] = dequant_pair<BITS, 1>(cw, z2, s2);
-      p[2] = dequant_pair<BITS, 2>(cw, z2, s2);   p[3] = dequant_pair<BITS, 3>(cw, z2, s2);
-      p[4] = dequant_pair<BITS, 4>(cw, z2, s2);   p[5] = dequant_pair<BITS, 5>(cw, z2, s2);
-      p[6] = dequant_pair<BITS, 6>(cw, z2, s2);   p[7] = dequant_pair<BITS, 7>(cw, z2, s2);
-      p[8] = dequant_pair<BITS, 8>(cw, z2, s2);   p[9] = dequant_pair<BITS, 9>(cw, z2, s2);
-      p[10] = dequant_pair<BITS, 10>(cw, z2, s2); p[11] = dequant_pair<BITS, 11>(cw, z2, s2);
-      p[12] = dequant_pair<BITS, 12>(cw, z2, s2); p[13] = dequant_pair<BITS, 13>(cw, z2, s2);
-      p[14] = dequant_pair<BITS, 14>(cw, z2, s2); p[15] = dequant_pair<BITS, 15>(cw, z2, s2);
-      u32x4 *bd = reinterpret_cast<u32x4 *>(&Bs[lr * kLdk + 32 * lh]);
+  for (int kk = 0; kk < 4; ++kk) a_rd[kk] = lds_addr(As) + (uint32_t)(ar * 128 + (a_slot(4 * bh + kk, ar) << 4));
+  constexpr _Float16 kHi = BITS == 4 ? (_Float16)0.0625f : (_Float16)1.0f;
+  const PairConsts pk = pair_consts<BITS>();
+
+  // One step: the waits, the barrier and the loads are unconditional (a
+  // step past the range only skips the products), so every iteration of the
+  // loop has the same loads in flight and the compiler's own waits for the
+  // weight registers stay as loose as this step's explicit one.
+  auto step = [&](auto sconst, int kt, bool active) {
+    constexpr int st = decltype(sconst)::value;
+    constexpr int nx = (st + kAhead) % kStages;
+    // this step's activations (this wave's rows) and weights: the younger
+    // loads are those of the kAhead - 1 steps issued after it
+    wait_vmcnt_regs<(kAhead - 1) * kIssue, BITS>(cw[st], sr[st], zr[st]);
+    __builtin_amdgcn_s_barrier();   // every wave's rows are in; step kt - 1's stage is free
+    issue(std::integral_constant<int, nx>{}, kt + kAhead);
+    if (!active) return;
+    half8 bop[2][4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) bd[i] = u32x4{p[4 * i], p[4 * i + 1], p[4 * i + 2], p[4 * i + 3]};
+    for (int j = 0; j < 2; ++j) {
+      const half2v s = as_h2((sr[st][j] & 0xFFFFu) * 0x10001u);
+      const half2v z = as_h2((zr[st][j] & 0xFFFFu) * 0x10001u);
+      const half2v c = {(_Float16)1.0f, kHi};
+      const half2v d = {(_Float16)-1024.0f, (_Float16)(BITS == 4 ? -64.0f : -1024.0f)};
+      bop[j][0] = b_operand<BITS, 0>(cw[st][j], pk, c, d, z, s);
+      bop[j][1] = b_operand<BITS, 1>(cw[st][j], pk, c, d, z, s);
+      bop[j][2] = b_operand<BITS, 2>(cw[st][j], pk, c, d, z, s);
+      bop[j][3] = b_operand<BITS, 3>(cw[st][j], pk, c, d, z, s);
     }
-    __syncthreads();
-    if (kt + 1 < KT) load(kt + 1);   // next step's loads overlap this step's products
 #pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
-      half8 av[2], bv[2];
+    for (int kk = 0; kk < 4; ++kk) {
+      half8 aop[4];
+      read_a<st>(a_rd[kk], aop);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        av[i] = *reinterpret_cast<const half8 *>(&As[(wm + 32 * i + (lane & 31)) * kLdk + 16 * kk + 8 * (lane >> 5)]);
-        bv[i] = *reinterpret_cast<const half8 *>(&Bs[(wn + 32 * i + (lane & 31)) * kLdk + 16 * kk + 8 * (lane >> 5)]);
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
 #if defined(__HIP_DEVICE_COMPILE__)   // the 32x32x16 f16 MFMA exists only in the gfx950 pass
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aop[i], bop[j][kk], acc[i][j], 0, 0, 0);
 #endif
         }
     }
-    __syncthreads();
+  };
+
+  // the waits count loads in issue order: keep step kt0's loads ahead of
+  // step kt0 + 1's (inside the loop the steps' asm waits keep the order)
+  issue(std::integral_constant<int, 0>{}, kt0);
+  asm volatile("" ::: "memory");
+  issue(std::integral_constant<int, 1>{}, kt0 + 1);
+  if constexpr (kAhead > 2) {
+    asm volatile("" ::: "memory");
+    issue(std::integral_constant<int, 2>{}, kt0 + 2);
   }
+  for (int i0 = 0; i0 < T; i0 += kStages) {
+    step(std::integral_constant<int, 0>{}, kt0 + i0, true);
+    step(std::integral_constant<int, 1>{}, kt0 + i0 + 1, i0 + 1 < T);
+    step(std::integral_constant<int, 2>{}, kt0 + i0 + 2, i0 + 2 < T);
+    if constexpr (kStages > 3) step(std::integral_constant<int, 3>{}, kt0 + i0 + 3, i0 + 3 < T);
+  }
+  wait_vmcnt<0>();   // the trailing out-of-range loads still write LDS
 
   // epilogue: accumulator register v of lane l is C[8 (v/4) + 4 (l/32) + v%4][l % 32]
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int col = n0 + wn + 32 * j + (lane & 31);
+      const int col = nw0 + 32 * j + (lane & 31);
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int row = m0 + wm + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (row < a.m && col < a.n) {
+        const int row = m0 + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (row < L.m && col < L.n) {
           const float r = acc[i][j][v];
-          if (a.out_f32) {
-            reinterpret_cast<float *>(a.y)[(size_t)row * a.ldy + col] = r;
+          if (L.ksplit > 1) {
+            L.part[((size_t)ks * L.m + row) * L.n + col] = r;
+          } else if (L.out_f32) {
+            reinterpret_cast<float *>(L.y)[(size_t)row * L.ldy + col] = r;
           } else {
             const _Float16 h = (_Float16)r;
-            reinterpret_cast<uint16_t *>(a.y)[(size_t)row * a.ldy + col] = __builtin_bit_cast(uint16_t, h);
+            reinterpret_cast<uint16_t *>(L.y)[(size_t)row * L.ldy + col] = __builtin_bit_cast(uint16_t, h);
           }
         }
       }
     }
 }
 
+// The K splits of a linear, added in split order: y = sum_s part[s].
+__global__ __launch_bounds__(256) void gemm_finalize_kernel(GemmBatch a) {
+  int l = -1, base = 0;
+  for (int i = 0; i < a.count; ++i) {
+    if (a.lin[i].ksplit <= 1) continue;
+    const int nblk = (int)(((int64_t)a.lin[i].m * a.lin[i].n / 4 + 255) / 256);
+    if ((int)blockIdx.x < base + nblk) {
+      l = i;
+      break;
+    }
+    base += nblk;
+  }
+  if (l < 0) return;
+  const GemmLin &L = a.lin[l];
+  const int64_t e = ((int64_t)(blockIdx.x - base) * 256 + threadIdx.x) * 4;   // n % 4 == 0: 4 columns of one row
+  const int64_t mn = (int64_t)L.m * L.n;
+  if (e >= mn) return;
+  float4 s = *reinterpret_cast<const float4 *>(&L.part[e]);
+  for (int q = 1; q < L.ksplit; ++q) {
+    const float4 p = *reinterpret_cast<const float4 *>(&L.part[(size_t)q * mn + e]);
+    s.x += p.x; s.y += p.y; s.z += p.z; s.w += p.w;
+  }
+  const int64_t row = e / L.n, col = e - row * L.n;
+  if (L.out_f32) {
+    float *y = reinterpret_cast<float *>(L.y) + row * L.ldy + col;
+    y[0] = s.x; y[1] = s.y; y[2] = s.z; y[3] = s.w;
+  } else {
+    uint16_t *y = reinterpret_cast<uint16_t *>(L.y) + row * L.ldy + col;
+    y[0] = __builtin_bit_cast(uint16_t, (_Float16)s.x);
+    y[1] = __builtin_bit_cast(uint16_t, (_Float16)s.y);
+    y[2] = __builtin_bit_cast(uint16_t, (_Float16)s.z);
+    y[3] = __builtin_bit_cast(uint16_t, (_Float16)s.w);
+  }
+}
+
 }  // namespace
 
 bool gemm_available(int bits) { return bits == 3 || bits == 4 || bits == 6 || bits == 8; }
 
-size_t gemm_workspace(const wq_weight &w, int64_t m) {
-  (void)w;
-  (void)m;
-  return 0;
+// K splits per linear: long K is cut so that the workgroups of a launch have
+// similar lengths; a split costs 8 M N bytes of fp32 partial traffic, so
+// short linears stay whole.
+void gemm_plan(int count, const wq_weight *w, int64_t m, int *ksplit) {
+  int64_t units = 0;
+  for (int i = 0; i < count; ++i) {
+    const int64_t tiles = ((m + kTM - 1) / kTM) * ((w[i].n + kTN - 1) / kTN);
+    units += tiles * (w[i].k / kBK);
+  }
+  const int64_t slots = 2 * 256;   // two workgroups per CU
+  const int64_t target = std::max<int64_t>(24, (units + slots - 1) / slots);
+  for (int i = 0; i < count; ++i) {
+    const int64_t kt = w[i].k / kBK;
+    int64_t s = (kt + target - 1) / target;
+    s = std::max<int64_t>(1, std::min<int64_t>(s, kt / 8));
+    ksplit[i] = w[i].n % 4 ? 1 : (int)s;
+  }
 }
 
-hipError_t launch_gemm(const wq_weight &w, const uint16_t *xr, int64_t m, int64_t ldx, void *y, int out_f32,
-                       int64_t ldy, void *workspace, hipStream_t s) {
-  (void)workspace;
-  if (!gemm_available(w.bits) || w.k % kBK) return hipErrorInvalidValue;
-  if ((uint64_t)m * (uint64_t)ldx * 2 > 0xFFFFFFFFull || (uint64_t)w.n * (uint64_t)w.k > 0xFFFFFFFFull)
-    return hipErrorInvalidValue;   // 32-bit buffer offsets
-  GemmArgs a;
-  a.codes = w.codes;
-  a.scales = w.scales;
-  a.zeros = w.zeros;
-  a.x = xr;
-  a.y = y;
-  a.ldx = ldx;
-  a.ldy = ldy;
-  a.m = (int32_t)m;
-  a.n = (int32_t)w.n;
-  a.k = (int32_t)w.k;
-  a.mtiles = (int32_t)((m + kBM - 1) / kBM);
-  a.ntiles = (int32_t)((w.n + kBN - 1) / kBN);
-  a.out_f32 = out_f32;
-  const unsigned grid = (unsigned)(a.mtiles * a.ntiles);
-  switch (w.bits) {
-    case 3: hipLaunchKernelGGL(gemm_kernel<3>, dim3(grid), dim3(kGemmThreads), 0, s, a); break;
-    case 4: hipLaunchKernelGGL(gemm_kernel<4>, dim3(grid), dim3(kGemmThreads), 0, s, a); break;
-    case 6: hipLaunchKernelGGL(gemm_kernel<6>, dim3(grid), dim3(kGemmThreads), 0, s, a); break;
-    case 8: hipLaunchKernelGGL(gemm_kernel<8>, dim3(grid), dim3(kGemmThreads), 0, s, a); break;
+size_t gemm_partial_bytes(const wq_weight &w, int64_t m, int ksplit) {
+  return ksplit > 1 ? (size_t)ksplit * (size_t)m * (size_t)w.n * sizeof(float) : 0;
+}
+
+hipError_t launch_gemm_batch(int count, const wq_weight *w, const uint16_t *const *xr, const int64_t *ldx,
+                             int64_t m, void *const *y, const int *out_f32, const int64_t *ldy,
+                             const int *ksplit, float *const *part, hipStream_t s) {
+  if (count <= 0 || count > kMaxBatch) return hipErrorInvalidValue;
+  GemmBatch a;
+  memset(&a, 0, sizeof a);
+  for (int i = 0; i < kMaxBatch; ++i) a.first_tile[i] = INT32_MAX;
+  a.count = count;
+  int64_t tiles = 0, fin_blocks = 0;
+  for (int i = 0; i < count; ++i) {
+    if (!gemm_available(w[i].bits) || w[i].bits != w[0].bits || w[i].k % kBK) return hipErrorInvalidValue;
+    if (ksplit[i] > 1 && w[i].n % 4) return hipErrorInvalidValue;   // the partial sums run 4 columns at a time
+    if ((uint64_t)m * (uint64_t)ldx[i] * 2 > 0x7FFFFFFFull || (uint64_t)w[i].n * (uint64_t)w[i].k > 0x7FFFFFFFull)
+      return hipErrorInvalidValue;   // 32-bit buffer offsets
+    GemmLin &L = a.lin[i];
+    L.codes = w[i].codes;
+    L.scales = w[i].scales;
+    L.zeros = w[i].zeros;
+    L.x = xr[i];
+    L.y = y[i];
+    L.part = ksplit[i] > 1 ? part[i] : nullptr;
+    if (ksplit[i] > 1 && !part[i]) return hipErrorInvalidValue;
+    L.ldx = ldx[i];
+    L.ldy = ldy[i];
+    L.m = (int32_t)m;
+    L.n = (int32_t)w[i].n;
+    L.k = (int32_t)w[i].k;
+    L.out_f32 = out_f32[i];
+    L.mtiles = (int32_t)((m + kTM - 1) / kTM);
+    L.ntiles = (int32_t)((w[i].n + kTN - 1) / kTN);
+    const int kt = (int)(w[i].k / kBK);
+    L.ksplit = ksplit[i];
+    L.ksteps = (kt + ksplit[i] - 1) / ksplit[i];
+    L.ksplit = (kt + L.ksteps - 1) / L.ksteps;   // no empty split
+    L.tile_begin = (int32_t)tiles;
+    a.first_tile[i] = (int32_t)tiles;
+    tiles += (int64_t)L.mtiles * L.ntiles * L.ksplit;
+    if (L.ksplit > 1) fin_blocks += ((int64_t)m * w[i].n / 4 + 255) / 256;
   }
+  if (tiles > INT32_MAX) return hipErrorInvalidValue;
+  a.tiles = (int32_t)tiles;
+  switch (w[0].bits) {
+    case 3: hipLaunchKernelGGL(gemm_kernel<3>, dim3((unsigned)tiles), dim3(kGemmThreads), 0, s, a); break;
+    case 4: hipLaunchKernelGGL(gemm_kernel<4>, dim3((unsigned)tiles), dim3(kGemmThreads), 0, s, a); break;
+    case 6: hipLaunchKernelGGL(gemm_kernel<6>, dim3((unsigned)tiles), dim3(kGemmThreads), 0, s, a); break;
+    case 8: hipLaunchKernelGGL(gemm_kernel<8>, dim3((unsigned)tiles), dim3(kGemmThreads), 0, s, a); break;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || fin_blocks == 0) return e;
+  hipLaunchKernelGGL(gemm_finalize_kernel, dim3((unsigned)fin_blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -10,19 +10,18 @@
 // lanes by DPP.  fp32 inside, one rounding to fp16 at the end.
 #include "wq_internal.h"
 
+#include <climits>
+#include <cstring>
+
 namespace wq {
 using namespace dev;
 
 namespace {
 
-__global__ __launch_bounds__(256) void rht_kernel(const uint16_t *__restrict__ x, uint16_t *y,
-                                                  const uint32_t *__restrict__ signs, int64_t m,
-                                                  int64_t k, int64_t ldx, int64_t ldy) {
-  const int64_t nb = k / 128;
-  const int64_t item = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int jj = threadIdx.x & 15;
-  if (item >= m * nb) return;   // whole 16-lane rows leave together
-  const int64_t row = item / nb, b = item % nb;
+// Block b of row `row`, lane jj's eight elements.
+__device__ __forceinline__ void rotate_block(const uint16_t *__restrict__ x, uint16_t *y,
+                                             const uint32_t *__restrict__ signs, int64_t row, int64_t b,
+                                             int jj, int64_t ldx, int64_t ldy) {
   const int64_t kk = b * 128 + 8 * jj;
   const uint4 raw = *reinterpret_cast<const uint4 *>(x + row * ldx + kk);
   float v[8];
@@ -43,6 +42,43 @@ __global__ __launch_bounds__(256) void rht_kernel(const uint16_t *__restrict__ x
   *reinterpret_cast<uint4 *>(y + row * ldy + kk) = out;
 }
 
+__global__ __launch_bounds__(256) void rht_kernel(const uint16_t *__restrict__ x, uint16_t *y,
+                                                  const uint32_t *__restrict__ signs, int64_t m,
+                                                  int64_t k, int64_t ldx, int64_t ldy) {
+  const int64_t nb = k / 128;
+  const int64_t item = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  if (item >= m * nb) return;   // whole 16-lane rows leave together
+  rotate_block(x, y, signs, item / nb, item % nb, threadIdx.x & 15, ldx, ldy);
+}
+
+// Several matrices in one launch: workgroups (16 blocks each) dealt to the
+// matrices by a packed table of first workgroups.
+struct RhtMat {
+  const uint16_t *x;
+  uint16_t *y;
+  const uint32_t *signs;
+  int64_t m, k, ldx, ldy;
+  int32_t wg_begin;
+};
+
+struct RhtBatch {
+  int32_t first_wg[kMaxBatch];   // mat[i].wg_begin, packed; INT32_MAX past count
+  RhtMat mat[kMaxBatch];
+};
+
+__global__ __launch_bounds__(256) void rht_batch_kernel(RhtBatch a) {
+  const int w = blockIdx.x;
+  int l = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxBatch; ++i)
+    if (w >= a.first_wg[i]) l = i;
+  const RhtMat M = a.mat[l];
+  const int64_t nb = M.k / 128;
+  const int64_t item = (int64_t)(w - M.wg_begin) * 16 + (threadIdx.x >> 4);
+  if (item >= M.m * nb) return;
+  rotate_block(M.x, M.y, M.signs, item / nb, item % nb, threadIdx.x & 15, M.ldx, M.ldy);
+}
+
 }  // namespace
 
 hipError_t launch_rht(const uint16_t *x, uint16_t *y, const uint32_t *signs, int64_t m, int64_t k,
@@ -51,6 +87,32 @@ hipError_t launch_rht(const uint16_t *x, uint16_t *y, const uint32_t *signs, int
   const int64_t blocks = (items + 15) / 16;
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL(rht_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, y, signs, m, k, ldx, ldy);
+  return hipGetLastError();
+}
+
+hipError_t launch_rht_batch(int count, const uint16_t *const *x, uint16_t *const *y, const uint32_t *const *signs,
+                            int64_t m, const int64_t *k, const int64_t *ldx, const int64_t *ldy, hipStream_t s) {
+  if (count <= 0 || count > kMaxBatch) return hipErrorInvalidValue;
+  RhtBatch a;
+  memset(&a, 0, sizeof a);
+  for (int i = 0; i < kMaxBatch; ++i) a.first_wg[i] = INT32_MAX;
+  int64_t wgs = 0;
+  for (int i = 0; i < count; ++i) {
+    RhtMat &M = a.mat[i];
+    M.x = x[i];
+    M.y = y[i];
+    M.signs = signs[i];
+    M.m = m;
+    M.k = k[i];
+    M.ldx = ldx[i];
+    M.ldy = ldy[i];
+    M.wg_begin = (int32_t)wgs;
+    a.first_wg[i] = (int32_t)wgs;
+    wgs += (m * (k[i] / 128) + 15) / 16;
+  }
+  if (wgs == 0) return hipSuccess;
+  if (wgs > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(rht_batch_kernel, dim3((unsigned)wgs), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -65,6 +65,9 @@ int gemv_lds_bytes(int mt, int chunk, int rows, int64_t k);
 // Other launchers.
 hipError_t launch_rht(const uint16_t *x, uint16_t *y, const uint32_t *signs, int64_t m,
                       int64_t k, int64_t ldx, int64_t ldy, hipStream_t s);
+// the same rotation for up to kMaxBatch matrices of m rows in one launch
+hipError_t launch_rht_batch(int count, const uint16_t *const *x, uint16_t *const *y, const uint32_t *const *signs,
+                            int64_t m, const int64_t *k, const int64_t *ldx, const int64_t *ldy, hipStream_t s);
 hipError_t launch_quantize(int bits, int64_t n, int64_t k, const float *w,
                            const uint32_t *signs, const uint8_t *block_bits, uint8_t *codes,
                            uint16_t *scales, uint16_t *zeros, hipStream_t s);
@@ -75,12 +78,17 @@ hipError_t launch_unpack(int bits, int64_t n, int64_t k, const uint32_t *packed,
                          const uint8_t *block_bits, const uint64_t *block_off, uint8_t *codes,
                          hipStream_t s);
 
-// MFMA GEMM for m >= 64 (gemm.hip).  xr: fp16 activations already rotated
-// (or unrotated weights), [m][ldx].
+// MFMA GEMM for m >= 64 (gemm.hip), one launch for up to kMaxBatch linears
+// of one code width.  xr[i]: fp16 activations already rotated (or used as
+// given), [m][ldx[i]].  ksplit[i] > 1 cuts K over that many workgroups whose
+// fp32 partials go to part[i] ([ksplit][m][n], gemm_partial_bytes) and are
+// added by a second kernel.
 bool gemm_available(int bits);
-size_t gemm_workspace(const wq_weight &w, int64_t m);
-hipError_t launch_gemm(const wq_weight &w, const uint16_t *xr, int64_t m, int64_t ldx, void *y,
-                       int out_f32, int64_t ldy, void *workspace, hipStream_t s);
+void gemm_plan(int count, const wq_weight *w, int64_t m, int *ksplit);
+size_t gemm_partial_bytes(const wq_weight &w, int64_t m, int ksplit);
+hipError_t launch_gemm_batch(int count, const wq_weight *w, const uint16_t *const *xr, const int64_t *ldx,
+                             int64_t m, void *const *y, const int *out_f32, const int64_t *ldy,
+                             const int *ksplit, float *const *part, hipStream_t s);
 
 }  // namespace wq
 
