@@ -179,8 +179,10 @@ size_t wq_linear_workspace(const wq_weight *w, int64_t m);
  *   y          out: fp16 or fp32 [m][ldy] (y_dtype)
  *   workspace  device scratch of at least wq_linear_workspace(w, m) bytes
  *              (caller-owned, 16-byte aligned; NULL when that is 0).  The
- *              matrix-core path keeps the rotated activations there; its
- *              contents need no initialisation and are not preserved.
+ *              matrix-core path keeps the rotated activations there, and
+ *              the fp32 partial sums when it splits a long K over several
+ *              workgroups; its contents need no initialisation and are not
+ *              preserved.
  */
 wq_status wq_linear(const wq_weight *w, const uint16_t *x, int64_t m, int64_t ldx,
                     void *y, wq_dtype y_dtype, int64_t ldy, uint32_t flags,
@@ -188,11 +190,14 @@ wq_status wq_linear(const wq_weight *w, const uint16_t *x, int64_t m, int64_t ld
 
 /* Several independent linears (up to WQ_MAX_BATCH), each with its own
  * weight, activations and output, all at the same batch size m and code
- * width.  For m <= 16 they run as one GEMV launch (workspace size 0); for
- * larger m they run one after another on the stream exactly as wq_linear
- * would, sharing one workspace of wq_linear_batch_workspace bytes.  Same
- * math and layout as wq_linear, applied to each w[i], x[i], y[i].  Arrays of
- * length `count` are host arrays. */
+ * width.  For m <= 16 they run as one GEMV launch (workspace size 0).  For
+ * m >= 64 with a uniform code width they run as one matrix-core launch
+ * (after one launch rotating every linear's activations); the workspace of
+ * wq_linear_batch_workspace bytes then holds every linear's rotated
+ * activations and split-K partial sums.  Otherwise (17 <= m < 64, or the
+ * mixed 6/8-bit layout) they run one after another on the stream exactly
+ * as wq_linear would.  Same math and layout as wq_linear, applied to each
+ * w[i], x[i], y[i].  Arrays of length `count` are host arrays. */
 size_t wq_linear_batch_workspace(int32_t count, const wq_weight *w, int64_t m);
 wq_status wq_linear_batch(int32_t count, const wq_weight *w,
                           const uint16_t *const *x, const int64_t *ldx, int64_t m,
