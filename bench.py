@@ -93,7 +93,7 @@ PEAK_MFMA_F16_TFLOPS = 2500.0
 def kernel_name(bits: int, m: int) -> str:
     """The kernel one step launches (the planner's choice for these shapes)."""
     if m >= 64:
-        return f"gemm_kernel<{bits}> (matrix cores), after rht_kernel per linear"
+        return f"gemm_kernel<{bits}> (matrix cores, all linears in one launch), after rht_batch_kernel"
     if m == 1:
         return f"gemv_ring_kernel<{bits}, true> (LDS-ring weight stream)"
     return f"gemv_stream_kernel<{bits}, {1 if m == 1 else 2 if m == 2 else 4}> (register prefetch)"

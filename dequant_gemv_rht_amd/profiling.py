@@ -8,6 +8,10 @@
         HBM bytes per launch of the GEMV from FETCH_SIZE / WRITE_SIZE, each
         scaled by what the same counter reads for a plain copy of N bytes
 
+    python -m dequant_gemv_rht_amd.profiling counters DIR --match gemm_kernel
+        every counter of a `--pmc` run, per dispatch of the matching kernels
+        (summed over the counter's instances: XCDs, SEs, channels)
+
 Counters are taken per dispatch (rocprofv3 reports FETCH_SIZE and WRITE_SIZE
 in KiB); the copy's dispatches are the largest ones of its run.
 """
@@ -110,6 +114,18 @@ def traffic(a) -> dict:
     return rec
 
 
+def counters(d: str, match: str):
+    """{counter: (mean per dispatch, dispatches)} for kernels whose name contains `match`."""
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    for f in _files(d, "_results.db"):
+        con = sqlite3.connect(f)
+        q = "select dispatch_id, kernel_name, counter_name, value from counters_collection"
+        for disp, name, cname, value in con.execute(q):
+            if match in name:
+                per[cname][(f, disp)] += float(value)
+    return {c: (sum(v.values()) / len(v), len(v)) for c, v in per.items()}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -123,6 +139,9 @@ def main(argv=None):
     c.add_argument("--key", required=True)
     c.add_argument("--match", default="gemv")
     c.add_argument("--out", required=True)
+    n = sub.add_parser("counters")
+    n.add_argument("dir")
+    n.add_argument("--match", default="")
     a = ap.parse_args(argv)
     if a.cmd == "trace":
         rows = kernel_stats(a.dir, a.match)
@@ -132,6 +151,13 @@ def main(argv=None):
         for name, calls, avg, mn, mx, p10, p50, p90 in rows:
             print(f"{name[:64]:64s} {calls:6d} {avg / 1e3:8.3f} {mn / 1e3:8.3f} {p10 / 1e3:8.3f} {p50 / 1e3:8.3f} "
                   f"{p90 / 1e3:8.3f} {mx / 1e3:8.3f}")
+    elif a.cmd == "counters":
+        rows = counters(a.dir, a.match)
+        if not rows:
+            raise SystemExit("no matching dispatches")
+        for c in sorted(rows):
+            mean, n = rows[c]
+            print(f"{c:32s} {mean:18.1f} per dispatch ({n} dispatches)")
     else:
         rec = traffic(a)
         with open(a.out, "w") as f:
