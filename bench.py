@@ -64,6 +64,17 @@ def algorithmic_bytes(lins, m: int) -> int:
     return total
 
 
+def linear_bytes(lin, m: int, sel=None) -> int:
+    """Algorithmic bytes of one linear at batch m.  Mixed width (bits 0): the
+    64-row blocks' codes at their own widths plus the per-block selectors."""
+    if lin.bits:
+        w = int(lin.n * lin.k * bytes_per_weight(lin.bits))
+    else:
+        w = int(sum(64 * lin.k * int(b) // 8 for b in sel)) + lin.n * lin.k // 32 + len(sel)
+    w += 2 * m * lin.k + (4 if lin.out_f32 else 2) * m * lin.n
+    return w + (lin.k // 8 if lin.rht else 0)
+
+
 def source_digest() -> str:
     """Digest of the sources that decide the measured kernel and its launch."""
     h = hashlib.sha256()
@@ -129,6 +140,198 @@ def cpu_baseline(wl, lins, m, budget_s: float):
                       f"rotation + dequant + fp64 triple loop, excluding quantisation"}
 
 
+def _pool_views(t, copies: int):
+    """``copies`` distinct copies of ``t`` in one allocation, each starting on a
+    256-byte boundary (views keep the dtype and shape)."""
+    import torch
+    nbytes = t.numel() * t.element_size()
+    stride = (nbytes + 255) // 256 * 256 // t.element_size()
+    buf = torch.empty(copies * stride, dtype=t.dtype, device=t.device)
+    out = []
+    for i in range(copies):
+        v = buf[i * stride:i * stride + t.numel()].view(t.shape)
+        v.copy_(t)
+        out.append(v)
+    return out
+
+
+def _time_launches(fns, stream, min_launches: int = 200, replays: int = 3) -> float:
+    """Mean µs per launch over a graph of back-to-back launches cycling through
+    ``fns`` (each call launches once on ``stream``); median over replays."""
+    import torch
+    k = max(min_launches, len(fns))
+    sptr = stream.cuda_stream
+    with torch.cuda.stream(stream):
+        for i in range(min(len(fns), 64)):
+            fns[i](sptr)
+    stream.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(k):
+            fns[i % len(fns)](sptr)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    times = []
+    with torch.cuda.stream(stream):
+        g.replay()
+        for _ in range(replays):
+            t0.record(stream)
+            g.replay()
+            t1.record(stream)
+            torch.cuda.synchronize()
+            times.append(t0.elapsed_time(t1) * 1e3 / k)
+    del g
+    return float(np.median(times))
+
+
+class _ReadCeiling:
+    """The plain streaming-read kernel over cold data of a given size."""
+
+    def __init__(self, pool_bytes: int):
+        import torch
+        self.buf = torch.empty(pool_bytes, dtype=torch.uint8, device="cuda").fill_(7)
+        self.sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+
+    def us(self, nbytes: int, stream) -> float:
+        import dequant_gemv_rht_amd as dq
+        nb = (nbytes + 15) // 16 * 16
+        stride = (nb + 255) // 256 * 256
+        copies = self.buf.numel() // stride
+        if copies < 2:
+            raise ValueError(f"read ceiling: {nbytes} bytes need a pool of at least {2 * stride} bytes")
+        lib, base, sink = dq.lib(), self.buf.data_ptr(), self.sink.data_ptr()
+
+        def one(i):
+            off = base + (i % copies) * stride
+            return lambda sp: dq._check("wq_stream_read", lib.wq_stream_read(off, nb, sink, sp))
+        return _time_launches([one(i) for i in range(copies)], stream)
+
+
+def _oracle_ms(w_rows, x, signs, bits_rows, lin, threads: int) -> float:
+    """The oracle's time for the whole linear, from a row sample: the activation
+    rotation once, plus dequantise-and-contract of the sampled rows scaled to
+    all N rows (rows are independent and cost the same)."""
+    from oracle import linear as OL
+    from oracle import rtn as OR
+    q, s, z = OR.prepare(w_rows, signs, bits_rows)
+    t0 = time.perf_counter()
+    x64 = np.atleast_2d(x).astype(np.float64)
+    xr = OL.rht(x64, signs) if (lin.rht and signs is not None) else x64
+    t_rot = time.perf_counter() - t0
+    reps, t_rows = 0, 0.0
+    while t_rows < 0.2 or reps < 1:
+        t1 = time.perf_counter()
+        OL.contract(OL.dequant(q, s, z), xr, threads)
+        t_rows += time.perf_counter() - t1
+        reps += 1
+    return (t_rot + t_rows / reps * lin.n / len(w_rows)) * 1e3
+
+
+def sweep(args) -> None:
+    """Per-config, per-linear and per-step table: µs, GB/s, fraction of 8 TB/s,
+    fraction of the plain-read ceiling at the same size, TFLOP/s at M >= 64,
+    and the oracle's CPU time for the same linear (row-sampled)."""
+    import torch
+    import dequant_gemv_rht_amd as dq
+
+    stream = torch.cuda.Stream()
+    ceiling = _ReadCeiling(args.pool_bytes)
+    threads_all = len(os.sched_getaffinity(0))
+    rows_out = []
+    hdr = ("| config | linear | M | bits | K→N | alg. bytes | µs | GB/s | % of 8 TB/s | read ceiling µs "
+           "| % of ceiling | TFLOP/s (% of 2.5 P) | oracle ms, 1 thread | oracle ms, "
+           f"{threads_all} threads |")
+    print(hdr, flush=True)
+    print("|" + "---|" * (hdr.count("|") - 1), flush=True)
+    rng = np.random.default_rng(5)
+
+    def emit(cfg, name, m, bits, shape, nbytes, us, ceil_us, flops, o1, oa):
+        gbs = nbytes / us / 1e3
+        tf = f"{flops / us / 1e6:.1f} ({flops / us / 1e6 / PEAK_MFMA_F16_TFLOPS:.1%})" if flops else "–"
+        f1 = f"{o1:.2f}" if o1 is not None else "–"
+        fa = f"{oa:.2f}" if oa is not None else "–"
+        line = (f"| {cfg} | {name} | {m} | {bits} | {shape} | {nbytes:,} | {us:.2f} | {gbs:.0f} | "
+                f"{gbs / PEAK_HBM_GBS:.1%} | {ceil_us:.2f} | {ceil_us / us:.1%} | {tf} | {f1} | {fa} |")
+        print(line, flush=True)
+        rows_out.append(line)
+
+    for cfg, wname in (("c1", "single_int4"), ("c2", "block_int4"), ("c3", "block_int3"),
+                       ("c4", "block_int6_head_int8"), ("c5", "prefill_and_mixed")):
+        wl = W.WORKLOADS[wname]
+        if args.sweep_only and cfg not in args.sweep_only.split(","):
+            continue
+        for m in wl.ms:
+            lins = [(i, l) for i, l in enumerate(wl.linears)]
+            if cfg == "c5":   # part A is the projections at M=512, part B the mixed down_proj at M=1
+                lins = [(i, l) for i, l in lins if (l.bits == 0) == (m == 1)]
+            log(f"sweep {cfg} {wname} M={m}: {len(lins)} linear(s)")
+            qws, xs, ys, hosts = [], [], [], []
+            for i, lin in lins:
+                w, x, signs, sel = W.linear_inputs(0, wl.wid, i, lin, m)
+                sg = torch.from_numpy(signs.view(np.int32)).cuda() if signs is not None else None
+                bb = torch.from_numpy(sel).cuda() if sel is not None else None
+                qws.append(dq.quantize_weight(torch.from_numpy(w).cuda(), lin.bits, sg, bb))
+                xs.append(torch.from_numpy(x).cuda())
+                ys.append(torch.empty((m, lin.n), dtype=torch.float32 if lin.out_f32 else torch.float16,
+                                      device="cuda"))
+                rows = np.sort(rng.choice(lin.n, min(lin.n, args.cpu_rows if m < 64 else args.cpu_rows // 4),
+                                          replace=False))
+                bits_rows = np.repeat(sel, 64)[rows] if sel is not None else lin.bits
+                hosts.append((w[rows].copy(), x, signs, bits_rows, sel))
+                del w
+            torch.cuda.synchronize()
+
+            def pooled(ws_list, total_bytes):
+                copies = max(2, math.ceil(args.pool_bytes / max(1, total_bytes)))
+                views = [[] for _ in range(copies)]
+                for q in ws_list:
+                    cs = _pool_views(q.codes, copies)
+                    ss = _pool_views(q.scales, copies)
+                    zs = _pool_views(q.zeros, copies)
+                    for c in range(copies):
+                        views[c].append(dq.QWeight(q.bits, q.n, q.k, cs[c], ss[c], zs[c], q.signs,
+                                                   q.block_bits, q.block_off))
+                return views
+
+            step_bytes, step_flops = 0, 0
+            for j, (i, lin) in enumerate(lins):
+                q = qws[j]
+                nbytes = linear_bytes(lin, m, hosts[j][4])
+                wbytes = q.codes.numel() * 4 + q.scales.numel() * 4
+                pool = pooled([q], wbytes)
+                wsz = dq.wq_linear_batch_workspace([q], m)
+                ws = dq.new_workspace(wsz)
+                calls = [dq.BatchCall(p, [xs[j]], [ys[j]], True, ws) for p in pool]
+                us = _time_launches(calls, stream)
+                del calls, pool
+                ceil_us = ceiling.us(nbytes, stream)
+                flops = 2 * m * lin.n * lin.k if m >= 64 else 0
+                w_rows, x, signs, bits_rows, _ = hosts[j]
+                o1 = oa = None
+                if not args.no_cpu_baseline:
+                    o1 = _oracle_ms(w_rows, x, signs, bits_rows, lin, 1)
+                    oa = _oracle_ms(w_rows, x, signs, bits_rows, lin, threads_all)
+                emit(cfg, lin.name, m, lin.bits or "6/8", f"{lin.k}→{lin.n}", nbytes, us, ceil_us, flops, o1, oa)
+                step_bytes += nbytes
+                step_flops += flops
+            # the grouped step: all linears of one width in one call
+            same = [j for j, (_, l) in enumerate(lins) if l.bits == lins[0][1].bits and l.bits and not l.out_f32]
+            if len(same) > 1:
+                sb = sum(linear_bytes(lins[j][1], m) for j in same)
+                sf = sum(2 * m * lins[j][1].n * lins[j][1].k for j in same) if m >= 64 else 0
+                sel_q = [qws[j] for j in same]
+                pool = pooled(sel_q, sum(q.codes.numel() * 4 + q.scales.numel() * 4 for q in sel_q))
+                ws = dq.new_workspace(dq.wq_linear_batch_workspace(sel_q, m))
+                calls = [dq.BatchCall(p, [xs[j] for j in same], [ys[j] for j in same], True, ws) for p in pool]
+                us = _time_launches(calls, stream)
+                del calls, pool
+                emit(cfg, f"**{len(same)} linears, one call**", m, lins[same[0]][1].bits, "all", sb, us,
+                     ceiling.us(sb, stream), sf, None, None)
+            del qws, xs, ys, hosts
+            torch.cuda.empty_cache()
+    log(f"sweep done: {len(rows_out)} rows; host threads {threads_all}")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -139,6 +342,11 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pool-bytes", type=int, default=POOL_BYTES)
+    ap.add_argument("--sweep", action="store_true",
+                    help="print the per-config, per-linear table instead of the headline JSON line")
+    ap.add_argument("--sweep-only", default="", help="comma-separated configs for --sweep (c1..c5)")
+    ap.add_argument("--cpu-rows", type=int, default=256,
+                    help="output rows the oracle computes per linear in --sweep (scaled to all rows)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES (for counter calibration) and exit")
     args = ap.parse_args()
@@ -160,6 +368,9 @@ def main():
         calibrate_copy(args.calibrate_copy, max(1, args.steps))
         return
     dq.lib()  # fail loudly if the library is missing
+    if args.sweep:
+        sweep(args)
+        return
 
     wl = W.WORKLOADS[args.workload]
     m = args.m

@@ -59,6 +59,7 @@ SIGNATURES = {
                                _i64, ctypes.POINTER(_vp), ctypes.POINTER(_i32), ctypes.POINTER(_i64),
                                _u32, _vp, _sz, _vp]),
     "wq_last_error": (ctypes.c_char_p, []),
+    "wq_stream_read": (_i32, [_vp, _sz, _vp, _vp]),
 }
 
 _lib = None
@@ -266,3 +267,13 @@ def wq_linear_batch(weights: Sequence[QWeight], xs: Sequence[torch.Tensor], out_
         workspace = new_workspace(wq_linear_batch_workspace(weights, m), xs[0].device)
     BatchCall(weights, xs, ys, fuse_rht, workspace)()
     return ys
+
+
+def stream_read(src: torch.Tensor, sink: torch.Tensor, nbytes: Optional[int] = None) -> None:
+    """Plain streaming read of ``nbytes`` (default: all) of ``src`` on the
+    current stream: the read ceiling a workload's weight stream is compared
+    with (include/wq_measure.h)."""
+    n = src.numel() * src.element_size() if nbytes is None else nbytes
+    if not src.is_cuda or not sink.is_cuda or sink.numel() * sink.element_size() < 4:
+        raise ValueError("stream_read: src and a 4-byte sink must be GPU tensors")
+    _check("wq_stream_read", lib().wq_stream_read(src.data_ptr(), n, sink.data_ptr(), _stream()))

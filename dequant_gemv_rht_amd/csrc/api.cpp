@@ -9,6 +9,7 @@
 #include <algorithm>
 
 #include "wq_internal.h"
+#include "../../include/wq_measure.h"
 
 namespace {
 
@@ -514,6 +515,17 @@ wq_status wq_linear_batch(int32_t count, const wq_weight *w, const uint16_t *con
     if (st != WQ_OK) return st;
   }
   return WQ_OK;
+}
+
+wq_status wq_stream_read(const void *src, size_t bytes, uint32_t *sink, void *stream) {
+  clear_err();
+  if (!src || !sink) return fail(WQ_E_ARG, "wq_stream_read: NULL pointer");
+  if (bytes == 0 || bytes % 16)
+    return fail(WQ_E_ARG, "wq_stream_read: bytes=%zu must be a positive multiple of 16", bytes);
+  if (!aligned16(src) || !aligned16(sink)) return fail(WQ_E_ALIGN, "wq_stream_read: pointers must be 16-byte aligned");
+  if ((bytes / 16 + 511) / 512 > 0x7FFFFFFFull) return fail(WQ_E_ARG, "wq_stream_read: %zu bytes is too large", bytes);
+  const hipError_t e = wq::launch_stream_read(src, bytes, sink, (hipStream_t)stream);
+  return e == hipSuccess ? WQ_OK : fail(WQ_E_HIP, "wq_stream_read: %s", hipGetErrorString(e));
 }
 
 }  // extern "C"

@@ -66,6 +66,10 @@ int gemv_lds_bytes(int mt, int chunk, int rows, int64_t k);
 hipError_t launch_rht(const uint16_t *x, uint16_t *y, const uint32_t *signs, int64_t m,
                       int64_t k, int64_t ldx, int64_t ldy, hipStream_t s);
 // the same rotation for up to kMaxBatch matrices of m rows in one launch
+// One plain read of `bytes` (a multiple of 16) at `src`, nothing stored
+// (the read ceiling of include/wq_measure.h).
+hipError_t launch_stream_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t s);
+
 hipError_t launch_rht_batch(int count, const uint16_t *const *x, uint16_t *const *y, const uint32_t *const *signs,
                             int64_t m, const int64_t *k, const int64_t *ldx, const int64_t *ldy, hipStream_t s);
 hipError_t launch_quantize(int bits, int64_t n, int64_t k, const float *w,

@@ -6,6 +6,7 @@ call, so no GPU is needed.
 """
 
 import ctypes
+import glob
 import os
 import re
 
@@ -14,13 +15,15 @@ import pytest
 import dequant_gemv_rht_amd as dq
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "wq.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^(?:wq_status|size_t|const char \*)\s*(\w+)\s*\(", text, flags=re.M)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"^(?:wq_status|size_t|const char \*)\s*(\w+)\s*\(", text, flags=re.M))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -33,7 +36,8 @@ def lib():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for required in ["wq_pack", "rht_apply", "wq_linear", "wq_quantize", "wq_unpack",
-                     "wq_linear_workspace", "wq_linear_batch", "wq_packed_words", "wq_last_error"]:
+                     "wq_linear_workspace", "wq_linear_batch", "wq_packed_words", "wq_last_error",
+                     "wq_stream_read"]:
         assert required in names
 
 
@@ -171,3 +175,10 @@ def test_matrix_core_path_workspace_covers_rotated_activations(lib):
     st = lib.wq_linear(ctypes.byref(w), 16, 512, 2560, 16, dq.WQ_F16, 256, dq.WQ_FUSE_RHT, 16, 16, None)
     assert st == dq.WQ_E_WORKSPACE
     assert "workspace" in lib.wq_last_error().decode()
+
+
+def test_stream_read_rejects_bad_arguments(lib):
+    assert lib.wq_stream_read(None, 16, 16, None) == dq.WQ_E_ARG
+    assert lib.wq_stream_read(16, 0, 16, None) == dq.WQ_E_ARG
+    assert lib.wq_stream_read(16, 24, 16, None) == dq.WQ_E_ARG
+    assert lib.wq_stream_read(8, 16, 16, None) == dq.WQ_E_ALIGN
