@@ -107,7 +107,8 @@ def kernel_name(bits: int, m: int) -> str:
         return f"gemm_kernel<{bits}> (matrix cores, all linears in one launch), after rht_batch_kernel"
     if m == 1:
         return f"gemv_ring_kernel<{bits}, true> (LDS-ring weight stream)"
-    return f"gemv_stream_kernel<{bits}, {1 if m == 1 else 2 if m == 2 else 4}> (register prefetch)"
+    return (f"gemv_quad_kernel<{bits}, {2 if m == 2 else 4}> (row quads, register prefetch), "
+            f"after xprep_kernel<{bits}> (activations rotated and arranged once)")
 
 
 def cpu_baseline(wl, lins, m, budget_s: float):

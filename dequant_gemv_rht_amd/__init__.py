@@ -206,7 +206,7 @@ def wq_linear_workspace(weight: QWeight, m: int) -> int:
 
 
 def new_workspace(size: int, device="cuda") -> torch.Tensor:
-    """Zero-filled workspace (the library leaves it zero-filled after each call)."""
+    """A workspace of ``size`` bytes (zero-filled; the library needs no particular contents)."""
     return torch.zeros(max(size, 16), dtype=torch.uint8, device=device)
 
 

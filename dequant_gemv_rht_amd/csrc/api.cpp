@@ -120,13 +120,16 @@ bool plan_stream(int count, const wq_weight *w, int64_t m, bool rotate, int *wg,
   const int ncu = device_cus();
   if (count > ncu) return false;
   const double round_bytes = rotate ? 8192.0 : 3072.0;
+  const int gran = mt >= 2 ? 4 : 2;   // rows per task: quads at batch tiles 2 and 4, pairs at 1
   double bytes[WQ_MAX_BATCH], prep[WQ_MAX_BATCH];
   int64_t maxwg[WQ_MAX_BATCH];
   for (int i = 0; i < count; ++i) {
     bytes[i] = (double)w[i].n * (double)w[i].k * (w[i].bits / 8.0 + 4.0 / 128.0);
     const int64_t items = mt * (w[i].k / wq::kGroup);
-    prep[i] = round_bytes * (double)((items + 15) / 16);
-    maxwg[i] = (w[i].n + 1) / 2;
+    // batch 1 rotates in the workgroup; batch tiles 2 and 4 copy the
+    // arranged activations (80 bytes per 32 elements) from L2
+    prep[i] = mt == 1 ? round_bytes * (double)((items + 15) / 16) : 0.625 * (double)(mt * w[i].k);
+    maxwg[i] = (w[i].n + gran - 1) / gran;
     wg[i] = 1;
   }
   // hand out the CUs one at a time to the linear with the longest estimate
@@ -147,7 +150,7 @@ bool plan_stream(int count, const wq_weight *w, int64_t m, bool rotate, int *wg,
   int ring_lds = 0;
   for (int i = 0; i < count; ++i) {
     int64_t r = (w[i].n + wg[i] - 1) / wg[i];
-    r = (r + 1) / 2 * 2;
+    r = (r + gran - 1) / gran * gran;
     rows_per_wg[i] = (int)r;
     wg[i] = (int)((w[i].n + r - 1) / r);
     const int need = wq::gemv_stream_lds_bytes(w[i].bits, mt, w[i].k, (int)r, false);
@@ -161,10 +164,58 @@ bool plan_stream(int count, const wq_weight *w, int64_t m, bool rotate, int *wg,
   return *lds <= kMaxLds;
 }
 
-// Launch one GEMV over `count` linears with batch rows m (<= 16).
+// Bytes of the arranged activations of m rows of a linear with k columns
+// (the batch-tile kernels' LDS slice layout: 80 bytes per 32 elements).
+size_t xprep_bytes(int64_t k, int64_t m) { return align256((size_t)m * (size_t)(k / wq::kSlice) * 80); }
+
+bool uses_xprep(const wq_weight &w, int64_t m) { return m >= 2 && w.bits != 0; }
+
+wq_status launch_tile(int count, const wq_weight *w, const uint16_t *const *x, const int64_t *ldx, int64_t m,
+                      void *const *y, const wq_dtype *ydt, const int64_t *ldy, bool rotate,
+                      const uint32_t *const *xq, hipStream_t s);
+
+// One GEMV over `count` linears with batch rows m (<= 16).  Above one row
+// (uniform width) the activations are arranged once into the workspace, then
+// each tile of up to 4 batch rows is one pass of the row-quad kernel over
+// the weights (a larger tile would run out of registers for the unpacked
+// codes and the partials of four rows).
 wq_status run_gemv(int count, const wq_weight *w, const uint16_t *const *x, const int64_t *ldx,
                    int64_t m, void *const *y, const wq_dtype *ydt, const int64_t *ldy,
-                   bool rotate, hipStream_t s) {
+                   bool rotate, void *workspace, hipStream_t s) {
+  if (!uses_xprep(w[0], m)) return launch_tile(count, w, x, ldx, m, y, ydt, ldy, rotate, nullptr, s);
+  uint32_t *xq[WQ_MAX_BATCH];
+  const uint32_t *sg[WQ_MAX_BATCH];
+  int64_t kk[WQ_MAX_BATCH];
+  size_t off = 0;
+  for (int i = 0; i < count; ++i) {
+    xq[i] = reinterpret_cast<uint32_t *>(static_cast<char *>(workspace) + off);
+    off += xprep_bytes(w[i].k, m);
+    sg[i] = rotate ? w[i].rht_signs : nullptr;
+    kk[i] = w[i].k;
+  }
+  wq_status st = hip_status(wq::launch_xprep(w[0].bits, count, x, ldx, sg, kk, m, xq, s), "wq_linear");
+  if (st != WQ_OK) return st;
+  const uint32_t *xt[WQ_MAX_BATCH];
+  const uint16_t *xc[WQ_MAX_BATCH];
+  void *yc[WQ_MAX_BATCH];
+  for (int64_t m0 = 0; m0 < m; m0 += 4) {
+    for (int i = 0; i < count; ++i) {
+      xt[i] = xq[i] + (size_t)m0 * (size_t)(w[i].k / wq::kSlice) * 20;
+      xc[i] = x[i] + m0 * ldx[i];
+      yc[i] = static_cast<char *>(y[i]) + (size_t)m0 * (size_t)ldy[i] * (ydt[i] == WQ_F32 ? 4 : 2);
+    }
+    st = launch_tile(count, w, xc, ldx, m - m0 < 4 ? m - m0 : 4, yc, ydt, ldy, rotate, xt, s);
+    if (st != WQ_OK) return st;
+  }
+  return WQ_OK;
+}
+
+// One launch over `count` linears for a batch tile of m <= 4 rows (any m
+// for the tiled kernel).  xq: the tile's arranged activations per linear, or
+// NULL where the kernel rotates for itself.
+wq_status launch_tile(int count, const wq_weight *w, const uint16_t *const *x, const int64_t *ldx, int64_t m,
+                      void *const *y, const wq_dtype *ydt, const int64_t *ldy, bool rotate,
+                      const uint32_t *const *xq, hipStream_t s) {
   wq::GemvArgs a;
   memset(&a, 0, sizeof a);
   for (int i = 0; i < wq::kMaxBatch; ++i) a.first_tile[i] = INT32_MAX;
@@ -196,6 +247,7 @@ wq_status run_gemv(int count, const wq_weight *w, const uint16_t *const *x, cons
     L.block_bits = w[i].block_bits;
     L.block_off = w[i].block_off;
     L.signs = rotate ? w[i].rht_signs : nullptr;
+    L.xq = xq ? xq[i] : nullptr;
     L.x = x[i];
     L.y = y[i];
     L.ldx = ldx[i];
@@ -336,7 +388,7 @@ wq_status linear_one(const wq_weight &w, const uint16_t *x, int64_t m, int64_t l
     const int64_t mc = (m - m0) < 16 ? (m - m0) : 16;
     const uint16_t *xc = x + m0 * ldx;
     void *yc = static_cast<char *>(y) + (size_t)m0 * (size_t)ldy * esz;
-    wq_status st = run_gemv(1, &w, &xc, &ldx, mc, &yc, &y_dtype, &ldy, rotate, s);
+    wq_status st = run_gemv(1, &w, &xc, &ldx, mc, &yc, &y_dtype, &ldy, rotate, workspace, s);
     if (st != WQ_OK) return st;
   }
   return WQ_OK;
@@ -440,7 +492,9 @@ size_t wq_linear_workspace(const wq_weight *w, int64_t m) {
     return (size_t)-1;
   }
   if (use_gemm(*w, m)) return gemm_path_workspace(*w, m);
-  return 0;   // the GEMV needs no workspace
+  // the GEMV above one batch row: the arranged activations of a chunk of
+  // up to 16 rows
+  return uses_xprep(*w, m) ? xprep_bytes(w->k, m < 16 ? m : 16) : 0;
 }
 
 wq_status wq_linear(const wq_weight *w, const uint16_t *x, int64_t m, int64_t ldx, void *y,
@@ -470,14 +524,22 @@ size_t wq_linear_batch_workspace(int32_t count, const wq_weight *w, int64_t m) {
     fail(WQ_E_ARG, "wq_linear_batch_workspace: m must be positive");
     return (size_t)-1;
   }
-  bool gemm = m > 16;   // m <= 16: one GEMV launch, no workspace
+  bool gemm = m > 16;
+  size_t all = 0, largest = 0;
   for (int i = 0; i < count; ++i) {
     if (check_weight(&w[i], "wq_linear_batch_workspace") != WQ_OK) return (size_t)-1;
     gemm = gemm && use_gemm(w[i], m) && w[i].bits == w[0].bits;
+    if (uses_xprep(w[i], m)) {
+      all += xprep_bytes(w[i].k, m);
+      const size_t one = xprep_bytes(w[i].k, m < 16 ? m : 16);
+      if (one > largest) largest = one;
+    }
   }
   // m >= 64 with one uniform width: one matrix-core launch over all of them;
-  // otherwise the GEMV in chunks of 16 rows, one linear after another
-  return gemm ? gemm_layout(count, w, m, true).total : 0;
+  // m <= 16: every linear's arranged activations side by side; otherwise
+  // the GEMV in chunks of 16 rows, one linear after another
+  if (gemm) return gemm_layout(count, w, m, true).total;
+  return m <= 16 ? all : largest;
 }
 
 wq_status wq_linear_batch(int32_t count, const wq_weight *w, const uint16_t *const *x, const int64_t *ldx,
@@ -499,13 +561,13 @@ wq_status wq_linear_batch(int32_t count, const wq_weight *w, const uint16_t *con
       return fail(WQ_E_UNSUPPORTED, "wq_linear_batch: rotate all linears or none");
   }
   const bool rotate = (flags & WQ_FUSE_RHT) && w[0].rht_signs;
-  if (m <= 16) return run_gemv(count, w, x, ldx, m, y, y_dtype, ldy, rotate, (hipStream_t)stream);
   const size_t need = wq_linear_batch_workspace(count, w, m);
   if (need == (size_t)-1) return WQ_E_ARG;
   if (need > workspace_bytes || (need && !workspace))
     return fail(WQ_E_WORKSPACE, "wq_linear_batch: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
   if (workspace && !aligned16(workspace))
     return fail(WQ_E_ALIGN, "wq_linear_batch: workspace must be 16-byte aligned");
+  if (m <= 16) return run_gemv(count, w, x, ldx, m, y, y_dtype, ldy, rotate, workspace, (hipStream_t)stream);
   if (use_gemm(w[0], m))   // one width (checked above): all on the matrix cores in one launch
     return run_gemm(count, w, x, ldx, m, y, y_dtype, ldy, rotate, workspace, (hipStream_t)stream,
                     "wq_linear_batch");

@@ -41,6 +41,8 @@
 // ds_read_b128 hit 16 distinct 4-bank groups.
 #include "wq_internal.h"
 
+#include <climits>
+#include <cstring>
 #include <type_traits>
 
 namespace wq {
@@ -83,41 +85,74 @@ __device__ __forceinline__ uint32_t field(const uint32_t (&w)[N]) {
 }
 
 struct UnpackConsts {
-  uint32_t mask, bias;
+  uint32_t mask, mask2, bias;
 };
 
 // Constants kept in VGPRs so each code pair costs one v_and_or_b32 (gfx9
-// VOP3 instructions cannot take two literal constants).
+// VOP3 instructions cannot take literal constants).
+//
+// A code pair becomes two fp16 values with one v_and_or_b32: the masks keep
+// one code in each 16-bit half of a 32-bit window of the packed bits, in
+// place, and 1024.0's exponent is OR-ed in.  A code sitting at bit s of its
+// half (s + bits <= 10) reads as 1024 + 2^s q, so the activation it meets is
+// stored pre-multiplied by 2^-s (exact in fp16 barring underflow).  Windows
+// are the packed words themselves or funnel shifts of two of them.
+//   int4: word i: (codes 8i+r, 8i+r+4) at s = 0 (r = 0, 2) or 4 (r = 1, 3),
+//         r = 2, 3 from the word shifted right by 8.
+//   int8: v_perm_b32 puts bytes r and r+2 of a word next to 0x64 bytes.
+//   int3: octet o (codes 8o..8o+7, bits 24o..24o+23 of the 96-bit run):
+//         window at bit 24o - 4 gives (8o, 8o+4) at s = (4, 0) and
+//         (8o+1, 8o+5) at s = (7, 3); the window at bit 24o + 2 gives
+//         (8o+2, 8o+6) and (8o+3, 8o+7) the same way.
+//   int6: octet o (bits 48o'..48o'+47 of its 96-bit run of 16 codes,
+//         o' = o mod 2): windows at 48o' - 4, +2, +20, +26 give the pairs
+//         (0,2), (1,3), (4,6), (5,7) of the octet at s = (4, 0).
 template <int BITS>
 __device__ __forceinline__ UnpackConsts unpack_consts() {
-  constexpr uint32_t m = BITS == 4 ? 0x000F000Fu : BITS == 8 ? 0x00FF00FFu : BITS == 3 ? 0x00070007u : 0x003F003Fu;
+  constexpr uint32_t m = BITS == 4 ? 0x000F000Fu : BITS == 8 ? 0x00FF00FFu : BITS == 3 ? 0x00070070u : 0x003F03F0u;
+  constexpr uint32_t m2 = BITS == 3 ? 0x00380380u : 0u;
   constexpr uint32_t b = BITS == 8 ? 0x64646464u : kBias;
   UnpackConsts c;
   asm volatile("v_mov_b32 %0, %1" : "=v"(c.mask) : "i"(m));
+  if constexpr (BITS == 3) asm volatile("v_mov_b32 %0, %1" : "=v"(c.mask2) : "i"(m2));
+  else c.mask2 = 0u;
   asm volatile("v_mov_b32 %0, %1" : "=v"(c.bias) : "i"(b));
   return c;
+}
+
+// 32 bits of a run of N packed words starting at bit B (-32 < B < 32 N);
+// bits outside the run read as zero.
+template <int B, int N>
+__device__ __forceinline__ uint32_t window(const uint32_t *w) {
+  if constexpr (B < 0) {
+    return w[0] << (-B);
+  } else {
+    constexpr int k = B / 32, sh = B % 32;
+    if constexpr (sh == 0) return w[k];
+    else if constexpr (k + 1 >= N) return w[k] >> sh;
+    else return __builtin_amdgcn_alignbit(w[k + 1], w[k], sh);
+  }
 }
 
 // Code pair P of a 32-code slice as two fp16 values.
 template <int BITS, int P>
 __device__ __forceinline__ uint32_t pair_at(const uint32_t (&w)[BITS], UnpackConsts c) {
   if constexpr (BITS == 4) {
-    // word P/4: r=0 codes (0,4), r=1 codes (1,5) read as 1024+16q, r=2
-    // codes (2,6), r=3 codes (3,7) read as 1024+16q
     constexpr int wi = P / 4, r = P % 4;
     const uint32_t v = (r < 2) ? w[wi] : (w[wi] >> 8);
     return (r & 1) ? ((v & (c.mask << 4)) | c.bias) : ((v & c.mask) | c.bias);
   } else if constexpr (BITS == 8) {
-    // word P/2: bytes (r, r+2) next to 0x64 bytes -> (1024 + q) each
     constexpr int wi = P / 2, r = P % 2;
     return __builtin_amdgcn_perm(c.bias, w[wi], r ? 0x04030401u : 0x04020400u);
   } else if constexpr (BITS == 3) {
-    const uint32_t t = field<6 * P, 6>(w);       // codes 2P, 2P+1: bits [6P, 6P+6)
-    return ((t | (t << 13)) & c.mask) | c.bias;
+    constexpr int o = P / 4, r = P % 4;
+    const uint32_t v = window<(r < 2) ? 24 * o - 4 : 24 * o + 2, 3>(w);
+    return (v & ((r & 1) ? c.mask2 : c.mask)) | c.bias;
   } else {
-    constexpr int run = P / 8, q = P % 8;         // two 96-bit runs of 16 codes
-    const uint32_t t = (run == 0) ? field<12 * q, 12>(w) : field<96 + 12 * q, 12>(w);
-    return ((t | (t << 10)) & c.mask) | c.bias;
+    constexpr int o = P / 4, r = P % 4;
+    constexpr int off[4] = {-4, 2, 20, 26};
+    const uint32_t v = window<48 * (o % 2) + off[r], 3>(w + 3 * (o / 2));
+    return (v & c.mask) | c.bias;
   }
 }
 
@@ -127,10 +162,21 @@ __device__ __forceinline__ void unpack_pairs(const uint32_t (&w)[BITS], UnpackCo
   if constexpr (P + 1 < 16) unpack_pairs<BITS, P + 1>(w, c, p);
 }
 
+// int3 and int6: the factor 2^s of the low and high half of pair e
+template <int BITS>
+__host__ __device__ constexpr float up_lo(int e) {
+  return BITS == 3 ? ((e & 1) ? 128.f : 16.f) : 16.f;
+}
+template <int BITS>
+__host__ __device__ constexpr float up_hi(int e) {
+  return BITS == 3 ? ((e & 1) ? 8.f : 1.f) : 1.f;
+}
+
 // fp16 activation pairs in the order unpack_pairs produces code pairs (the
-// lane's 8 values are codes 8w..8w+7 of its 32-code slice), and their
-// contribution to the slice sums: x_eff (what multiplies q) and x_st (what
-// multiplies the 1024 offset).
+// lane's 8 values are codes 8o..8o+7 of its 32-code slice, octet o), each
+// pre-multiplied by 2^-s of its code's position, and their contribution to
+// the slice sums: x_eff (what multiplies q: the values as meant) and x_st
+// (what multiplies the 1024 offset: the values as stored).
 template <int BITS>
 __device__ __forceinline__ void pairs_in_dot_order(const float (&v)[8], uint32_t (&o)[4], float &x_eff,
                                                    float &x_st) {
@@ -144,22 +190,34 @@ __device__ __forceinline__ void pairs_in_dot_order(const float (&v)[8], uint32_t
                     half_bits_to_float(o[3] & 0xFFFF) + half_bits_to_float(o[3] >> 16);
     x_eff = a + 16.0f * b;
     x_st = a + b;
-  } else {
-    if constexpr (BITS == 8) {
-      o[0] = pack_half2(v[0], v[2]); o[1] = pack_half2(v[1], v[3]);
-      o[2] = pack_half2(v[4], v[6]); o[3] = pack_half2(v[5], v[7]);
-    } else {
-      o[0] = pack_half2(v[0], v[1]); o[1] = pack_half2(v[2], v[3]);
-      o[2] = pack_half2(v[4], v[5]); o[3] = pack_half2(v[6], v[7]);
-    }
+  } else if constexpr (BITS == 8) {
+    o[0] = pack_half2(v[0], v[2]); o[1] = pack_half2(v[1], v[3]);
+    o[2] = pack_half2(v[4], v[6]); o[3] = pack_half2(v[5], v[7]);
     float a = 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) a += half_bits_to_float(o[e] & 0xFFFF) + half_bits_to_float(o[e] >> 16);
     x_eff = a;
     x_st = a;
+  } else {
+    if constexpr (BITS == 3) {
+      o[0] = pack_half2(v[0] * 0.0625f, v[4]); o[1] = pack_half2(v[1] * 0.0078125f, v[5] * 0.125f);
+      o[2] = pack_half2(v[2] * 0.0625f, v[6]); o[3] = pack_half2(v[3] * 0.0078125f, v[7] * 0.125f);
+    } else {
+      o[0] = pack_half2(v[0] * 0.0625f, v[2]); o[1] = pack_half2(v[1] * 0.0625f, v[3]);
+      o[2] = pack_half2(v[4] * 0.0625f, v[6]); o[3] = pack_half2(v[5] * 0.0625f, v[7]);
+    }
+    // sums of the stored halves that share one factor 2^s back to the
+    // values meant: low halves of the even and odd pairs, high halves likewise
+    float lo[2] = {0.f, 0.f}, hi[2] = {0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      lo[e & 1] += half_bits_to_float(o[e] & 0xFFFF);
+      hi[e & 1] += half_bits_to_float(o[e] >> 16);
+    }
+    x_eff = up_lo<BITS>(0) * lo[0] + up_lo<BITS>(1) * lo[1] + up_hi<BITS>(0) * hi[0] + up_hi<BITS>(1) * hi[1];
+    x_st = (lo[0] + lo[1]) + (hi[0] + hi[1]);
   }
 }
-
 
 __device__ __forceinline__ void store_out(const LinDesc &L, int m, int row, float v) {
   if (L.out_f32) {
@@ -213,13 +271,13 @@ __device__ __forceinline__ u32x4 load8_h(rsrc_t rs, int e0, int n) {
 // (the branch is uniform across the 16 lanes of a row).
 // With SUMS_IN_SLICE the two slice sums go into the slice's spare bytes
 // (words 16 and 17 of its 20), so one LDS address serves both.
-template <int BITS, int MT, bool SUMS_IN_SLICE = false>
-__device__ __forceinline__ void rotate_item(bool rotate, u32x4 raw, uint32_t sword, int nb, int items, int it,
-                                            int jj, uint32_t *xp, float *xs, int S) {
-  if (it >= items) return;
-  int m, b;
-  item_mb<MT>(it, nb, m, b);
-  const int kk = 128 * b + 8 * jj;
+// Lane jj's eight activations of a 128-block (element kk = 128 b + 8 jj
+// onwards): signs, butterflies and 1/sqrt(128) when rotating, then fp16
+// pairs in dot order and the two slice sums (summed over the 4 lanes of the
+// slice).
+template <int BITS>
+__device__ __forceinline__ void arrange8(bool rotate, u32x4 raw, uint32_t sword, int kk, int jj, uint32_t (&o)[4],
+                                         float &xe, float &xt) {
   float v[8];
   v[0] = half_bits_to_float(raw.x & 0xFFFF); v[1] = half_bits_to_float(raw.x >> 16);
   v[2] = half_bits_to_float(raw.y & 0xFFFF); v[3] = half_bits_to_float(raw.y >> 16);
@@ -234,13 +292,23 @@ __device__ __forceinline__ void rotate_item(bool rotate, u32x4 raw, uint32_t swo
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] *= sc;
   }
-  uint32_t o[4];
-  float xe, xt;
   pairs_in_dot_order<BITS>(v, o, xe, xt);
   xe += dpp<kQuadXor1>(xe);
   xe += dpp<kQuadXor2>(xe);
   xt += dpp<kQuadXor1>(xt);
   xt += dpp<kQuadXor2>(xt);
+}
+
+template <int BITS, int MT, bool SUMS_IN_SLICE = false>
+__device__ __forceinline__ void rotate_item(bool rotate, u32x4 raw, uint32_t sword, int nb, int items, int it,
+                                            int jj, uint32_t *xp, float *xs, int S) {
+  if (it >= items) return;
+  int m, b;
+  item_mb<MT>(it, nb, m, b);
+  const int kk = 128 * b + 8 * jj;
+  uint32_t o[4];
+  float xe, xt;
+  arrange8<BITS>(rotate, raw, sword, kk, jj, o, xe, xt);
   const int slice = 4 * b + (jj >> 2);
   *reinterpret_cast<u32x4 *>(&xp[(m * S + slice) * kSliceStride + 4 * (jj & 3)]) = u32x4{o[0], o[1], o[2], o[3]};
   if ((jj & 3) == 0) {
@@ -888,6 +956,313 @@ __device__ __forceinline__ void stream_ring(const LinDesc &L, int r0, int rows, 
   }
 }
 
+// ---------------------------------------------------------------------------
+// Batch tiles 2 and 4: row quads, activations arranged once.
+//
+// With more than one batch row, rotating the activations in every
+// workgroup would cost more than the workgroup's share of the product (each
+// workgroup needs the whole K for every batch row), and a task of two rows
+// would read every activation slice from LDS once per row.  So:
+//   * one pre-pass (xprep_kernel) rotates each linear's activations once and
+//     writes them in the LDS slice layout below (fp16 pairs in the order the
+//     unpacker produces code pairs, the two slice sums in words 16 and 17);
+//     each workgroup copies that block into LDS, its loads issued before the
+//     first code loads so that waiting for them never waits for the weights;
+//   * a 16-lane DPP row owns a "unit": one row quad and a contiguous range of
+//     its 512-wide K segments (the whole K when the workgroup has at least
+//     32 quads; otherwise p = 32 / quads DPP rows share a quad, one part of
+//     K each).  It walks the unit's segments in order, keeping the 4 x MT
+//     scaled partials of its lanes in registers;
+//   * per segment a lane unpacks its 32-code slice of the four rows once,
+//     then for each batch row reads the slice's activations once and feeds
+//     all four rows (four v_dot2 chains per slice read); the chain starts
+//     from the zero-point and offset correction, and the scale multiplies
+//     the slice's sum into the accumulator;
+//   * at the unit's end the partials are summed over the 16 lanes by a
+//     reduce-scatter (each step halves the values a lane holds and pairs it
+//     with a lane of the other half), leaving one value per lane, which goes
+//     to LDS; the p parts of each row are added in order at the end.
+// 512-thread workgroups (two waves per SIMD) give each lane the registers
+// for the four rows' unpacked codes.
+// ---------------------------------------------------------------------------
+
+constexpr int kQuadThreads = 512;
+constexpr int kQRG = kQuadThreads / 16;   // DPP rows per workgroup
+
+// One reduce-scatter step over V values: lanes whose `hi` bit is clear keep
+// the lower half and receive their partner's lower half; the others the
+// upper half.  CTRL pairs each lane with one in the other half.
+template <int CTRL, int V>
+__device__ __forceinline__ void rs_step(float (&v)[16], bool hi) {
+#pragma unroll
+  for (int e = 0; e < V / 2; ++e) {
+    const float keep = hi ? v[e + V / 2] : v[e];
+    const float send = hi ? v[e] : v[e + V / 2];
+    v[e] = keep + dpp<CTRL>(send);
+  }
+}
+
+// Sum V (8 or 16) values over the 16 lanes of a DPP row.  Lane j returns
+// the sum of value j (V = 16) or j >> 1 (V = 8, lanes j and j ^ 1 alike).
+template <int V>
+__device__ __forceinline__ float reduce_scatter16(float (&v)[16], int j) {
+  static_assert(V == 8 || V == 16, "4 rows x 2 or 4 batch rows");
+  rs_step<kRowRor8, V>(v, j & 8);
+  rs_step<kRowHalfMirror, V / 2>(v, j & 4);
+  rs_step<kQuadXor2, V / 4>(v, j & 2);
+  if constexpr (V == 16) {
+    rs_step<kQuadXor1, 2>(v, j & 1);
+  } else {
+    v[0] += dpp<kQuadXor1>(v[0]);
+  }
+  return v[0];
+}
+
+// DPP rows per quad: with fewer quads than DPP rows they share them, one
+// contiguous part of the K segments each (at least one segment per part).
+__host__ __device__ inline int quad_split(int nq, int ks) {
+  const int p = nq >= kQRG ? 1 : kQRG / nq;
+  return p < ks ? p : ks;
+}
+
+struct QuadLds {
+  int part, szl, total;   // 4-byte words
+};
+
+__host__ __device__ inline QuadLds quad_lds(int mt, int S, int KS, int G, int nq) {
+  QuadLds l;
+  const int p = quad_split(nq, KS);
+  l.part = (mt * S * kSliceStride + 3) & ~3;      // activations [mt][S][20], sums in words 16, 17
+  l.szl = (l.part + 4 * nq * p * mt + 1) & ~1;    // row parts [4 nq][p][mt]
+  l.total = l.szl + ((4 * nq * G + 7) & ~7) * 2;  // scale, zero as fp32 [4 nq][G][2], whole groups of 8
+  return l;
+}
+
+// Unit u (= quad q, part sub of p): its segments [s, e).
+__device__ __forceinline__ void unit_range(int u, int p, int KS, int &q, int &s, int &e) {
+  q = u / p;
+  const int sub = u - q * p;
+  s = KS * sub / p;
+  e = KS * (sub + 1) / p;
+}
+
+template <int BITS, int MT, int D>
+__device__ __forceinline__ void stream_quads(const LinDesc &L, int m_valid, int r0, int rows, uint32_t *smem) {
+  static_assert(MT == 2 || MT == 4, "batch tile");
+  constexpr int ZL = 2;
+  constexpr int XCH = 3 * MT;               // 8 KB copy passes held in registers (K <= 9830 at MT 4)
+  const int t = threadIdx.x, rg = t >> 4, j = t & 15;
+  const int K = L.k, KS = (K + kSeg - 1) / kSeg, G = K / kGroup, S = K / kSlice;
+  const int wpr = S * BITS;
+  const int NQ = (rows + 3) >> 2;
+  const int p = quad_split(NQ, KS), NU = NQ * p;
+  const bool full = (K % kSeg) == 0;
+  const QuadLds lay = quad_lds(MT, S, KS, G, NQ);
+  uint32_t *xp = smem;
+  float *part = reinterpret_cast<float *>(smem + lay.part);
+  float *szl = reinterpret_cast<float *>(smem + lay.szl);
+
+  const rsrc_t rc = make_rsrc(L.codes + (size_t)r0 * wpr, (uint32_t)rows * wpr * 4);
+  const int nszv = rows * G;
+  const rsrc_t rsc = make_rsrc(L.scales + (size_t)r0 * G, (uint32_t)nszv * 2);
+  const rsrc_t rz = make_rsrc(L.zeros + (size_t)r0 * G, (uint32_t)nszv * 2);
+
+  // 1. scales and zeros, then the arranged activations (batch rows past
+  //    m_valid read zero), ahead of the weight stream
+  const int nsz = 4 * NQ * G;               // scale/zero entries, padded to whole quads
+  u32x4 sr[ZL], zr[ZL];
+#pragma unroll
+  for (int q = 0; q < ZL; ++q) {
+    const int e0 = 8 * (t + kQuadThreads * q);
+    sr[q] = load8_h(rsc, e0, nszv);
+    zr[q] = load8_h(rz, e0, nszv);
+  }
+  // the first XCH 8 KB passes of the copy go to registers here and to LDS
+  // once the code loads are out (their waits then cover these loads alone)
+  const int xtotal = MT * S * kSliceStride * 4;          // bytes of the LDS block
+  const rsrc_t rxq = make_rsrc(L.xq, (uint32_t)(m_valid * S * kSliceStride * 4));
+  u32x4 xr[XCH];
+#pragma unroll
+  for (int c = 0; c < XCH; ++c) {
+    const int off = 16 * (t + kQuadThreads * c);
+    xr[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rxq, off < xtotal ? (uint32_t)off : kOOB,
+                                                                            0, 0));
+  }
+
+  // 2. the first D steps of this DPP row's tasks
+  const uint32_t seg_step = 16 * BITS * 4;
+  const uint32_t row_bytes = (uint32_t)wpr * 4;
+  const uint32_t quad_bytes = 4 * row_bytes;
+  const uint32_t lane_off = (uint32_t)j * (BITS * 4);
+  int lu = rg, lq, ls, le;                  // load side: unit, quad, segment, end
+  unit_range(lu, p, KS, lq, ls, le);
+  uint32_t cw[D][4][BITS];
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    const bool ok = lu < NU && (full || ls * 16 + j < S);
+    const uint32_t co = __umul24((uint32_t)lq, quad_bytes) + (uint32_t)ls * seg_step + lane_off;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) load_slice<BITS>(rc, ok ? co + r * row_bytes : kOOB, cw[d][r]);
+    if (++ls == le) { lu += kQRG; unit_range(lu, p, KS, lq, ls, le); }
+  }
+
+  // 3. scales, zeros and activations into LDS
+#pragma unroll
+  for (int q = 0; q < ZL; ++q) {
+    const int e0 = 8 * (t + kQuadThreads * q);
+    if (e0 < nsz) {
+      const uint32_t av[4] = {sr[q].x, sr[q].y, sr[q].z, sr[q].w};
+      const uint32_t bv[4] = {zr[q].x, zr[q].y, zr[q].z, zr[q].w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h)
+        *reinterpret_cast<float4 *>(&szl[2 * (e0 + 2 * h)]) =
+            make_float4(half_bits_to_float(av[h] & 0xFFFF), half_bits_to_float(bv[h] & 0xFFFF),
+                        half_bits_to_float(av[h] >> 16), half_bits_to_float(bv[h] >> 16));
+    }
+  }
+  for (int e0 = 8 * (t + kQuadThreads * ZL); e0 < nsz; e0 += 8 * kQuadThreads) {
+    const u32x4 a = load8_h(rsc, e0, nszv);
+    const u32x4 b = load8_h(rz, e0, nszv);
+    const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+      *reinterpret_cast<float4 *>(&szl[2 * (e0 + 2 * h)]) =
+          make_float4(half_bits_to_float(av[h] & 0xFFFF), half_bits_to_float(bv[h] & 0xFFFF),
+                      half_bits_to_float(av[h] >> 16), half_bits_to_float(bv[h] >> 16));
+  }
+#pragma unroll
+  for (int c = 0; c < XCH; ++c) {
+    const int off = 16 * (t + kQuadThreads * c);
+    if (off < xtotal) *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(xp) + off) = xr[c];
+  }
+  for (int off = 16 * (t + kQuadThreads * XCH); off < xtotal; off += 16 * kQuadThreads)
+    *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(xp) + off) =
+        __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rxq, (uint32_t)off, 0, 0));
+  __syncthreads();
+
+  // 4. walk the units: values r * MT + m accumulate s * sum (q - z) x over
+  //    the unit's segments
+  const UnpackConsts uc = unpack_consts<BITS>();
+  int cu = rg, cq, cs, ce;                  // compute side
+  unit_range(cu, p, KS, cq, cs, ce);
+  const int steps = ((NU + kQRG - 1) / kQRG) * ((KS + p - 1) / p);
+  float acc[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+  for (int i0 = 0; i0 < steps; i0 += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      if (cu < NU) {
+        const int slice = cs * 16 + j;
+        const bool sv = full || slice < S;
+        const int sl = sv ? slice : 0;
+        const uint32_t zi = __umul24((uint32_t)(4 * cq), (uint32_t)G) + (uint32_t)(sl >> 2);
+        float sf[4], zf[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float2 sz = *reinterpret_cast<const float2 *>(&szl[2 * (zi + r * G)]);
+          sf[r] = sv ? sz.x : 0.f;
+          zf[r] = sz.y;
+        }
+        uint32_t pr[4][16];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) unpack_pairs<BITS>(cw[d][r], uc, pr[r]);
+        // s * (sum (1024+q') x' - 1024 XS - z X) = s * sum (q - z) x
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          const uint32_t *src = &xp[(m * S + sl) * kSliceStride];
+          uint32_t xv[16];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const u32x4 v = reinterpret_cast<const u32x4 *>(src)[q];
+            xv[4 * q + 0] = v.x; xv[4 * q + 1] = v.y; xv[4 * q + 2] = v.z; xv[4 * q + 3] = v.w;
+          }
+          const float2 xq = *reinterpret_cast<const float2 *>(src + 16);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float dd = fmaf(-zf[r], xq.x, -xq.y);
+#pragma unroll
+            for (int q = 0; q < 16; ++q) dd = dot2(pr[r][q], xv[q], dd);
+            acc[r * MT + m] = fmaf(sf[r], dd, acc[r * MT + m]);
+          }
+        }
+        if (cs + 1 == ce) {
+          // the unit is done: its row parts over the 16 lanes, one per lane
+          const float v = reduce_scatter16<4 * MT>(acc, j);
+          const int vi = (4 * MT == 16) ? j : (j >> 1);
+          const int sub = cu - cq * p;
+          if (4 * MT == 16 || (j & 1) == 0)
+            part[((4 * cq + vi / MT) * p + sub) * MT + vi % MT] = v;
+#pragma unroll
+          for (int v2 = 0; v2 < 16; ++v2) acc[v2] = 0.f;
+          cu += kQRG;
+          unit_range(cu, p, KS, cq, cs, ce);
+        } else {
+          ++cs;
+        }
+      }
+      // refill this buffer with the task D steps ahead
+      const bool ok = lu < NU && (full || ls * 16 + j < S);
+      const uint32_t co = __umul24((uint32_t)lq, quad_bytes) + (uint32_t)ls * seg_step + lane_off;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) load_slice<BITS>(rc, ok ? co + r * row_bytes : kOOB, cw[d][r]);
+      if (++ls == le) { lu += kQRG; unit_range(lu, p, KS, lq, ls, le); }
+    }
+  }
+  __syncthreads();
+
+  // 5. add each row's parts in order, store
+  for (int e = t; e < rows * m_valid; e += kQuadThreads) {
+    const int row = e / m_valid, m = e % m_valid;
+    float sum = 0.f;
+    for (int u = 0; u < p; ++u) sum += part[(row * p + u) * MT + m];
+    store_out(L, m, r0 + row, sum);
+  }
+}
+
+// The pre-pass of the batch-tile kernels: every linear's activations, all m
+// rows, rotated (when the linear has signs) and arranged in the LDS slice
+// layout [m][K/32][20 words].  16 blocks of 128 per 256-thread workgroup;
+// workgroups dealt to the linears by a packed table of first workgroups.
+struct XprepMat {
+  const uint16_t *x;
+  uint32_t *out;
+  const uint32_t *signs;
+  int64_t ldx;
+  int32_t k, m, wg_begin;
+};
+
+struct XprepBatch {
+  int32_t first_wg[kMaxBatch];   // mat[i].wg_begin, packed; INT32_MAX past count
+  XprepMat mat[kMaxBatch];
+};
+
+template <int BITS>
+__global__ __launch_bounds__(256) void xprep_kernel(XprepBatch a) {
+  const int w = blockIdx.x;
+  int l = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxBatch; ++i)
+    if (w >= a.first_wg[i]) l = i;
+  const XprepMat M = a.mat[l];
+  const int nb = M.k / kGroup;
+  const int item = (w - M.wg_begin) * 16 + (int)(threadIdx.x >> 4);
+  if (item >= M.m * nb) return;   // whole 16-lane rows leave together
+  const int m = item / nb, b = item - m * nb, jj = threadIdx.x & 15;
+  const int kk = 128 * b + 8 * jj;
+  const u32x4 raw = *reinterpret_cast<const u32x4 *>(M.x + (size_t)m * M.ldx + kk);
+  const uint32_t sword = M.signs ? M.signs[kk >> 5] : 0u;
+  uint32_t o[4];
+  float xe, xt;
+  arrange8<BITS>(M.signs != nullptr, raw, sword, kk, jj, o, xe, xt);
+  const int S = M.k / kSlice, slice = 4 * b + (jj >> 2);
+  uint32_t *dst = M.out + ((size_t)m * S + slice) * kSliceStride;
+  *reinterpret_cast<u32x4 *>(dst + 4 * (jj & 3)) = u32x4{o[0], o[1], o[2], o[3]};
+  if ((jj & 3) == 0)
+    *reinterpret_cast<u32x4 *>(dst + 16) =
+        u32x4{__builtin_bit_cast(uint32_t, xe), __builtin_bit_cast(uint32_t, 1024.0f * xt), 0u, 0u};
+}
+
 template <int BITS, bool FULL>
 __global__ __launch_bounds__(kStreamThreads) void gemv_ring_kernel(GemvArgs a) {
   extern __shared__ uint32_t smem[];
@@ -918,6 +1293,24 @@ __global__ __launch_bounds__(kStreamThreads) void gemv_stream_kernel(GemvArgs a)
   stream_rows<BITS, MT, Depth<BITS, MT>::d>(L, a.m, r0, rows, smem);
 }
 
+// Segments of code loads a lane keeps in flight (4 rows x BITS words each);
+// deeper prefetch measured no faster, as most of a wave's segments are
+// then requested at once at the start.
+template <int BITS>
+struct QDepth {
+  static constexpr int d = 2;
+};
+
+template <int BITS, int MT>
+__global__ __launch_bounds__(kQuadThreads) void gemv_quad_kernel(GemvArgs a) {
+  extern __shared__ uint32_t smem[];
+  const int w = blockIdx.x;
+  const LinDesc L = fetch_desc(a, w);
+  const int r0 = (w - L.tile_begin) * L.rows_per_wg;
+  if (r0 >= L.n) return;
+  stream_quads<BITS, MT, QDepth<BITS>::d>(L, a.m, r0, min(L.rows_per_wg, L.n - r0), smem);
+}
+
 template <int BITS>
 hipError_t launch_bits(int mt, const GemvArgs &a, hipStream_t s) {
   if (a.ring) {
@@ -935,10 +1328,10 @@ hipError_t launch_bits(int mt, const GemvArgs &a, hipStream_t s) {
       hipLaunchKernelGGL((gemv_stream_kernel<BITS, 1>), dim3(a.tiles), dim3(kStreamThreads), a.lds_bytes, s, a);
       break;
     case 2:
-      hipLaunchKernelGGL((gemv_stream_kernel<BITS, 2>), dim3(a.tiles), dim3(kStreamThreads), a.lds_bytes, s, a);
+      hipLaunchKernelGGL((gemv_quad_kernel<BITS, 2>), dim3(a.tiles), dim3(kQuadThreads), a.lds_bytes, s, a);
       break;
     case 4:
-      hipLaunchKernelGGL((gemv_stream_kernel<BITS, 4>), dim3(a.tiles), dim3(kStreamThreads), a.lds_bytes, s, a);
+      hipLaunchKernelGGL((gemv_quad_kernel<BITS, 4>), dim3(a.tiles), dim3(kQuadThreads), a.lds_bytes, s, a);
       break;
     default:
       return hipErrorInvalidValue;
@@ -951,7 +1344,8 @@ hipError_t launch_bits(int mt, const GemvArgs &a, hipStream_t s) {
 int gemv_stream_lds_bytes(int bits, int mt, int64_t k, int rows_per_wg, bool ring) {
   const int64_t S = k / kSlice, KS = (k + kSeg - 1) / kSeg, G = k / kGroup;
   const int64_t np = (rows_per_wg + 1) / 2;
-  if (S * kSliceStride * mt + np * (KS + G) * 2 * mt > (int64_t)1 << 26) return 1 << 30;
+  if (S * kSliceStride * mt + np * (KS + G) * 4 * mt > (int64_t)1 << 26) return 1 << 30;
+  if (!ring && mt >= 2) return quad_lds(mt, (int)S, (int)KS, (int)G, (rows_per_wg + 3) / 4).total * 4;
   if (!ring) return stream_lds(mt, (int)S, (int)KS, (int)G, (int)np).total * 4;
   if (mt != 1) return 1 << 30;
   switch (bits) {
@@ -961,6 +1355,37 @@ int gemv_stream_lds_bytes(int bits, int mt, int64_t k, int rows_per_wg, bool rin
     case 8: return ring_lds((int)S, (int)KS, (int)np, Ring<8>::slot, Ring<8>::depth).total;
   }
   return 1 << 30;
+}
+
+hipError_t launch_xprep(int bits, int count, const uint16_t *const *x, const int64_t *ldx,
+                        const uint32_t *const *signs, const int64_t *k, int64_t m, uint32_t *const *out,
+                        hipStream_t s) {
+  if (count <= 0 || count > kMaxBatch || m <= 0) return hipErrorInvalidValue;
+  XprepBatch a;
+  memset(&a, 0, sizeof a);
+  for (int i = 0; i < kMaxBatch; ++i) a.first_wg[i] = INT32_MAX;
+  int64_t wgs = 0;
+  for (int i = 0; i < count; ++i) {
+    XprepMat &M = a.mat[i];
+    M.x = x[i];
+    M.out = out[i];
+    M.signs = signs[i];
+    M.ldx = ldx[i];
+    M.k = (int32_t)k[i];
+    M.m = (int32_t)m;
+    M.wg_begin = (int32_t)wgs;
+    a.first_wg[i] = (int32_t)wgs;
+    wgs += (m * (k[i] / kGroup) + 15) / 16;
+  }
+  if (wgs > INT32_MAX) return hipErrorInvalidValue;
+  switch (bits) {
+    case 3: hipLaunchKernelGGL(xprep_kernel<3>, dim3((unsigned)wgs), dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL(xprep_kernel<4>, dim3((unsigned)wgs), dim3(256), 0, s, a); break;
+    case 6: hipLaunchKernelGGL(xprep_kernel<6>, dim3((unsigned)wgs), dim3(256), 0, s, a); break;
+    case 8: hipLaunchKernelGGL(xprep_kernel<8>, dim3((unsigned)wgs), dim3(256), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_gemv_stream(int bits, int mt, const GemvArgs &a, hipStream_t s) {

@@ -38,6 +38,7 @@ struct LinDesc {
   int32_t tile_begin;           // first workgroup of this linear in the grid
   int32_t out_f32;
   int32_t ks_inv;               // ceil(2^16 / KS), KS = ceil(k / 512): x / KS = (x * ks_inv) >> 16 for x <= 64
+  const uint32_t *xq;           // batch tiles 2, 4: the tile's arranged activations [mt][k/32][20] (xprep)
 };
 
 struct GemvArgs {
@@ -56,6 +57,12 @@ hipError_t launch_gemv(int bits, int mt, const GemvArgs &a, hipStream_t s);
 // width, batch tile <= 4, the linear's whole rotated K range in LDS.
 constexpr int kStreamThreads = 1024;
 hipError_t launch_gemv_stream(int bits, int mt, const GemvArgs &a, hipStream_t s);
+// Batch tiles 2 and 4: one pass arranging every linear's m activation rows
+// (rotated when signs[i] is set) in the stream kernels' slice layout,
+// out[i] = [m][k/32][20] u32 (80 bytes per 32-element slice).
+hipError_t launch_xprep(int bits, int count, const uint16_t *const *x, const int64_t *ldx,
+                        const uint32_t *const *signs, const int64_t *k, int64_t m, uint32_t *const *out,
+                        hipStream_t s);
 // LDS bytes of one stream workgroup; ring = batch-1 kernel with the LDS ring
 int gemv_stream_lds_bytes(int bits, int mt, int64_t k, int rows_per_wg, bool ring);
 void gemv_shape(int bits, int mt, int64_t k, int &mode, int &rows);

@@ -162,7 +162,11 @@ wq_status rht_apply(const uint16_t *x, uint16_t *y, const uint32_t *signs,
                     void *stream);
 
 /* Bytes of workspace wq_linear needs for this weight and batch size m.
- * 0 means none is needed.  Returns (size_t)-1 for an invalid request. */
+ * 0 means none is needed: m = 1, or the mixed 6/8-bit layout below m = 64.
+ * For 2 <= m < 64 with one code width it is the arranged activations of up
+ * to 16 batch rows (80 bytes per 32 elements per row); for m >= 64 the
+ * matrix-core path's rotated activations and split-K partials.  Returns
+ * (size_t)-1 for an invalid request. */
 size_t wq_linear_workspace(const wq_weight *w, int64_t m);
 
 /* The layer: y[m][n] = sum_k (q[n][k] - z[n][g]) * s[n][g] * x'[m][k],
@@ -173,16 +177,18 @@ size_t wq_linear_workspace(const wq_weight *w, int64_t m);
  * m <= 16 runs the dequantising GEMV; 17 <= m < 64 runs it in chunks of 16
  * rows; m >= 64 runs the matrix-core GEMM (the weight is dequantised to
  * fp16 in registers before the contraction).  The rotated activations are
- * rounded to fp16 before the product.
+ * rounded to fp16 before the product.  Above one batch row the GEMV first
+ * rotates and arranges the activations into the workspace in one pass, then
+ * streams the weights once per tile of up to 4 batch rows.
  *   w          host struct describing the device weight
  *   x          fp16 [m][ldx]
  *   y          out: fp16 or fp32 [m][ldy] (y_dtype)
  *   workspace  device scratch of at least wq_linear_workspace(w, m) bytes
  *              (caller-owned, 16-byte aligned; NULL when that is 0).  The
- *              matrix-core path keeps the rotated activations there, and
- *              the fp32 partial sums when it splits a long K over several
- *              workgroups; its contents need no initialisation and are not
- *              preserved.
+ *              GEMV keeps the arranged activations there; the matrix-core
+ *              path the rotated activations and the fp32 partial sums when
+ *              it splits a long K over several workgroups.  Its contents
+ *              need no initialisation and are not preserved.
  */
 wq_status wq_linear(const wq_weight *w, const uint16_t *x, int64_t m, int64_t ldx,
                     void *y, wq_dtype y_dtype, int64_t ldy, uint32_t flags,
@@ -190,13 +196,15 @@ wq_status wq_linear(const wq_weight *w, const uint16_t *x, int64_t m, int64_t ld
 
 /* Several independent linears (up to WQ_MAX_BATCH), each with its own
  * weight, activations and output, all at the same batch size m and code
- * width.  For m <= 16 they run as one GEMV launch (workspace size 0).  For
- * m >= 64 with a uniform code width they run as one matrix-core launch
- * (after one launch rotating every linear's activations); the workspace of
- * wq_linear_batch_workspace bytes then holds every linear's rotated
- * activations and split-K partial sums.  Otherwise (17 <= m < 64, or the
- * mixed 6/8-bit layout) they run one after another on the stream exactly
- * as wq_linear would.  Same math and layout as wq_linear, applied to each
+ * width.  For m <= 16 they run as one GEMV launch per tile of up to 4 batch
+ * rows (after, for m > 1, one launch arranging every linear's activations
+ * in the workspace).  For m >= 64 with a uniform code width they run as one
+ * matrix-core launch (after one launch rotating every linear's
+ * activations); the workspace of wq_linear_batch_workspace bytes then holds
+ * every linear's rotated activations and split-K partial sums.  Otherwise
+ * (17 <= m < 64, or the mixed 6/8-bit layout above m = 16) they run one
+ * after another on the stream exactly as wq_linear would, sharing the
+ * workspace.  Same math and layout as wq_linear, applied to each
  * w[i], x[i], y[i].  Arrays of length `count` are host arrays. */
 size_t wq_linear_batch_workspace(int32_t count, const wq_weight *w, int64_t m);
 wq_status wq_linear_batch(int32_t count, const wq_weight *w,

@@ -114,12 +114,28 @@ def test_linear_rejects_bad_io(lib, args, status, text):
     assert text in lib.wq_last_error().decode()
 
 
+def _arranged(k, m):
+    # the batch-tile GEMV's arranged activations: 80 bytes per 32 elements
+    # and batch row, rounded up to 256 bytes
+    return (m * (k // 32) * 80 + 255) // 256 * 256
+
+
 def test_workspace_sizes(lib):
-    # the GEMV (m < 64) keeps its partial sums in LDS: no workspace at any K
+    # batch 1: the GEMV keeps everything in LDS, no workspace at any K
     assert lib.wq_linear_workspace(ctypes.byref(_weight()), 1) == 0
     w = _weight(n=4096, k=2560, rht_signs=16, rht_block=128)
-    for m in (1, 16, 63):
-        assert lib.wq_linear_workspace(ctypes.byref(w), m) == 0
+    assert lib.wq_linear_workspace(ctypes.byref(w), 1) == 0
+    # 2..63 rows: the arranged activations of a chunk of up to 16 rows
+    for m in (2, 3, 4, 16):
+        assert lib.wq_linear_workspace(ctypes.byref(w), m) == _arranged(2560, m)
+    for m in (17, 63):
+        assert lib.wq_linear_workspace(ctypes.byref(w), m) == _arranged(2560, 16)
+    # without rotation the activations are still arranged (pair order, sums)
+    w_plain = _weight(n=4096, k=2560)
+    assert lib.wq_linear_workspace(ctypes.byref(w_plain), 4) == _arranged(2560, 4)
+    # the mixed 6/8-bit layout runs the tiled GEMV, which needs none
+    w_mixed = _weight(bits=0, n=128, k=256, block_bits=16, block_off=16)
+    assert lib.wq_linear_workspace(ctypes.byref(w_mixed), 16) == 0
     # the matrix-core path (m >= 64) stages the rotated activations, fp16 [m][k]
     assert lib.wq_linear_workspace(ctypes.byref(w), 64) >= 64 * 2560 * 2
     assert lib.wq_linear_workspace(ctypes.byref(w), 0) == ctypes.c_size_t(-1).value
@@ -147,12 +163,16 @@ def test_other_entry_points_reject(lib):
 
 
 def test_batch_workspace_for_large_m(lib):
-    # m <= 16: one GEMV launch, no workspace; m >= 64: one matrix-core launch
-    # over all the linears, whose workspace holds every linear's rotated
-    # activations (fp16 [m][k]) and the fp32 partial sums of split K
+    # m = 1: no workspace; 2 <= m <= 16: every linear's arranged activations
+    # side by side; 17 <= m < 64: the largest single linear's chunk; m >= 64:
+    # one matrix-core launch over all the linears, whose workspace holds
+    # every linear's rotated activations (fp16 [m][k]) and the fp32 partial
+    # sums of split K
     sg = dict(rht_signs=16, rht_block=128)
     arr = (dq.WqWeight * 2)(_weight(n=256, k=2560, **sg), _weight(n=128, k=9728, **sg))
-    assert lib.wq_linear_batch_workspace(2, arr, 16) == 0
+    assert lib.wq_linear_batch_workspace(2, arr, 1) == 0
+    assert lib.wq_linear_batch_workspace(2, arr, 16) == _arranged(2560, 16) + _arranged(9728, 16)
+    assert lib.wq_linear_batch_workspace(2, arr, 5) == _arranged(2560, 5) + _arranged(9728, 5)
     need = lib.wq_linear_batch_workspace(2, arr, 512)
     assert need >= 512 * (2560 + 9728) * 2
     assert need >= lib.wq_linear_workspace(ctypes.byref(arr[0]), 512)
@@ -182,3 +202,22 @@ def test_stream_read_rejects_bad_arguments(lib):
     assert lib.wq_stream_read(16, 0, 16, None) == dq.WQ_E_ARG
     assert lib.wq_stream_read(16, 24, 16, None) == dq.WQ_E_ARG
     assert lib.wq_stream_read(8, 16, 16, None) == dq.WQ_E_ALIGN
+
+
+def test_gemv_batch_rejects_small_workspace(lib):
+    # above one batch row the GEMV arranges the activations in the workspace;
+    # a missing or short one is refused before anything is launched
+    sg = dict(rht_signs=16, rht_block=128)
+    w = _weight(n=256, k=2560, **sg)
+    need = lib.wq_linear_workspace(ctypes.byref(w), 4)
+    assert need == _arranged(2560, 4)
+    st = lib.wq_linear(ctypes.byref(w), 16, 4, 2560, 16, dq.WQ_F16, 256, dq.WQ_FUSE_RHT, 16, need - 16, None)
+    assert st == dq.WQ_E_WORKSPACE
+    arr = (dq.WqWeight * 1)(w)
+    xs = (ctypes.c_void_p * 1)(16)
+    lds = (ctypes.c_int64 * 1)(2560)
+    ys = (ctypes.c_void_p * 1)(16)
+    dts = (ctypes.c_int32 * 1)(dq.WQ_F16)
+    ldy = (ctypes.c_int64 * 1)(256)
+    st = lib.wq_linear_batch(1, arr, xs, lds, 4, ys, dts, ldy, dq.WQ_FUSE_RHT, None, 0, None)
+    assert st == dq.WQ_E_WORKSPACE

@@ -235,21 +235,24 @@ def test_linear_mixed(m, rht):
     check_close(y.float().cpu().numpy(), ref, "mixed")
 
 
-def test_mixed_all_six_equals_uniform_six():
-    # At m = 2 the mixed-width and uniform kernels share the arithmetic and
-    # its order, so all-6-bit blocks must give the uniform int6 result bit
-    # for bit.  At m = 1 the uniform path stages weights through LDS and sums
-    # in another order: there both are held to the oracle.
+def test_mixed_all_six_matches_uniform_six():
+    # All-6-bit blocks in the mixed layout hold the same codes, scales and
+    # zeros as the uniform int6 layout: the packed words agree bit for bit,
+    # and both layouts' products meet the oracle at m = 1 and m = 2.  (The
+    # two run different kernels, which sum in different orders, so their
+    # outputs are compared through the oracle, not with each other.)
     say("mixed all-6 == int6")
     n, k = 128, 512
     w, x, signs = _inputs(n, k, 2, 31)
     sel = np.array([6, 6], np.uint8)
     mixed, uni = _gpu_weight(w, signs, 0, sel), _gpu_weight(w, signs, 6)
-    assert torch.equal(dq.wq_linear(mixed, dev(x)), dq.wq_linear(uni, dev(x)))
+    assert torch.equal(mixed.codes, uni.codes)
+    assert torch.equal(mixed.scales, uni.scales) and torch.equal(mixed.zeros, uni.zeros)
     q, s, z = OR.prepare(w, signs, 6)
-    ref = OL.linear(q, s, z, x[:1], signs)
-    for qw in (mixed, uni):
-        check_close(dq.wq_linear(qw, dev(x[:1])).float().cpu().numpy(), ref, "all-6 m=1")
+    for mm in (1, 2):
+        ref = OL.linear(q, s, z, x[:mm], signs)
+        for qw in (mixed, uni):
+            check_close(dq.wq_linear(qw, dev(x[:mm])).float().cpu().numpy(), ref, f"all-6 m={mm}")
 
 
 def test_batch_call_matches_single_calls():
@@ -266,19 +269,19 @@ def test_batch_call_matches_single_calls():
         assert torch.equal(a, b)
 
 
-def test_deterministic_and_workspace_left_zero():
+def test_deterministic_with_uninitialised_workspace():
+    # the workspace needs no initialisation: one filled with NaN bit
+    # patterns gives the same bits as a zeroed one, call after call
     say("determinism")
     w, x, signs = _inputs(512, 4096, 2, 5)
     qw = _gpu_weight(w, signs, 4)
-    ws = dq.new_workspace(dq.wq_linear_workspace(qw, 2))
+    need = dq.wq_linear_workspace(qw, 2)
+    assert need > 0
     xd = dev(x)
-    first = dq.wq_linear(qw, xd, workspace=ws)
+    first = dq.wq_linear(qw, xd, workspace=dq.new_workspace(need))
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
     for _ in range(5):
         assert torch.equal(dq.wq_linear(qw, xd, workspace=ws), first)
-    torch.cuda.synchronize()
-    # fp32 partials may stay; the arrival counters (the tail) must be zero again
-    n_counter_bytes = (512 + 127) // 128 * 4
-    assert int(ws[-256:][:n_counter_bytes].count_nonzero()) == 0
 
 
 def test_graph_replay_matches_eager():
