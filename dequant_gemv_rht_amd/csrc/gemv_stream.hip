@@ -564,20 +564,29 @@ __device__ __forceinline__ void stream_rows(const LinDesc &L, int m_valid, int r
 // loop, so the compiler has no load of its own to wait for there.
 // ---------------------------------------------------------------------------
 
-// A row's BITS words per lane travel as direct loads of 16 or 4 bytes per
-// lane (lane L's bytes land at chunk + L * size): int3 3 x 4, int4 16,
-// int6 16 + 4 + 4, int8 16 + 16.  Chunk c covers words [word(c), word(c) +
-// size / 4) and sits at byte 64 * 4 * word(c) of the row's region.
+// int4 and int8: a row's BITS words per lane travel as direct loads of 16
+// bytes per lane (lane L's bytes land at chunk + 16 L), int4 one, int8 two;
+// chunk c covers words [4c, 4c + 4) and sits at byte 64 * 16 c of the row's
+// region.  The wave's four DPP rows hold consecutive tasks, so each load
+// reads 1 KB of consecutive bytes unless the tasks wrap to the next row pair.
+//
+// int3 and int6 ("flat"): a lane's slice is 12 or 24 bytes, so the step's
+// code bytes travel as 16-byte items in their order in LDS: row r of the
+// pair, then DPP row g, then 16-byte piece c of g's run of 16 slices.  Item
+// i = 64 k + L is lane L's piece in load k (int3: two loads, the second for
+// lanes 0..31; int6: three), read from g's task.  Lane j of DPP row g finds
+// row r of its slice at byte 256 BITS r + 64 BITS g + 4 BITS j of the
+// region.
 template <int BITS>
 struct Ring {
-  static constexpr int nc = BITS == 3 ? 3 : BITS == 4 ? 1 : BITS == 6 ? 3 : 2;   // loads per row
-  __host__ __device__ static constexpr int size(int c) { return BITS == 3 ? 4 : (BITS == 6 && c > 0) ? 4 : 16; }
-  __host__ __device__ static constexpr int word(int c) { return BITS == 3 ? c : BITS == 6 ? (c == 0 ? 0 : 3 + c) : 4 * c; }
+  static constexpr bool flat = BITS == 3 || BITS == 6;
+  static constexpr int nc = BITS == 4 ? 1 : 2;                      // loads per row (int4, int8)
   static constexpr int row = 64 * 4 * BITS;                         // bytes per row per wave per step
   static constexpr int codes = 2 * row;                             // code bytes per wave per step
+  static constexpr int ni = (codes + 1023) / 1024;                  // loads per step (flat)
   static constexpr int slot = codes + 2 * 64 * 4;                   // + scales, zeros
   static constexpr int depth = BITS == 3 ? 4 : BITS == 4 ? 3 : 2;  // steps in flight
-  static constexpr int q = 2 * nc + 2;                             // vector loads per wave per step
+  static constexpr int q = (flat ? ni : 2 * nc) + 2;               // vector loads per wave per step
 };
 
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
@@ -590,8 +599,7 @@ template <int BITS, int C = 0>
 __device__ __forceinline__ void ring_row_loads(rsrc_t rc, uint32_t row, uint32_t off) {
   using RS = Ring<BITS>;
 #if defined(__HIP_DEVICE_COMPILE__)   // 16-byte LDS loads exist only in the gfx950 pass
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (lds_ptr_t)(row + 256 * RS::word(C)), RS::size(C),
-                                           off + 4 * RS::word(C), 0, 0, kNT);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (lds_ptr_t)(row + 1024 * C), 16, off + 16 * C, 0, 0, kNT);
 #endif
   if constexpr (C + 1 < RS::nc) ring_row_loads<BITS, C + 1>(rc, row, off);
 }
@@ -611,14 +619,36 @@ struct RingCursor {
   int ls;
   uint32_t lco;   // byte offset of this lane's code words, row 0 of the task
   uint32_t lso;   // byte offset of the scale/zero this lane fetches (lanes 0..7 of a task)
+  // flat layouts: per load k, the segment and byte offset of this lane's item
+  int fls[RS::flat ? RS::ni : 1];
+  uint32_t flco[RS::flat ? RS::ni : 1];
+  bool flast;     // int3: this lane carries an item in the last load
 
   template <int D>
   __device__ __forceinline__ void issue() {
     const uint32_t slot = slot0 + D * (kStreamThreads / 64) * RS::slot;
-    // row 2p + 1 at the same offset from the second row: past the last row
-    // (an odd row count) it is out of range and reads zero
-    ring_row_loads<BITS>(rc, slot, lco);
-    ring_row_loads<BITS>(rc1, slot + RS::row, lco);
+    if constexpr (RS::flat) {
+#if defined(__HIP_DEVICE_COMPILE__)
+#pragma unroll
+      for (int k = 0; k < RS::ni; ++k) {
+        // items past the pair's last row are out of range and read zero
+        if (k + 1 < RS::ni || BITS == 6 || flast)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (lds_ptr_t)(slot + 1024 * k), 16, flco[k], 0, 0, kNT);
+      }
+#endif
+#pragma unroll
+      for (int k = 0; k < RS::ni; ++k) {
+        fls[k] += ds;
+        const bool w = fls[k] >= KS;
+        fls[k] = w ? fls[k] - KS : fls[k];
+        flco[k] += w ? wco : dco;
+      }
+    } else {
+      // row 2p + 1 at the same offset from the second row: past the last
+      // row (an odd row count) it is out of range and reads zero
+      ring_row_loads<BITS>(rc, slot, lco);
+      ring_row_loads<BITS>(rc1, slot + RS::row, lco);
+    }
 #if defined(__HIP_DEVICE_COMPILE__)
     // one fp16 per lane, zero-extended to 4 bytes at slot + 4 L: a 2-byte
     // load never reaches past the end of its range (a load that does
@@ -629,7 +659,7 @@ struct RingCursor {
     ls += ds;
     const bool wrap = ls >= KS;
     ls = wrap ? ls - KS : ls;
-    lco += wrap ? wco : dco;
+    if constexpr (!RS::flat) lco += wrap ? wco : dco;
     lso += wrap ? wso : dso;
   }
 };
@@ -730,15 +760,15 @@ __device__ __forceinline__ void read_task(uint32_t xa, uint32_t sza, uint32_t ca
     w[1][0] = c2.x; w[1][1] = c2.y; w[1][2] = c2.z; w[1][3] = c2.w;
     w[1][4] = c3.x; w[1][5] = c3.y; w[1][6] = c3.z; w[1][7] = c3.w;
   } else if constexpr (BITS == 3) {
-    // row r: word k at r * 768 + 256 k + 4 L
+    // row r: the lane's 12 bytes at r * 768 + 192 g + 12 j (ca4)
     uint32_t c[6];
     asm volatile(WQ_OPS_READS
                  "ds_read_b32 %[c0], %[ca4]\n\t"
-                 "ds_read_b32 %[c1], %[ca4] offset:256\n\t"
-                 "ds_read_b32 %[c2], %[ca4] offset:512\n\t"
+                 "ds_read_b32 %[c1], %[ca4] offset:4\n\t"
+                 "ds_read_b32 %[c2], %[ca4] offset:8\n\t"
                  "ds_read_b32 %[c3], %[ca4] offset:768\n\t"
-                 "ds_read_b32 %[c4], %[ca4] offset:1024\n\t"
-                 "ds_read_b32 %[c5], %[ca4] offset:1280\n\t"
+                 "ds_read_b32 %[c4], %[ca4] offset:772\n\t"
+                 "ds_read_b32 %[c5], %[ca4] offset:776\n\t"
                  "s_waitcnt lgkmcnt(0)"
                  : WQ_OPS_OUT, [c0] "=&v"(c[0]), [c1] "=&v"(c[1]), [c2] "=&v"(c[2]), [c3] "=&v"(c[3]),
                    [c4] "=&v"(c[4]), [c5] "=&v"(c[5])
@@ -750,24 +780,25 @@ __device__ __forceinline__ void read_task(uint32_t xa, uint32_t sza, uint32_t ca
       w[1][e] = c[3 + e];
     }
   } else {
-    // int6 row r: words 0..3 at r * 1536 + 16 L, word 4 at r * 1536 + 1024 + 4 L,
-    // word 5 at r * 1536 + 1280 + 4 L
-    u32x4 c0, c1;
-    uint32_t d0, d1, d2, d3;
+    // int6 row r: the lane's 24 bytes at r * 1536 + 384 g + 24 j (ca4)
+    uint64_t c[6];
     asm volatile(WQ_OPS_READS
-                 "ds_read_b128 %[c0], %[ca16]\n\t"
-                 "ds_read_b32 %[d0], %[ca4] offset:1024\n\t"
-                 "ds_read_b32 %[d1], %[ca4] offset:1280\n\t"
-                 "ds_read_b128 %[c1], %[ca16] offset:1536\n\t"
-                 "ds_read_b32 %[d2], %[ca4] offset:2560\n\t"
-                 "ds_read_b32 %[d3], %[ca4] offset:2816\n\t"
+                 "ds_read_b64 %[c0], %[ca4]\n\t"
+                 "ds_read_b64 %[c1], %[ca4] offset:8\n\t"
+                 "ds_read_b64 %[c2], %[ca4] offset:16\n\t"
+                 "ds_read_b64 %[c3], %[ca4] offset:1536\n\t"
+                 "ds_read_b64 %[c4], %[ca4] offset:1544\n\t"
+                 "ds_read_b64 %[c5], %[ca4] offset:1552\n\t"
                  "s_waitcnt lgkmcnt(0)"
-                 : WQ_OPS_OUT, [c0] "=&v"(c0), [c1] "=&v"(c1), [d0] "=&v"(d0), [d1] "=&v"(d1), [d2] "=&v"(d2),
-                   [d3] "=&v"(d3)
+                 : WQ_OPS_OUT, [c0] "=&v"(c[0]), [c1] "=&v"(c[1]), [c2] "=&v"(c[2]), [c3] "=&v"(c[3]),
+                   [c4] "=&v"(c[4]), [c5] "=&v"(c[5])
                  : WQ_OPS_IN
                  : "memory");
-    w[0][0] = c0.x; w[0][1] = c0.y; w[0][2] = c0.z; w[0][3] = c0.w; w[0][4] = d0; w[0][5] = d1;
-    w[1][0] = c1.x; w[1][1] = c1.y; w[1][2] = c1.z; w[1][3] = c1.w; w[1][4] = d2; w[1][5] = d3;
+#pragma unroll
+    for (int e = 0; e < 3; ++e) {
+      w[0][2 * e] = (uint32_t)c[e]; w[0][2 * e + 1] = (uint32_t)(c[e] >> 32);
+      w[1][2 * e] = (uint32_t)c[3 + e]; w[1][2 * e + 1] = (uint32_t)(c[3 + e] >> 32);
+    }
   }
 #undef WQ_OPS_READS
 #undef WQ_OPS_OUT
@@ -847,6 +878,20 @@ __device__ __forceinline__ void stream_ring(const LinDesc &L, int r0, int rows, 
     cur.wso = cur.dso + (uint32_t)(2 * (2 * G - 4 * KS));
     cur.ls = cs0;
     cur.lco = __umul24((uint32_t)cp0, pair_bytes) + (uint32_t)cs0 * seg_step + (uint32_t)j * (BITS * 4);
+    if constexpr (RS::flat) {
+      constexpr int per_row = 16 * BITS, per_g = 4 * BITS;   // 16-byte items per row, per DPP row's run
+#pragma unroll
+      for (int k = 0; k < RS::ni; ++k) {
+        const int i = 64 * k + lane;
+        const int r = i / per_row, ir = i - r * per_row, g = ir / per_g, c = ir - g * per_g;
+        const int rgk = 4 * wave + g;                   // the DPP row whose task this item belongs to
+        const int pk = (int)(__umul24((uint32_t)rgk, (uint32_t)L.ks_inv) >> 16), sk = rgk - pk * KS;
+        cur.fls[k] = sk;
+        cur.flco[k] = __umul24((uint32_t)pk, pair_bytes) + (uint32_t)sk * seg_step + (uint32_t)r * row_bytes +
+                      (uint32_t)(16 * c);
+      }
+      cur.flast = lane < 2 * per_row - 64 * (RS::ni - 1);
+    }
     // lanes j < 8 fetch the scale/zero of row 2p + (j >> 2), group 4s + (j & 3);
     // the other lanes start past any resource (bit 31 set) and stay there as the offset advances
     cur.lso = (__umul24((uint32_t)(2 * cp0 + (j >> 2)), (uint32_t)(2 * G)) + (uint32_t)(8 * cs0 + 2 * (j & 3))) |
@@ -887,7 +932,8 @@ __device__ __forceinline__ void stream_ring(const LinDesc &L, int r0, int rows, 
   const uint32_t dpa = (uint32_t)((2 * dp * KS + ds) * 4), wpa = dpa + (uint32_t)(KS * 4);
   int cs = cs0;   // only needed to mask slices of a partial last segment
   const uint32_t sza_l = cur.slot0 + RS::codes + (lane & 48) * 4 + (j >> 2) * 4;
-  const uint32_t ca16_l = cur.slot0 + lane * 16, ca4_l = cur.slot0 + lane * 4;
+  const uint32_t ca16_l = cur.slot0 + lane * 16;
+  const uint32_t ca4_l = cur.slot0 + (uint32_t)((lane >> 4) * (64 * BITS) + j * (4 * BITS));   // flat layouts
   constexpr uint32_t kStage = (kStreamThreads / 64) * RS::slot;   // bytes between ring stages
   // one step i in ring slot D (a compile-time constant, so slot addresses fold)
   auto step = [&](auto dconst, int i) {
