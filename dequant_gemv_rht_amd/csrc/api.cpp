@@ -234,7 +234,22 @@ wq_status launch_tile(int count, const wq_weight *w, const uint16_t *const *x, c
   for (int o = 0; o < count; ++o) ws[o] = w[order[o]];
   int wg[WQ_MAX_BATCH], rpw[WQ_MAX_BATCH], slds = 0;
   bool ring = false;
-  const bool stream = plan_stream(count, ws, m, rotate, wg, rpw, &slds, &ring);
+  bool stream = plan_stream(count, ws, m, rotate, wg, rpw, &slds, &ring);
+  if (!stream && count == 1 && w[0].bits == 0 && m == 1) {
+    // mixed 6/8 at batch 1: the ring, each workgroup inside one 64-row block
+    const int64_t nblk = w[0].n / WQ_MIXED_ROWS;
+    int64_t wpb = device_cus() / nblk;
+    wpb = wpb < 1 ? 1 : (wpb > WQ_MIXED_ROWS / 2 ? WQ_MIXED_ROWS / 2 : wpb);
+    const int r = (int)((WQ_MIXED_ROWS + wpb - 1) / wpb);
+    const int need = wq::gemv_stream_lds_bytes(0, 1, w[0].k, r, true);
+    if (need <= kMaxLds && nblk * wpb <= INT32_MAX) {
+      stream = ring = true;
+      slds = need;
+      rpw[0] = r;
+      wg[0] = (int)(nblk * wpb);
+      a.mixed_wpb = (int32_t)wpb;
+    }
+  }
   int64_t tiles = 0;
   int lds = 0;
   for (int o = 0; o < count; ++o) {

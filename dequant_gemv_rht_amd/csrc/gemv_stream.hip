@@ -350,7 +350,8 @@ __host__ __device__ inline StreamLds stream_lds(int mt, int S, int KS, int G, in
 }
 
 template <int BITS, int MT, int D>
-__device__ __forceinline__ void stream_rows(const LinDesc &L, int m_valid, int r0, int rows, uint32_t *smem) {
+__device__ __forceinline__ void stream_rows(const LinDesc &L, const uint32_t *codes0, int m_valid, int r0, int rows,
+                                            uint32_t *smem) {
   constexpr int XC = 2;                     // rotation passes whose loads precede the codes
   constexpr int ZL = 2;                     // 16-byte scale (zero) loads per thread before the codes
   const int t = threadIdx.x, rg = t >> 4, j = t & 15;
@@ -364,7 +365,7 @@ __device__ __forceinline__ void stream_rows(const LinDesc &L, int m_valid, int r
   float *part = reinterpret_cast<float *>(smem + lay.part);
   float *szl = reinterpret_cast<float *>(smem + lay.szl);
 
-  const rsrc_t rc = make_rsrc(L.codes + (size_t)r0 * wpr, (uint32_t)rows * wpr * 4);
+  const rsrc_t rc = make_rsrc(codes0, (uint32_t)rows * wpr * 4);
   const int nszv = rows * G;                 // scale (zero) values of the workgroup's rows
   const rsrc_t rsc = make_rsrc(L.scales + (size_t)r0 * G, (uint32_t)nszv * 2);
   const rsrc_t rz = make_rsrc(L.zeros + (size_t)r0 * G, (uint32_t)nszv * 2);
@@ -819,7 +820,10 @@ __device__ __forceinline__ void consume(u32x4 a, uint32_t b) { asm volatile("" :
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 template <int BITS, bool FULL>
-__device__ __forceinline__ void stream_ring(const LinDesc &L, int r0, int rows, uint32_t *smem) {
+// r0: the workgroup's first row; codes0: that row's code words (the rows
+// that follow are consecutive at BITS * k / 32 words each).
+__device__ __forceinline__ void stream_ring(const LinDesc &L, const uint32_t *codes0, int r0, int rows,
+                                            uint32_t *smem) {
   using RS = Ring<BITS>;
   constexpr int R = RS::depth, Q = RS::q;
   constexpr int XC = 2;
@@ -864,8 +868,8 @@ __device__ __forceinline__ void stream_ring(const LinDesc &L, int r0, int rows, 
   {
     const uint32_t row_bytes = (uint32_t)wpr * 4, pair_bytes = 2 * row_bytes;
     const uint32_t seg_step = 16 * BITS * 4;
-    cur.rc = make_rsrc(L.codes + (size_t)r0 * wpr, (uint32_t)rows * row_bytes);
-    cur.rc1 = make_rsrc(L.codes + (size_t)(r0 + 1) * wpr, (uint32_t)(rows - 1) * row_bytes);
+    cur.rc = make_rsrc(codes0, (uint32_t)rows * row_bytes);
+    cur.rc1 = make_rsrc(codes0 + wpr, (uint32_t)(rows - 1) * row_bytes);
     const uint32_t szb = (uint32_t)rows * G * 2;
     cur.rsc = make_rsrc(L.scales + (size_t)r0 * G, szb);
     cur.rz = make_rsrc(L.zeros + (size_t)r0 * G, szb);
@@ -1316,8 +1320,9 @@ __global__ __launch_bounds__(kStreamThreads) void gemv_ring_kernel(GemvArgs a) {
   const LinDesc L = fetch_desc(a, w);
   const int r0 = (w - L.tile_begin) * L.rows_per_wg;
   if (r0 >= L.n) return;
-  stream_ring<BITS, FULL>(L, r0, min(L.rows_per_wg, L.n - r0), smem);
+  stream_ring<BITS, FULL>(L, L.codes + (size_t)r0 * (L.k / kSlice) * BITS, r0, min(L.rows_per_wg, L.n - r0), smem);
 }
+
 
 // Tasks (two code loads each) a lane keeps in flight.  A 1024-thread
 // workgroup per CU with 4 tasks per lane has 128 KB of int4 codes in flight,
@@ -1336,7 +1341,29 @@ __global__ __launch_bounds__(kStreamThreads) void gemv_stream_kernel(GemvArgs a)
   const int r0 = (w - L.tile_begin) * L.rows_per_wg;
   if (r0 >= L.n) return;
   const int rows = min(L.rows_per_wg, L.n - r0);
-  stream_rows<BITS, MT, Depth<BITS, MT>::d>(L, a.m, r0, rows, smem);
+  stream_rows<BITS, MT, Depth<BITS, MT>::d>(L, L.codes + (size_t)r0 * (L.k / kSlice) * BITS, a.m, r0, rows, smem);
+}
+
+// The mixed 6/8-bit layout at batch 1: workgroup w streams rows of one
+// 64-row block (mixed_wpb workgroups per block), so the code width is
+// uniform across it.  6-bit blocks take the LDS ring; 8-bit blocks the
+// register-prefetch stream (an 8-bit ring for a long K needs more LDS than
+// a compute unit has).
+template <bool FULL>
+__global__ __launch_bounds__(kStreamThreads) void gemv_ring_mixed_kernel(GemvArgs a) {
+  extern __shared__ uint32_t smem[];
+  const int w = blockIdx.x;
+  const LinDesc L = fetch_desc(a, w);
+  const int blk = w / a.mixed_wpb, sub = w - blk * a.mixed_wpb;
+  const int r0 = kMixedRows * blk + sub * L.rows_per_wg;
+  const int rows = min(min(L.rows_per_wg, kMixedRows * (blk + 1) - r0), L.n - r0);
+  if (rows <= 0) return;
+  const int bits = L.block_bits[blk];
+  const uint32_t *codes0 = L.codes + L.block_off[blk] + (size_t)(r0 - kMixedRows * blk) * (L.k / kSlice) * bits;
+  if (bits == 8)
+    stream_rows<8, 1, Depth<8, 1>::d>(L, codes0, 1, r0, rows, smem);
+  else
+    stream_ring<6, FULL>(L, codes0, r0, rows, smem);
 }
 
 // Segments of code loads a lane keeps in flight (4 rows x BITS words each);
@@ -1395,6 +1422,11 @@ int gemv_stream_lds_bytes(int bits, int mt, int64_t k, int rows_per_wg, bool rin
   if (!ring) return stream_lds(mt, (int)S, (int)KS, (int)G, (int)np).total * 4;
   if (mt != 1) return 1 << 30;
   switch (bits) {
+    case 0: {   // mixed 6/8: room for the 6-bit ring and the 8-bit stream
+      const int l6 = ring_lds((int)S, (int)KS, (int)np, Ring<6>::slot, Ring<6>::depth).total;
+      const int l8 = stream_lds(1, (int)S, (int)KS, (int)G, (int)np).total * 4;
+      return l6 > l8 ? l6 : l8;
+    }
     case 3: return ring_lds((int)S, (int)KS, (int)np, Ring<3>::slot, Ring<3>::depth).total;
     case 4: return ring_lds((int)S, (int)KS, (int)np, Ring<4>::slot, Ring<4>::depth).total;
     case 6: return ring_lds((int)S, (int)KS, (int)np, Ring<6>::slot, Ring<6>::depth).total;
@@ -1435,6 +1467,14 @@ hipError_t launch_xprep(int bits, int count, const uint16_t *const *x, const int
 }
 
 hipError_t launch_gemv_stream(int bits, int mt, const GemvArgs &a, hipStream_t s) {
+  if (bits == 0) {
+    if (!a.ring || mt != 1 || a.count != 1 || a.mixed_wpb <= 0) return hipErrorInvalidValue;
+    if (a.lin[0].k % kSeg == 0)
+      hipLaunchKernelGGL((gemv_ring_mixed_kernel<true>), dim3(a.tiles), dim3(kStreamThreads), a.lds_bytes, s, a);
+    else
+      hipLaunchKernelGGL((gemv_ring_mixed_kernel<false>), dim3(a.tiles), dim3(kStreamThreads), a.lds_bytes, s, a);
+    return hipGetLastError();
+  }
   switch (bits) {
     case 3: return launch_bits<3>(mt, a, s);
     case 4: return launch_bits<4>(mt, a, s);

@@ -16,6 +16,7 @@ constexpr int kSeg = 512;          // K per GEMV tile segment: 16 lanes x 32 cod
 constexpr int kSlice = 32;         // codes per lane per row
 constexpr int kThreads = 256;      // GEMV workgroup
 constexpr int kMaxBatch = WQ_MAX_BATCH;
+constexpr int kMixedRows = WQ_MIXED_ROWS;   // rows per block of one width in the mixed layout
 
 // ---------------------------------------------------------------------------
 // GEMV launch description
@@ -49,6 +50,7 @@ struct GemvArgs {
   int32_t tiles;                // total workgroups
   int32_t lds_bytes;            // dynamic LDS per workgroup
   int32_t ring;                 // stream kernel, batch 1: weights staged through an LDS ring
+  int32_t mixed_wpb;            // batch-1 ring over the mixed 6/8-bit layout: workgroups per 64-row block
 };
 
 // Host-side launchers (gemv*.hip).  `bits` 0 = mixed.  mt = 1,2,4,8,16.
