@@ -262,8 +262,10 @@ wq_status launch_tile(int count, const wq_weight *w, const uint16_t *const *x, c
     L.block_bits = w[i].block_bits;
     L.block_off = w[i].block_off;
     L.signs = rotate ? w[i].rht_signs : nullptr;
-    L.xq = xq ? xq[i] : nullptr;
-    L.x = x[i];
+    if (xq && stream && m >= 2)
+      L.xq = xq[i];   // the row-quad kernel reads the arranged activations
+    else
+      L.x = x[i];
     L.y = y[i];
     L.ldx = ldx[i];
     L.ldy = ldy[i];

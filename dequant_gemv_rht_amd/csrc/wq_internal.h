@@ -28,7 +28,10 @@ struct LinDesc {
   const uint8_t *block_bits;    // mixed width only
   const uint64_t *block_off;    // mixed width only
   const uint32_t *signs;        // nullptr: activations used as given
-  const uint16_t *x;
+  union {
+    const uint16_t *x;          // the fp16 activations [m][ldx]
+    const uint32_t *xq;         // batch tiles 2, 4: the tile's arranged activations [mt][k/32][20] (xprep)
+  };
   void *y;
   int64_t ldx, ldy;
   int32_t n, k;
@@ -39,7 +42,6 @@ struct LinDesc {
   int32_t tile_begin;           // first workgroup of this linear in the grid
   int32_t out_f32;
   int32_t ks_inv;               // ceil(2^16 / KS), KS = ceil(k / 512): x / KS = (x * ks_inv) >> 16 for x <= 64
-  const uint32_t *xq;           // batch tiles 2, 4: the tile's arranged activations [mt][k/32][20] (xprep)
 };
 
 struct GemvArgs {
