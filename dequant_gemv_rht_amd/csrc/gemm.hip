@@ -58,6 +58,8 @@ constexpr int kTM = 128, kTN = 256, kBK = 64;
 constexpr int kWaves = 4, kGemmThreads = 64 * kWaves;
 constexpr int kStages = 3;                    // steps in flight + 1: activation stages in LDS, weight register sets
 constexpr int kAhead = kStages - 1;           // steps loaded ahead of the one computed
+constexpr int kMaxSteps = 48;                 // 64-k steps per workgroup at most (longer K is split)
+constexpr int kMaxGroups = kMaxSteps / 2 + 1; // groups of 128 a workgroup's K range touches at most
 
 // LDS slot of 16-byte chunk c of activation row r
 __device__ __forceinline__ int a_slot(int c, int r) { return c ^ (r & 7); }
@@ -184,14 +186,12 @@ __device__ __forceinline__ void wait_vmcnt() {
 // The same wait, also taking a step's weight registers as operands, so that
 // no arithmetic on them is scheduled above it.
 template <int N, int BITS>
-__device__ __forceinline__ void wait_vmcnt_regs(uint32_t (&w)[2][BITS], uint32_t (&sr)[2], uint32_t (&zr)[2]) {
+__device__ __forceinline__ void wait_vmcnt_regs(uint32_t (&w)[2][BITS]) {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int e = 0; e < BITS; ++e) asm volatile("" : "+v"(w[j][e]));
-    asm volatile("" : "+v"(sr[j]), "+v"(zr[j]));
-  }
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void *p) { return (uint32_t)(uintptr_t)(lds_ptr_t)p; }
@@ -214,6 +214,19 @@ __device__ __forceinline__ void read_a(uint32_t addr, half8 (&a)[4]) {
       : "memory");
 }
 
+// The packed scale and zero (s | z << 16) of the lane's two rows for one
+// step, read from LDS and waited for in one statement (kept out of the
+// compiler's view like read_a).
+__device__ __forceinline__ void read_sz(uint32_t a0, uint32_t a1, uint32_t &v0, uint32_t &v1) {
+  asm volatile(
+      "ds_read_b32 %0, %2\n\t"
+      "ds_read_b32 %1, %3\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v0), "=&v"(v1)
+      : "v"(a0), "v"(a1)
+      : "memory");
+}
+
 // Logical tile of workgroup b: runs of consecutive tiles (the m tiles of one
 // n tile and K split, which read the same weights) on one XCD, so they share
 // its L2; workgroups are dealt to the 8 XCDs round robin.
@@ -225,6 +238,8 @@ __device__ __forceinline__ int logical_tile(int b, int nb) {
 template <int BITS>
 __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmBatch a) {
   __shared__ __attribute__((aligned(16))) uint8_t As[kStages * kAStage];
+  // scale and zero of each wave's 64 rows over the workgroup's groups, (s | z << 16)
+  __shared__ uint32_t SZ[kWaves * 64 * kMaxGroups];
   const int tile = logical_tile(blockIdx.x, a.tiles);
   int l = 0;
 #pragma unroll
@@ -265,14 +280,26 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmBatch a) {
   const rsrc_t rz = make_rsrc(L.zeros + (size_t)nw0 * G, (uint32_t)nrows * G * 2);
   const int bn = lane & 31, bh = lane >> 5;
   const uint32_t b_vo0 = (uint32_t)(bn * wpr * 4 + bh * BITS * 4), b_vo1 = b_vo0 + (uint32_t)(32 * wpr * 4);
-  const uint32_t s_vo0 = (uint32_t)(bn * G * 2), s_vo1 = s_vo0 + (uint32_t)(32 * G * 2);
+
+  // scales and zeros of this wave's rows (lane = row) over the split's
+  // groups g0 .. g0 + ng - 1: loaded once here, written to LDS once the
+  // first steps' loads are out; rows past N read zero
+  const int g0 = kt0 >> 1, ng = ((kt0 + T - 1) >> 1) - g0 + 1;
+  uint32_t szs[kMaxGroups], szz[kMaxGroups];
+#pragma unroll
+  for (int g = 0; g < kMaxGroups; ++g) {
+    const uint32_t off = g < ng ? (uint32_t)((lane * G + g0 + g) * 2) : kOOB;
+    szs[g] = __builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0);
+    szz[g] = __builtin_amdgcn_raw_buffer_load_b16(rz, off, 0, 0);
+  }
+  uint32_t *szw = SZ + wave * 64 * kMaxGroups;
+  const uint32_t sz_rd0 = lds_addr(szw) + (uint32_t)(bn * kMaxGroups * 4), sz_rd1 = sz_rd0 + 32 * kMaxGroups * 4;
 
   uint32_t cw[kStages][2][BITS];
-  uint32_t sr[kStages][2], zr[kStages][2];
   auto issue = [&](auto sconst, int kt) {
     constexpr int st = decltype(sconst)::value;
     const int kc = min(kt, kt0 + T - 1);
-    const uint32_t so_a = (uint32_t)kc * (kBK * 2), so_b = (uint32_t)kc * (2 * BITS * 4), so_s = (uint32_t)(kc >> 1) * 2;
+    const uint32_t so_a = (uint32_t)kc * (kBK * 2), so_b = (uint32_t)kc * (2 * BITS * 4);
 #if defined(__HIP_DEVICE_COMPILE__)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -280,14 +307,10 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmBatch a) {
 #endif
     load_slice<BITS>(rc, b_vo0, so_b, cw[st][0]);
     load_slice<BITS>(rc, b_vo1, so_b, cw[st][1]);
-    sr[st][0] = __builtin_amdgcn_raw_buffer_load_b16(rs, s_vo0, so_s, 0);
-    sr[st][1] = __builtin_amdgcn_raw_buffer_load_b16(rs, s_vo1, so_s, 0);
-    zr[st][0] = __builtin_amdgcn_raw_buffer_load_b16(rz, s_vo0, so_s, 0);
-    zr[st][1] = __builtin_amdgcn_raw_buffer_load_b16(rz, s_vo1, so_s, 0);
   };
   // vector-memory operations of one issue, the count waited on
   constexpr int kLoadsB = BITS == 3 || BITS == 4 ? 1 : 2;
-  constexpr int kIssue = 4 + 2 * kLoadsB + 4;
+  constexpr int kIssue = 4 + 2 * kLoadsB;
 
   f32x16 acc[4][2];
 #pragma unroll
@@ -313,15 +336,18 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmBatch a) {
     constexpr int nx = (st + kAhead) % kStages;
     // this step's activations (this wave's rows) and weights: the younger
     // loads are those of the kAhead - 1 steps issued after it
-    wait_vmcnt_regs<(kAhead - 1) * kIssue, BITS>(cw[st], sr[st], zr[st]);
+    wait_vmcnt_regs<(kAhead - 1) * kIssue, BITS>(cw[st]);
     __builtin_amdgcn_s_barrier();   // every wave's rows are in; step kt - 1's stage is free
     issue(std::integral_constant<int, nx>{}, kt + kAhead);
     if (!active) return;
+    uint32_t szv[2];
+    const uint32_t gofs = (uint32_t)(((kt >> 1) - g0) * 4);
+    read_sz(sz_rd0 + gofs, sz_rd1 + gofs, szv[0], szv[1]);
     half8 bop[2][4];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const half2v s = as_h2((sr[st][j] & 0xFFFFu) * 0x10001u);
-      const half2v z = as_h2((zr[st][j] & 0xFFFFu) * 0x10001u);
+      const half2v s = as_h2((szv[j] & 0xFFFFu) * 0x10001u);
+      const half2v z = as_h2((szv[j] >> 16) * 0x10001u);
       const half2v c = {(_Float16)1.0f, kHi};
       const half2v d = {(_Float16)-1024.0f, (_Float16)(BITS == 4 ? -64.0f : -1024.0f)};
       bop[j][0] = b_operand<BITS, 0>(cw[st][j], pk, c, d, z, s);
@@ -353,11 +379,27 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmBatch a) {
     asm volatile("" ::: "memory");
     issue(std::integral_constant<int, 2>{}, kt0 + 2);
   }
+  if constexpr (kAhead > 3) {
+    asm volatile("" ::: "memory");
+    issue(std::integral_constant<int, 3>{}, kt0 + 3);
+  }
+  if constexpr (kAhead > 4) {
+    asm volatile("" ::: "memory");
+    issue(std::integral_constant<int, 4>{}, kt0 + 4);
+  }
+  // the scales and zeros into LDS (each wave reads back only its own rows)
+#pragma unroll
+  for (int g = 0; g < kMaxGroups; ++g)
+    if (g < ng) szw[lane * kMaxGroups + g] = (szs[g] & 0xFFFFu) | (szz[g] << 16);
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  static_assert(kStages >= 3 && kStages <= 6, "the loop below unrolls up to 6 stages");
   for (int i0 = 0; i0 < T; i0 += kStages) {
     step(std::integral_constant<int, 0>{}, kt0 + i0, true);
     step(std::integral_constant<int, 1>{}, kt0 + i0 + 1, i0 + 1 < T);
     step(std::integral_constant<int, 2>{}, kt0 + i0 + 2, i0 + 2 < T);
     if constexpr (kStages > 3) step(std::integral_constant<int, 3>{}, kt0 + i0 + 3, i0 + 3 < T);
+    if constexpr (kStages > 4) step(std::integral_constant<int, 4>{}, kt0 + i0 + 4, i0 + 4 < T);
+    if constexpr (kStages > 5) step(std::integral_constant<int, 5>{}, kt0 + i0 + 5, i0 + 5 < T);
   }
   wait_vmcnt<0>();   // the trailing out-of-range loads still write LDS
 
@@ -385,12 +427,18 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmBatch a) {
     }
 }
 
-// The K splits of a linear, added in split order: y = sum_s part[s].
+// The K splits of a linear, added in split order: y = sum_s part[s].  Four
+// columns per thread when n % 4 == 0, else one.
+__host__ __device__ inline int64_t finalize_items(const GemmLin &L) {
+  const int64_t mn = (int64_t)L.m * L.n;
+  return L.n % 4 ? mn : mn / 4;
+}
+
 __global__ __launch_bounds__(256) void gemm_finalize_kernel(GemmBatch a) {
   int l = -1, base = 0;
   for (int i = 0; i < a.count; ++i) {
     if (a.lin[i].ksplit <= 1) continue;
-    const int nblk = (int)(((int64_t)a.lin[i].m * a.lin[i].n / 4 + 255) / 256);
+    const int nblk = (int)((finalize_items(a.lin[i]) + 255) / 256);
     if ((int)blockIdx.x < base + nblk) {
       l = i;
       break;
@@ -399,9 +447,20 @@ __global__ __launch_bounds__(256) void gemm_finalize_kernel(GemmBatch a) {
   }
   if (l < 0) return;
   const GemmLin &L = a.lin[l];
-  const int64_t e = ((int64_t)(blockIdx.x - base) * 256 + threadIdx.x) * 4;   // n % 4 == 0: 4 columns of one row
   const int64_t mn = (int64_t)L.m * L.n;
-  if (e >= mn) return;
+  const int64_t item = (int64_t)(blockIdx.x - base) * 256 + threadIdx.x;
+  if (item >= finalize_items(L)) return;
+  if (L.n % 4) {
+    float s = L.part[item];
+    for (int q = 1; q < L.ksplit; ++q) s += L.part[(size_t)q * mn + item];
+    const int64_t row = item / L.n, col = item - row * L.n;
+    if (L.out_f32)
+      reinterpret_cast<float *>(L.y)[row * L.ldy + col] = s;
+    else
+      reinterpret_cast<uint16_t *>(L.y)[row * L.ldy + col] = __builtin_bit_cast(uint16_t, (_Float16)s);
+    return;
+  }
+  const int64_t e = item * 4;   // 4 columns of one row
   float4 s = *reinterpret_cast<const float4 *>(&L.part[e]);
   for (int q = 1; q < L.ksplit; ++q) {
     const float4 p = *reinterpret_cast<const float4 *>(&L.part[(size_t)q * mn + e]);
@@ -439,7 +498,9 @@ void gemm_plan(int count, const wq_weight *w, int64_t m, int *ksplit) {
     const int64_t kt = w[i].k / kBK;
     int64_t s = (kt + target - 1) / target;
     s = std::max<int64_t>(1, std::min<int64_t>(s, kt / 8));
-    ksplit[i] = w[i].n % 4 ? 1 : (int)s;
+    // a workgroup's scales and zeros sit in LDS: at most kMaxSteps steps each
+    s = std::max<int64_t>(s, (kt + kMaxSteps - 1) / kMaxSteps);
+    ksplit[i] = (int)s;
   }
 }
 
@@ -458,7 +519,6 @@ hipError_t launch_gemm_batch(int count, const wq_weight *w, const uint16_t *cons
   int64_t tiles = 0, fin_blocks = 0;
   for (int i = 0; i < count; ++i) {
     if (!gemm_available(w[i].bits) || w[i].bits != w[0].bits || w[i].k % kBK) return hipErrorInvalidValue;
-    if (ksplit[i] > 1 && w[i].n % 4) return hipErrorInvalidValue;   // the partial sums run 4 columns at a time
     if ((uint64_t)m * (uint64_t)ldx[i] * 2 > 0x7FFFFFFFull || (uint64_t)w[i].n * (uint64_t)w[i].k > 0x7FFFFFFFull)
       return hipErrorInvalidValue;   // 32-bit buffer offsets
     GemmLin &L = a.lin[i];
@@ -481,10 +541,11 @@ hipError_t launch_gemm_batch(int count, const wq_weight *w, const uint16_t *cons
     L.ksplit = ksplit[i];
     L.ksteps = (kt + ksplit[i] - 1) / ksplit[i];
     L.ksplit = (kt + L.ksteps - 1) / L.ksteps;   // no empty split
+    if (L.ksteps > kMaxSteps) return hipErrorInvalidValue;
     L.tile_begin = (int32_t)tiles;
     a.first_tile[i] = (int32_t)tiles;
     tiles += (int64_t)L.mtiles * L.ntiles * L.ksplit;
-    if (L.ksplit > 1) fin_blocks += ((int64_t)m * w[i].n / 4 + 255) / 256;
+    if (L.ksplit > 1) fin_blocks += (finalize_items(L) + 255) / 256;
   }
   if (tiles > INT32_MAX) return hipErrorInvalidValue;
   a.tiles = (int32_t)tiles;
