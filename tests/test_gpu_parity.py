@@ -167,6 +167,15 @@ def test_gemm_bits_and_ragged_shapes(bits, m, n, k):
     _run_case(n, k, m, bits, True, False, 7000 + 100 * bits + m)
 
 
+@pytest.mark.parametrize("out_f32", [False, True])
+def test_gemm_split_k_any_n(out_f32):
+    # K = 9728 (152 steps of 64) is split over workgroups whose fp32 partial
+    # tiles a second pass adds in split order; N = 130 is not a multiple of
+    # 4, so that pass adds them one column at a time
+    say(f"gemm split-K n=130 k=9728 f32={out_f32}")
+    _run_case(130, 9728, 64, 4, True, out_f32, 31 + out_f32)
+
+
 @pytest.mark.parametrize("rht,out_f32", [(False, False), (True, True), (False, True)])
 def test_gemm_rotation_and_output(rht, out_f32):
     say(f"gemm rht={rht} f32={out_f32}")
