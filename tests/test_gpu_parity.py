@@ -157,6 +157,23 @@ def test_linear_shapes(n, k, rht, out_f32, m):
     _run_case(n, k, m, 4, rht, out_f32, n + k + m)
 
 
+@pytest.mark.parametrize("m", [2, 4, 7])
+def test_batch_tiles_long_k_fall_back(m):
+    # K = 16384 arranged activations of a 4-row tile need 160 KB of LDS, more
+    # than a CU has: the call falls back to the tiled kernel, which rotates
+    # for itself; the result must be the same layer
+    say(f"linear long K m={m}")
+    _run_case(96, 16384, m, 4, True, False, 50 + m)
+
+
+@pytest.mark.parametrize("n", [1, 5, 129])
+def test_batch_tiles_few_rows(n):
+    # fewer row quads than DPP rows: several DPP rows share a quad, one part
+    # of K each, and their parts are added in order
+    say(f"linear few rows n={n} m=4")
+    _run_case(n, 2560, 4, 4, True, False, 60 + n)
+
+
 # ---------------------------------------------------------- matrix-core path
 
 @pytest.mark.parametrize("bits", [3, 4, 6, 8])
