@@ -1,44 +1,46 @@
-// Persistent fused rotation + dequantising GEMV for batch tiles up to 4
-// (gfx950).  Same arithmetic as the tiled kernel (gemv.hip): codes become
-// fp16 (1024 + q) in registers, v_dot2_f32_f16 accumulates against the
-// rotated fp16 activations, the scale multiplies each 32-code partial once
-// and the zero point (plus the 1024 offset) is removed with the partial's
-// activation sum.  Source of the arithmetic: model card "24B0978 - Week 01 -
-// Track 2, 20% target", section "How these techniques accelerate inference
-// on CUDA" (group-wise affine codes dequantised inside the product, scale
-// applied once per group; activations rotated by a fast Walsh-Hadamard
-// transform at run time).
+// Persistent fused rotation + dequantising GEMV for batch sizes up to 16
+// (gfx950).  Codes become fp16 (1024 + 2^s q) in registers, v_dot2_f32_f16
+// accumulates against the rotated fp16 activations, the scale multiplies
+// each 32-code partial once and the zero point (plus the 1024 offset) is
+// removed with the partial's activation sums.  Source of the arithmetic:
+// model card "24B0978 - Week 01 - Track 2, 20% target", section "How these
+// techniques accelerate inference on CUDA" (group-wise affine codes
+// dequantised inside the product, scale applied once per group; activations
+// rotated by a fast Walsh-Hadamard transform at run time).
 //
-// Work decomposition.  One 1024-thread workgroup per compute unit.  Each
-// linear of a launch gets a number of workgroups proportional to its bytes,
-// and each workgroup a contiguous range of rows.  A workgroup
-//   1. rotates its linear's activations for the whole K once into LDS (the
-//      rotation is paid once per workgroup, not once per tile);
-//   2. numbers its (row pair, 512-wide K segment) tasks row-pair-major and
-//      deals them out round-robin to its 64 16-lane DPP rows: at step i, DPP
-//      row g takes task 64 i + g, so each step the workgroup reads one
-//      contiguous run of its row block (two adjacent rows are adjacent in
-//      memory), which keeps DRAM pages open instead of scattering 128
-//      concurrent row streams per workgroup;
-//   3. keeps D steps of code loads in flight (raw buffer loads: out-of-range
-//      lanes read zero without memory traffic, so every load is issued on a
-//      straight-line path);
-//   4. sums each task's two row partials over the 16 lanes by DPP and leaves
-//      them in LDS at [row][segment];
-//   5. adds each row's partials in segment order (deterministic) and stores.
+// Kernels in this file (one persistent workgroup per compute unit; the
+// linears of a launch share the CUs in proportion to their estimated time,
+// and each workgroup owns a contiguous range of whole output rows, so no
+// output is shared between workgroups):
+//   * gemv_ring_kernel: batch 1.  Rotates its linear's activations once into
+//     LDS, streams the weights through an LDS ring by direct buffer-to-LDS
+//     loads (section "Batch 1" below).
+//   * gemv_ring_mixed_kernel: batch 1 over the mixed 6/8-bit layout, one
+//     64-row block of uniform width per workgroup.
+//   * gemv_stream_kernel: batch 1 when the ring does not fit in LDS: codes
+//     prefetched into registers.
+//   * xprep_kernel + gemv_quad_kernel: batch tiles of 2..4 rows (batches up
+//     to 16 as tiles of 4): activations rotated and arranged once, then row
+//     quads with register accumulation (section "Batch tiles 2 and 4").
 //
-// Unpacking.  A code pair becomes two fp16 values (1024 + q) with one
-// v_and_or_b32 against 1024.0's bit pattern.  For int4, nibbles in bits 4..7
-// of a 16-bit half are used in place: they read as (1024 + 16 q), so their
-// activations are stored pre-divided by 16 (exact in fp16), which saves two
-// of the three shifts per word.  int8 uses one v_perm_b32 per pair.  The
-// offsets are removed with two per-slice activation sums: X (the sum of the
-// effective activations, for the zero point) and XS (1024 times the sum of
-// the stored values, the 1024 offsets).
+// Tasks.  A lane's unit of work is a 32-code slice of one or more rows in a
+// 512-wide K segment (16 lanes of a DPP row cover the segment).  Every load
+// is a raw buffer load: out-of-range lanes read zero without memory
+// traffic, so loads are issued on straight-line paths.  Row partials are
+// summed over the 16 lanes by DPP and added in a fixed order at the end
+// (deterministic).
 //
-// LDS layout.  Each 32-code activation slice occupies 80 bytes (64 used):
-// with that stride the 16 lanes of a DPP row reading their slices with
-// ds_read_b128 hit 16 distinct 4-bank groups.
+// Unpacking.  A code pair becomes two fp16 values with one v_and_or_b32
+// against 1024.0's bit pattern; codes that sit at bit s of a 16-bit half are
+// used in place, reading as 1024 + 2^s q, and the activations they meet are
+// stored pre-multiplied by 2^-s (exact in fp16).  int8 uses one v_perm_b32
+// per pair.  The offsets are removed with two per-slice activation sums: X
+// (the sum of the values meant, for the zero point) and XS (1024 times the
+// sum of the values stored, for the 1024 offsets).
+//
+// LDS layout.  Each 32-code activation slice occupies 80 bytes (64 of pairs,
+// the two sums, 8 spare): with that stride the 16 lanes of a DPP row
+// reading their slices with ds_read_b128 hit 16 distinct 4-bank groups.
 #include "wq_internal.h"
 
 #include <climits>
