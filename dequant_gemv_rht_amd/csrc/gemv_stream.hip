@@ -1090,12 +1090,14 @@ __host__ __device__ inline QuadLds quad_lds(int mt, int S, int KS, int G, int nq
   return l;
 }
 
-// Unit u (= quad q, part sub of p): its segments [s, e).
-__device__ __forceinline__ void unit_range(int u, int p, int KS, int &q, int &s, int &e) {
-  q = u / p;
+// Unit u (= quad q, part sub of p): its segments [s, e).  Quotients by p
+// as (x * ceil(2^16 / p)) >> 16, exact for x < 2^16 / p (here x <= 32 KS
+// or x = u with p = 1).
+__device__ __forceinline__ void unit_range(int u, int p, uint32_t p_inv, int KS, int &q, int &s, int &e) {
+  q = (int)(__umul24((uint32_t)u, p_inv) >> 16);
   const int sub = u - q * p;
-  s = KS * sub / p;
-  e = KS * (sub + 1) / p;
+  s = (int)(__umul24((uint32_t)(KS * sub), p_inv) >> 16);
+  e = (int)(__umul24((uint32_t)(KS * (sub + 1)), p_inv) >> 16);
 }
 
 template <int BITS, int MT, int D>
@@ -1108,6 +1110,7 @@ __device__ __forceinline__ void stream_quads(const LinDesc &L, int m_valid, int 
   const int wpr = S * BITS;
   const int NQ = (rows + 3) >> 2;
   const int p = quad_split(NQ, KS), NU = NQ * p;
+  const uint32_t p_inv = (65536u + (uint32_t)p - 1u) / (uint32_t)p;
   const bool full = (K % kSeg) == 0;
   const QuadLds lay = quad_lds(MT, S, KS, G, NQ);
   uint32_t *xp = smem;
@@ -1147,7 +1150,7 @@ __device__ __forceinline__ void stream_quads(const LinDesc &L, int m_valid, int 
   const uint32_t quad_bytes = 4 * row_bytes;
   const uint32_t lane_off = (uint32_t)j * (BITS * 4);
   int lu = rg, lq, ls, le;                  // load side: unit, quad, segment, end
-  unit_range(lu, p, KS, lq, ls, le);
+  unit_range(lu, p, p_inv, KS, lq, ls, le);
   uint32_t cw[D][4][BITS];
 #pragma unroll
   for (int d = 0; d < D; ++d) {
@@ -1155,7 +1158,7 @@ __device__ __forceinline__ void stream_quads(const LinDesc &L, int m_valid, int 
     const uint32_t co = __umul24((uint32_t)lq, quad_bytes) + (uint32_t)ls * seg_step + lane_off;
 #pragma unroll
     for (int r = 0; r < 4; ++r) load_slice<BITS>(rc, ok ? co + r * row_bytes : kOOB, cw[d][r]);
-    if (++ls == le) { lu += kQRG; unit_range(lu, p, KS, lq, ls, le); }
+    if (++ls == le) { lu += kQRG; unit_range(lu, p, p_inv, KS, lq, ls, le); }
   }
 
   // 3. scales, zeros and activations into LDS
@@ -1196,7 +1199,7 @@ __device__ __forceinline__ void stream_quads(const LinDesc &L, int m_valid, int 
   //    the unit's segments
   const UnpackConsts uc = unpack_consts<BITS>();
   int cu = rg, cq, cs, ce;                  // compute side
-  unit_range(cu, p, KS, cq, cs, ce);
+  unit_range(cu, p, p_inv, KS, cq, cs, ce);
   const int steps = ((NU + kQRG - 1) / kQRG) * ((KS + p - 1) / p);
   float acc[16];
 #pragma unroll
@@ -1216,25 +1219,29 @@ __device__ __forceinline__ void stream_quads(const LinDesc &L, int m_valid, int 
           sf[r] = sv ? sz.x : 0.f;
           zf[r] = sz.y;
         }
+        uint32_t xv[MT][16];
+        float2 xq[MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          const uint32_t *src = &xp[(m * S + sl) * kSliceStride];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const u32x4 v = reinterpret_cast<const u32x4 *>(src)[q];
+            xv[m][4 * q + 0] = v.x; xv[m][4 * q + 1] = v.y; xv[m][4 * q + 2] = v.z; xv[m][4 * q + 3] = v.w;
+          }
+          xq[m] = *reinterpret_cast<const float2 *>(src + 16);
+        }
         uint32_t pr[4][16];
 #pragma unroll
         for (int r = 0; r < 4; ++r) unpack_pairs<BITS>(cw[d][r], uc, pr[r]);
         // s * (sum (1024+q') x' - 1024 XS - z X) = s * sum (q - z) x
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-          const uint32_t *src = &xp[(m * S + sl) * kSliceStride];
-          uint32_t xv[16];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const u32x4 v = reinterpret_cast<const u32x4 *>(src)[q];
-            xv[4 * q + 0] = v.x; xv[4 * q + 1] = v.y; xv[4 * q + 2] = v.z; xv[4 * q + 3] = v.w;
-          }
-          const float2 xq = *reinterpret_cast<const float2 *>(src + 16);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            float dd = fmaf(-zf[r], xq.x, -xq.y);
+            float dd = fmaf(-zf[r], xq[m].x, -xq[m].y);
 #pragma unroll
-            for (int q = 0; q < 16; ++q) dd = dot2(pr[r][q], xv[q], dd);
+            for (int q = 0; q < 16; ++q) dd = dot2(pr[r][q], xv[m][q], dd);
             acc[r * MT + m] = fmaf(sf[r], dd, acc[r * MT + m]);
           }
         }
@@ -1248,7 +1255,7 @@ __device__ __forceinline__ void stream_quads(const LinDesc &L, int m_valid, int 
 #pragma unroll
           for (int v2 = 0; v2 < 16; ++v2) acc[v2] = 0.f;
           cu += kQRG;
-          unit_range(cu, p, KS, cq, cs, ce);
+          unit_range(cu, p, p_inv, KS, cq, cs, ce);
         } else {
           ++cs;
         }
@@ -1258,7 +1265,7 @@ __device__ __forceinline__ void stream_quads(const LinDesc &L, int m_valid, int 
       const uint32_t co = __umul24((uint32_t)lq, quad_bytes) + (uint32_t)ls * seg_step + lane_off;
 #pragma unroll
       for (int r = 0; r < 4; ++r) load_slice<BITS>(rc, ok ? co + r * row_bytes : kOOB, cw[d][r]);
-      if (++ls == le) { lu += kQRG; unit_range(lu, p, KS, lq, ls, le); }
+      if (++ls == le) { lu += kQRG; unit_range(lu, p, p_inv, KS, lq, ls, le); }
     }
   }
   __syncthreads();
