@@ -1,4 +1,7 @@
-// Fused rotation + dequantising GEMV for batch sizes up to 16 (gfx950).
+// Tiled fused rotation + dequantising GEMV (gfx950): the mixed 6/8-bit
+// layout above batch 1 (tiles of up to 16 batch rows), and any uniform
+// width whose tile of up to 4 batch rows does not fit the stream kernels'
+// LDS.
 //
 // What it computes (model card "24B0978 - Week 01 - Track 2, 20% target",
 // section "How these techniques accelerate inference on CUDA"): for every
@@ -459,8 +462,12 @@ hipError_t launch_bits(int mt, const GemvArgs &a, hipStream_t s) {
     case 1: return launch_t<BITS, 1>(a, s);
     case 2: return launch_t<BITS, 2>(a, s);
     case 4: return launch_t<BITS, 4>(a, s);
-    case 8: return launch_t<BITS, 8>(a, s);
-    case 16: return launch_t<BITS, 16>(a, s);
+  }
+  if constexpr (BITS == 0) {   // uniform widths reach this kernel in tiles of at most 4 rows
+    switch (mt) {
+      case 8: return launch_t<0, 8>(a, s);
+      case 16: return launch_t<0, 16>(a, s);
+    }
   }
   return hipErrorInvalidValue;
 }
