@@ -116,17 +116,17 @@ constexpr int kMaxLds = 160 * 1024;
 bool plan_stream(int count, const wq_weight *w, int64_t m, bool rotate, int *wg, int *rows_per_wg, int *lds,
                  bool *ring) {
   const int mt = mtile(m);
-  if (w[0].bits == 0 || mt > 4) return false;
+  if (w[0].bits == 0 || mt > 8) return false;
   const int ncu = device_cus();
   if (count > ncu) return false;
   const double round_bytes = rotate ? 8192.0 : 3072.0;
-  const int gran = mt >= 2 ? 4 : 2;   // rows per task: quads at batch tiles 2 and 4, pairs at 1
+  const int gran = mt >= 2 ? 4 : 2;   // rows per task: quads at batch tiles 2 to 8, pairs at 1
   double bytes[WQ_MAX_BATCH], prep[WQ_MAX_BATCH];
   int64_t maxwg[WQ_MAX_BATCH];
   for (int i = 0; i < count; ++i) {
     bytes[i] = (double)w[i].n * (double)w[i].k * (w[i].bits / 8.0 + 4.0 / 128.0);
     const int64_t items = mt * (w[i].k / wq::kGroup);
-    // batch 1 rotates in the workgroup; batch tiles 2 and 4 copy the
+    // batch 1 rotates in the workgroup; batch tiles 2 to 8 copy the
     // arranged activations (80 bytes per 32 elements) from L2
     prep[i] = mt == 1 ? round_bytes * (double)((items + 15) / 16) : 0.625 * (double)(mt * w[i].k);
     maxwg[i] = (w[i].n + gran - 1) / gran;
@@ -174,15 +174,37 @@ wq_status launch_tile(int count, const wq_weight *w, const uint16_t *const *x, c
                       void *const *y, const wq_dtype *ydt, const int64_t *ldy, bool rotate,
                       const uint32_t *const *xq, hipStream_t s);
 
+// The linears in launch order: longest rows first, so that the longest
+// workgroups start first.
+void order_by_k(int count, const wq_weight *w, int *order, wq_weight *ws) {
+  for (int i = 0; i < count; ++i) order[i] = i;
+  for (int i = 1; i < count; ++i)
+    for (int j = i; j > 0 && w[order[j]].k > w[order[j - 1]].k; --j) {
+      int t = order[j];
+      order[j] = order[j - 1];
+      order[j - 1] = t;
+    }
+  for (int o = 0; o < count; ++o) ws[o] = w[order[o]];
+}
+
 // One GEMV over `count` linears with batch rows m (<= 16).  Above one row
 // (uniform width) the activations are arranged once into the workspace, then
-// each tile of up to 4 batch rows is one pass of the row-quad kernel over
-// the weights (a larger tile would run out of registers for the unpacked
-// codes and the partials of four rows).
+// each tile of batch rows is one pass of the row-quad kernel over the
+// weights: 8 rows where the 8 rows' arranged activations (80 bytes per 32
+// elements and row), the row parts and the scales fit in one workgroup's LDS
+// for every linear of the call, else 4.
 wq_status run_gemv(int count, const wq_weight *w, const uint16_t *const *x, const int64_t *ldx,
                    int64_t m, void *const *y, const wq_dtype *ydt, const int64_t *ldy,
                    bool rotate, void *workspace, hipStream_t s) {
   if (!uses_xprep(w[0], m)) return launch_tile(count, w, x, ldx, m, y, ydt, ldy, rotate, nullptr, s);
+  int64_t tile = 4;
+  if (m > 4) {
+    int order[WQ_MAX_BATCH], wg[WQ_MAX_BATCH], rpw[WQ_MAX_BATCH], lds = 0;
+    wq_weight ws[WQ_MAX_BATCH];
+    bool ring = false;
+    order_by_k(count, w, order, ws);
+    if (plan_stream(count, ws, 8, rotate, wg, rpw, &lds, &ring)) tile = 8;
+  }
   uint32_t *xq[WQ_MAX_BATCH];
   const uint32_t *sg[WQ_MAX_BATCH];
   int64_t kk[WQ_MAX_BATCH];
@@ -198,19 +220,19 @@ wq_status run_gemv(int count, const wq_weight *w, const uint16_t *const *x, cons
   const uint32_t *xt[WQ_MAX_BATCH];
   const uint16_t *xc[WQ_MAX_BATCH];
   void *yc[WQ_MAX_BATCH];
-  for (int64_t m0 = 0; m0 < m; m0 += 4) {
+  for (int64_t m0 = 0; m0 < m; m0 += tile) {
     for (int i = 0; i < count; ++i) {
       xt[i] = xq[i] + (size_t)m0 * (size_t)(w[i].k / wq::kSlice) * 20;
       xc[i] = x[i] + m0 * ldx[i];
       yc[i] = static_cast<char *>(y[i]) + (size_t)m0 * (size_t)ldy[i] * (ydt[i] == WQ_F32 ? 4 : 2);
     }
-    st = launch_tile(count, w, xc, ldx, m - m0 < 4 ? m - m0 : 4, yc, ydt, ldy, rotate, xt, s);
+    st = launch_tile(count, w, xc, ldx, m - m0 < tile ? m - m0 : tile, yc, ydt, ldy, rotate, xt, s);
     if (st != WQ_OK) return st;
   }
   return WQ_OK;
 }
 
-// One launch over `count` linears for a batch tile of m <= 4 rows (any m
+// One launch over `count` linears for a batch tile of m <= 8 rows (any m
 // for the tiled kernel).  xq: the tile's arranged activations per linear, or
 // NULL where the kernel rotates for itself.
 wq_status launch_tile(int count, const wq_weight *w, const uint16_t *const *x, const int64_t *ldx, int64_t m,
@@ -221,17 +243,9 @@ wq_status launch_tile(int count, const wq_weight *w, const uint16_t *const *x, c
   for (int i = 0; i < wq::kMaxBatch; ++i) a.first_tile[i] = INT32_MAX;
   a.count = count;
   a.m = (int32_t)m;
-  // longest rows first, so the longest workgroups start first
   int order[WQ_MAX_BATCH];
-  for (int i = 0; i < count; ++i) order[i] = i;
-  for (int i = 1; i < count; ++i)
-    for (int j = i; j > 0 && w[order[j]].k > w[order[j - 1]].k; --j) {
-      int t = order[j];
-      order[j] = order[j - 1];
-      order[j - 1] = t;
-    }
   wq_weight ws[WQ_MAX_BATCH];
-  for (int o = 0; o < count; ++o) ws[o] = w[order[o]];
+  order_by_k(count, w, order, ws);
   int wg[WQ_MAX_BATCH], rpw[WQ_MAX_BATCH], slds = 0;
   bool ring = false;
   bool stream = plan_stream(count, ws, m, rotate, wg, rpw, &slds, &ring);

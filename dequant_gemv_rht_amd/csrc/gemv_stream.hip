@@ -19,9 +19,10 @@
 //     64-row block of uniform width per workgroup.
 //   * gemv_stream_kernel: batch 1 when the ring does not fit in LDS: codes
 //     prefetched into registers.
-//   * xprep_kernel + gemv_quad_kernel: batch tiles of 2..4 rows (batches up
-//     to 16 as tiles of 4): activations rotated and arranged once, then row
-//     quads with register accumulation (section "Batch tiles 2 and 4").
+//   * xprep_kernel + gemv_quad_kernel: batch tiles of 2, 4 or 8 rows
+//     (batches up to 16 as tiles of 8, or of 4 where 8 rows of activations
+//     do not fit in LDS): activations rotated and arranged once, then row
+//     quads with register accumulation (section "Batch tiles").
 //
 // Tasks.  A lane's unit of work is a 32-code slice of one or more rows in a
 // 512-wide K segment (16 lanes of a DPP row cover the segment).  Every load
@@ -1009,7 +1010,7 @@ __device__ __forceinline__ void stream_ring(const LinDesc &L, const uint32_t *co
 }
 
 // ---------------------------------------------------------------------------
-// Batch tiles 2 and 4: row quads, activations arranged once.
+// Batch tiles (2, 4 or 8 rows): row quads, activations arranged once.
 //
 // With more than one batch row, rotating the activations in every
 // workgroup would cost more than the workgroup's share of the product (each
@@ -1032,10 +1033,13 @@ __device__ __forceinline__ void stream_ring(const LinDesc &L, const uint32_t *co
 //     the slice's sum into the accumulator;
 //   * at the unit's end the partials are summed over the 16 lanes by a
 //     reduce-scatter (each step halves the values a lane holds and pairs it
-//     with a lane of the other half), leaving one value per lane, which goes
-//     to LDS; the p parts of each row are added in order at the end.
+//     with a lane of the other half), leaving 4 MT / 16 values per lane
+//     (one lane pair per value at MT 2), which go to LDS; the p parts of
+//     each row are added in order at the end.
 // 512-thread workgroups (two waves per SIMD) give each lane the registers
-// for the four rows' unpacked codes.
+// for the four rows' unpacked codes and the 4 x MT partials.  At MT 8 a
+// lane reads one batch row's slice at a time (at 2 and 4 all of them ahead
+// of the unpack).
 // ---------------------------------------------------------------------------
 
 constexpr int kQuadThreads = 512;
@@ -1044,8 +1048,8 @@ constexpr int kQRG = kQuadThreads / 16;   // DPP rows per workgroup
 // One reduce-scatter step over V values: lanes whose `hi` bit is clear keep
 // the lower half and receive their partner's lower half; the others the
 // upper half.  CTRL pairs each lane with one in the other half.
-template <int CTRL, int V>
-__device__ __forceinline__ void rs_step(float (&v)[16], bool hi) {
+template <int CTRL, int V, int N>
+__device__ __forceinline__ void rs_step(float (&v)[N], bool hi) {
 #pragma unroll
   for (int e = 0; e < V / 2; ++e) {
     const float keep = hi ? v[e + V / 2] : v[e];
@@ -1054,20 +1058,21 @@ __device__ __forceinline__ void rs_step(float (&v)[16], bool hi) {
   }
 }
 
-// Sum V (8 or 16) values over the 16 lanes of a DPP row.  Lane j returns
-// the sum of value j (V = 16) or j >> 1 (V = 8, lanes j and j ^ 1 alike).
-template <int V>
-__device__ __forceinline__ float reduce_scatter16(float (&v)[16], int j) {
-  static_assert(V == 8 || V == 16, "4 rows x 2 or 4 batch rows");
+// Sum V (8, 16 or 32) values over the 16 lanes of a DPP row.  Lane j ends
+// with the sums of values (V / 16) j .. (V / 16) (j + 1) - 1 in v[0 ..]
+// (V = 32: two values; V = 16: one; V = 8: value j >> 1, lanes j and j ^ 1
+// alike).
+template <int V, int N>
+__device__ __forceinline__ void reduce_scatter16(float (&v)[N], int j) {
+  static_assert(V == 8 || V == 16 || V == 32, "4 rows x 2, 4 or 8 batch rows");
   rs_step<kRowRor8, V>(v, j & 8);
   rs_step<kRowHalfMirror, V / 2>(v, j & 4);
   rs_step<kQuadXor2, V / 4>(v, j & 2);
-  if constexpr (V == 16) {
-    rs_step<kQuadXor1, 2>(v, j & 1);
+  if constexpr (V >= 16) {
+    rs_step<kQuadXor1, V / 8>(v, j & 1);
   } else {
     v[0] += dpp<kQuadXor1>(v[0]);
   }
-  return v[0];
 }
 
 // DPP rows per quad: with fewer quads than DPP rows they share them, one
@@ -1102,9 +1107,9 @@ __device__ __forceinline__ void unit_range(int u, int p, uint32_t p_inv, int KS,
 
 template <int BITS, int MT, int D>
 __device__ __forceinline__ void stream_quads(const LinDesc &L, int m_valid, int r0, int rows, uint32_t *smem) {
-  static_assert(MT == 2 || MT == 4, "batch tile");
+  static_assert(MT == 2 || MT == 4 || MT == 8, "batch tile");
   constexpr int ZL = 2;
-  constexpr int XCH = 3 * MT;               // 8 KB copy passes held in registers (K <= 9830 at MT 4)
+  constexpr int XCH = MT <= 4 ? 3 * MT : 16;   // 8 KB copy passes held in registers (K <= 9830 at MT 4)
   const int t = threadIdx.x, rg = t >> 4, j = t & 15;
   const int K = L.k, KS = (K + kSeg - 1) / kSeg, G = K / kGroup, S = K / kSlice;
   const int wpr = S * BITS;
@@ -1201,9 +1206,10 @@ __device__ __forceinline__ void stream_quads(const LinDesc &L, int m_valid, int 
   int cu = rg, cq, cs, ce;                  // compute side
   unit_range(cu, p, p_inv, KS, cq, cs, ce);
   const int steps = ((NU + kQRG - 1) / kQRG) * ((KS + p - 1) / p);
-  float acc[16];
+  constexpr int NV = 4 * MT;   // partials of a unit: value r * MT + m
+  float acc[NV];
 #pragma unroll
-  for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+  for (int v = 0; v < NV; ++v) acc[v] = 0.f;
   for (int i0 = 0; i0 < steps; i0 += D) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
@@ -1219,17 +1225,23 @@ __device__ __forceinline__ void stream_quads(const LinDesc &L, int m_valid, int 
           sf[r] = sv ? sz.x : 0.f;
           zf[r] = sz.y;
         }
-        uint32_t xv[MT][16];
-        float2 xq[MT];
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
+        // the batch rows' activation slices (all of them up to 4 rows, read
+        // before the unpack so their latency overlaps it; one at a time at 8)
+        constexpr int XR = MT <= 4 ? MT : 1;
+        uint32_t xv[XR][16];
+        float2 xq[XR];
+        auto read_x = [&](int m, int slot) {
           const uint32_t *src = &xp[(m * S + sl) * kSliceStride];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const u32x4 v = reinterpret_cast<const u32x4 *>(src)[q];
-            xv[m][4 * q + 0] = v.x; xv[m][4 * q + 1] = v.y; xv[m][4 * q + 2] = v.z; xv[m][4 * q + 3] = v.w;
+            xv[slot][4 * q + 0] = v.x; xv[slot][4 * q + 1] = v.y; xv[slot][4 * q + 2] = v.z; xv[slot][4 * q + 3] = v.w;
           }
-          xq[m] = *reinterpret_cast<const float2 *>(src + 16);
+          xq[slot] = *reinterpret_cast<const float2 *>(src + 16);
+        };
+        if constexpr (MT <= 4) {
+#pragma unroll
+          for (int m = 0; m < MT; ++m) read_x(m, m);
         }
         uint32_t pr[4][16];
 #pragma unroll
@@ -1237,23 +1249,32 @@ __device__ __forceinline__ void stream_quads(const LinDesc &L, int m_valid, int 
         // s * (sum (1024+q') x' - 1024 XS - z X) = s * sum (q - z) x
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
+          const int xs = MT <= 4 ? m : 0;
+          if constexpr (MT > 4) read_x(m, 0);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            float dd = fmaf(-zf[r], xq[m].x, -xq[m].y);
+            float dd = fmaf(-zf[r], xq[xs].x, -xq[xs].y);
 #pragma unroll
-            for (int q = 0; q < 16; ++q) dd = dot2(pr[r][q], xv[m][q], dd);
+            for (int q = 0; q < 16; ++q) dd = dot2(pr[r][q], xv[xs][q], dd);
             acc[r * MT + m] = fmaf(sf[r], dd, acc[r * MT + m]);
           }
         }
         if (cs + 1 == ce) {
-          // the unit is done: its row parts over the 16 lanes, one per lane
-          const float v = reduce_scatter16<4 * MT>(acc, j);
-          const int vi = (4 * MT == 16) ? j : (j >> 1);
+          // the unit is done: its row parts over the 16 lanes, NV / 16 per lane
+          reduce_scatter16<NV>(acc, j);
           const int sub = cu - cq * p;
-          if (4 * MT == 16 || (j & 1) == 0)
-            part[((4 * cq + vi / MT) * p + sub) * MT + vi % MT] = v;
+          if constexpr (NV == 8) {
+            const int vi = j >> 1;
+            if ((j & 1) == 0) part[((4 * cq + vi / MT) * p + sub) * MT + vi % MT] = acc[0];
+          } else {
 #pragma unroll
-          for (int v2 = 0; v2 < 16; ++v2) acc[v2] = 0.f;
+            for (int e = 0; e < NV / 16; ++e) {
+              const int vi = (NV / 16) * j + e;
+              part[((4 * cq + vi / MT) * p + sub) * MT + vi % MT] = acc[e];
+            }
+          }
+#pragma unroll
+          for (int v2 = 0; v2 < NV; ++v2) acc[v2] = 0.f;
           cu += kQRG;
           unit_range(cu, p, p_inv, KS, cq, cs, ce);
         } else {
@@ -1414,6 +1435,9 @@ hipError_t launch_bits(int mt, const GemvArgs &a, hipStream_t s) {
       break;
     case 4:
       hipLaunchKernelGGL((gemv_quad_kernel<BITS, 4>), dim3(a.tiles), dim3(kQuadThreads), a.lds_bytes, s, a);
+      break;
+    case 8:
+      hipLaunchKernelGGL((gemv_quad_kernel<BITS, 8>), dim3(a.tiles), dim3(kQuadThreads), a.lds_bytes, s, a);
       break;
     default:
       return hipErrorInvalidValue;

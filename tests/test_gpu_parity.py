@@ -174,6 +174,25 @@ def test_batch_tiles_few_rows(n):
     _run_case(n, 2560, 4, 4, True, False, 60 + n)
 
 
+@pytest.mark.parametrize("m", [6, 16])
+@pytest.mark.parametrize("long_k", [False, True])
+def test_batch_tiles_of_eight_and_four(m, long_k):
+    # a call whose linears all fit 8 rows of arranged activations in LDS runs
+    # in tiles of 8 batch rows; with K = 9728 (8 rows take 190 KB) the whole
+    # call runs in tiles of 4; either way every output is its layer
+    shapes = [(256, 2560), (130, 4096)] + ([(64, 9728)] if long_k else [])
+    say(f"linear batch tiles m={m} long_k={long_k}")
+    qs, xs, refs = [], [], []
+    for i, (n, k) in enumerate(shapes):
+        w, x, signs = _inputs(n, k, m, 70 + 3 * i + m)
+        q, s, z = OR.prepare(w, signs, 3)
+        refs.append(OL.linear(q, s, z, x, signs))
+        qs.append(_gpu_weight(w, signs, 3))
+        xs.append(dev(x))
+    for (n, k), y, ref in zip(shapes, dq.wq_linear_batch(qs, xs), refs):
+        check_close(y.float().cpu().numpy(), ref, f"batch n={n} k={k} m={m}")
+
+
 # ---------------------------------------------------------- matrix-core path
 
 @pytest.mark.parametrize("bits", [3, 4, 6, 8])
