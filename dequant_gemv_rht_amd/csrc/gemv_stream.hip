@@ -1082,16 +1082,34 @@ __host__ __device__ inline int quad_split(int nq, int ks) {
   return p < ks ? p : ks;
 }
 
+constexpr int kQuadMaxChunks = 4;
+constexpr int kLdsWords = 160 * 1024 / 4;
+
+// A workgroup's LDS: the arranged activations of one K chunk (kc segments
+// of 16 slices, the last chunk shorter), the row parts of every unit and
+// chunk, and the scales and zeros of the whole K.
 struct QuadLds {
+  int chunks, kc, p;      // K chunks of kc segments; DPP rows per quad
+  int sc;                 // slices per batch row in the activation block
   int part, szl, total;   // 4-byte words
 };
 
-__host__ __device__ inline QuadLds quad_lds(int mt, int S, int KS, int G, int nq) {
+__host__ __device__ inline QuadLds quad_lds_at(int mt, int S, int KS, int G, int nq, int chunks) {
   QuadLds l;
-  const int p = quad_split(nq, KS);
-  l.part = (mt * S * kSliceStride + 3) & ~3;      // activations [mt][S][20], sums in words 16, 17
-  l.szl = (l.part + 4 * nq * p * mt + 1) & ~1;    // row parts [4 nq][p][mt]
-  l.total = l.szl + ((4 * nq * G + 7) & ~7) * 2;  // scale, zero as fp32 [4 nq][G][2], whole groups of 8
+  l.kc = (KS + chunks - 1) / chunks;
+  l.chunks = (KS + l.kc - 1) / l.kc;
+  l.p = quad_split(nq, KS - (l.chunks - 1) * l.kc);   // every chunk has a segment per part
+  l.sc = S < 16 * l.kc ? S : 16 * l.kc;
+  l.part = (mt * l.sc * kSliceStride + 3) & ~3;        // activations [mt][sc][20], sums in words 16, 17
+  l.szl = (l.part + 4 * nq * l.p * l.chunks * mt + 1) & ~1;   // row parts [4 nq][chunks][p][mt]
+  l.total = l.szl + ((4 * nq * G + 7) & ~7) * 2;      // scale, zero as fp32 [4 nq][G][2], whole groups of 8
+  return l;
+}
+
+// The fewest K chunks (up to kQuadMaxChunks) whose layout fits in 160 KB.
+__host__ __device__ inline QuadLds quad_lds(int mt, int S, int KS, int G, int nq) {
+  QuadLds l = quad_lds_at(mt, S, KS, G, nq, 1);
+  for (int c = 2; c <= kQuadMaxChunks && l.total > kLdsWords; ++c) l = quad_lds_at(mt, S, KS, G, nq, c);
   return l;
 }
 
@@ -1105,30 +1123,96 @@ __device__ __forceinline__ void unit_range(int u, int p, uint32_t p_inv, int KS,
   e = (int)(__umul24((uint32_t)(KS * (sub + 1)), p_inv) >> 16);
 }
 
-template <int BITS, int MT, int D>
+// A DPP row's walk over its tasks in one K chunk: the units rg, rg + 32,
+// ... (quad q, part sub) over the chunk's segments, then idle steps (u at
+// or past NU) up to the chunk's fixed step count T, so that every DPP row
+// enters a chunk at the same step.
+struct QuadWalk {
+  int u, q, s, e;   // unit, quad, segment, the unit's end segment (absolute)
+  int base, len;    // the chunk's first segment and segment count
+};
+
+struct QuadGeom {
+  int rg, NU, p, KS, kc, T;   // T: steps per chunk, the same in every DPP row
+  uint32_t p_inv;
+};
+
+__device__ __forceinline__ void walk_unit(const QuadGeom &g, QuadWalk &w) {
+  unit_range(w.u, g.p, g.p_inv, w.len, w.q, w.s, w.e);
+  w.s += w.base;
+  w.e += w.base;
+}
+
+// the walk of chunk c (past the last chunk: idle throughout)
+__device__ __forceinline__ void walk_start(const QuadGeom &g, QuadWalk &w, int c) {
+  w.base = c * g.kc;
+  w.len = min(g.kc, g.KS - w.base);
+  w.u = w.len > 0 ? g.rg : g.NU;
+  walk_unit(g, w);
+}
+
+__device__ __forceinline__ void walk_next(const QuadGeom &g, QuadWalk &w) {
+  if (++w.s == w.e) {
+    w.u += kQRG;
+    walk_unit(g, w);
+  }
+}
+
+template <int BITS, int MT, int D, bool CHUNKED>
 __device__ __forceinline__ void stream_quads(const LinDesc &L, int m_valid, int r0, int rows, uint32_t *smem) {
   static_assert(MT == 2 || MT == 4 || MT == 8, "batch tile");
   constexpr int ZL = 2;
-  constexpr int XCH = MT <= 4 ? 3 * MT : 16;   // 8 KB copy passes held in registers (K <= 9830 at MT 4)
+  constexpr int XCH = MT <= 4 ? 3 * MT : 16;   // 8 KB copy passes held in registers
   const int t = threadIdx.x, rg = t >> 4, j = t & 15;
   const int K = L.k, KS = (K + kSeg - 1) / kSeg, G = K / kGroup, S = K / kSlice;
   const int wpr = S * BITS;
   const int NQ = (rows + 3) >> 2;
-  const int p = quad_split(NQ, KS), NU = NQ * p;
-  const uint32_t p_inv = (65536u + (uint32_t)p - 1u) / (uint32_t)p;
   const bool full = (K % kSeg) == 0;
-  const QuadLds lay = quad_lds(MT, S, KS, G, NQ);
+  // the layout of a full workgroup (quad_lds, computed by the launcher): a
+  // last workgroup with fewer quads keeps its split, as more DPP rows per
+  // quad would need more room for row parts than the launch gave
+  const int chunks = CHUNKED ? L.q_chunks : 1, p = L.q_p, NU = NQ * p, PC = p * chunks;
+  QuadGeom geo;
+  geo.rg = rg;
+  geo.NU = NU;
+  geo.p = p;
+  geo.KS = KS;
+  geo.kc = L.q_kc;
+  geo.p_inv = L.q_pinv;
+  geo.T = ((NU + kQRG - 1) / kQRG) * L.q_spu;
+  geo.T = (geo.T + D - 1) / D * D;
+  const int sc = L.q_sc;
   uint32_t *xp = smem;
-  float *part = reinterpret_cast<float *>(smem + lay.part);
-  float *szl = reinterpret_cast<float *>(smem + lay.szl);
+  float *part = reinterpret_cast<float *>(smem + L.q_part);
+  float *szl = reinterpret_cast<float *>(smem + L.q_szl);
 
   const rsrc_t rc = make_rsrc(L.codes + (size_t)r0 * wpr, (uint32_t)rows * wpr * 4);
   const int nszv = rows * G;
   const rsrc_t rsc = make_rsrc(L.scales + (size_t)r0 * G, (uint32_t)nszv * 2);
   const rsrc_t rz = make_rsrc(L.zeros + (size_t)r0 * G, (uint32_t)nszv * 2);
 
-  // 1. scales and zeros, then the arranged activations (batch rows past
-  //    m_valid read zero), ahead of the weight stream
+  // The activation block of chunk c: batch row m's slices [16 kc c, +sc) of
+  // the arranged rows (S slices of 5 16-byte pieces each).  Piece x of the
+  // block comes from piece (m S + 16 kc c) 5 + (x - 5 m sc), m = x / (5 sc)
+  // by a 32-bit reciprocal (exact: x < 2^14).  With one chunk the block is
+  // the arranged rows as they are.
+  const uint32_t xrow = 5u * (uint32_t)sc;
+  const uint32_t xrow_inv = L.q_xinv;
+  const int xtotal = MT * sc * kSliceStride * 4;         // bytes of the LDS block
+  const rsrc_t rxq = make_rsrc(L.xq, (uint32_t)(m_valid * S * kSliceStride * 4));
+  auto x_src = [&](int off, int c) -> uint32_t {
+    if (off >= xtotal) return kOOB;
+    if constexpr (!CHUNKED) return (uint32_t)off;
+    const uint32_t x = (uint32_t)off >> 4;
+    const uint32_t m = __umulhi(x, xrow_inv);
+    return ((m * (uint32_t)S + 16u * (uint32_t)(geo.kc * c)) * 5u + (x - m * xrow)) << 4;
+  };
+  auto x_load = [&](uint32_t src) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rxq, src, 0, 0));
+  };
+
+  // 1. scales and zeros, then the arranged activations of chunk 0 (batch
+  //    rows past m_valid read zero), ahead of the weight stream
   const int nsz = 4 * NQ * G;               // scale/zero entries, padded to whole quads
   u32x4 sr[ZL], zr[ZL];
 #pragma unroll
@@ -1139,32 +1223,29 @@ __device__ __forceinline__ void stream_quads(const LinDesc &L, int m_valid, int 
   }
   // the first XCH 8 KB passes of the copy go to registers here and to LDS
   // once the code loads are out (their waits then cover these loads alone)
-  const int xtotal = MT * S * kSliceStride * 4;          // bytes of the LDS block
-  const rsrc_t rxq = make_rsrc(L.xq, (uint32_t)(m_valid * S * kSliceStride * 4));
   u32x4 xr[XCH];
 #pragma unroll
-  for (int c = 0; c < XCH; ++c) {
-    const int off = 16 * (t + kQuadThreads * c);
-    xr[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rxq, off < xtotal ? (uint32_t)off : kOOB,
-                                                                            0, 0));
-  }
+  for (int c = 0; c < XCH; ++c) xr[c] = x_load(x_src(16 * (t + kQuadThreads * c), 0));
 
   // 2. the first D steps of this DPP row's tasks
   const uint32_t seg_step = 16 * BITS * 4;
   const uint32_t row_bytes = (uint32_t)wpr * 4;
   const uint32_t quad_bytes = 4 * row_bytes;
   const uint32_t lane_off = (uint32_t)j * (BITS * 4);
-  int lu = rg, lq, ls, le;                  // load side: unit, quad, segment, end
-  unit_range(lu, p, p_inv, KS, lq, ls, le);
+  QuadWalk lw;                              // load side, D steps ahead
+  walk_start(geo, lw, 0);
   uint32_t cw[D][4][BITS];
+  auto issue = [&](uint32_t (&dst)[4][BITS]) {
+    const bool ok = lw.u < NU && (full || lw.s * 16 + j < S);
+    // past the range (kOOB + 3 rows stays above any buffer size): loads zero
+    const uint32_t co =
+        ok ? __umul24((uint32_t)lw.q, quad_bytes) + (uint32_t)lw.s * seg_step + lane_off : kOOB;
 #pragma unroll
-  for (int d = 0; d < D; ++d) {
-    const bool ok = lu < NU && (full || ls * 16 + j < S);
-    const uint32_t co = __umul24((uint32_t)lq, quad_bytes) + (uint32_t)ls * seg_step + lane_off;
+    for (int r = 0; r < 4; ++r) load_slice<BITS>(rc, co + r * row_bytes, dst[r]);
+    walk_next(geo, lw);
+  };
 #pragma unroll
-    for (int r = 0; r < 4; ++r) load_slice<BITS>(rc, ok ? co + r * row_bytes : kOOB, cw[d][r]);
-    if (++ls == le) { lu += kQRG; unit_range(lu, p, p_inv, KS, lq, ls, le); }
-  }
+  for (int d = 0; d < D; ++d) issue(cw[d]);
 
   // 3. scales, zeros and activations into LDS
 #pragma unroll
@@ -1196,106 +1277,118 @@ __device__ __forceinline__ void stream_quads(const LinDesc &L, int m_valid, int 
     if (off < xtotal) *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(xp) + off) = xr[c];
   }
   for (int off = 16 * (t + kQuadThreads * XCH); off < xtotal; off += 16 * kQuadThreads)
-    *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(xp) + off) =
-        __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rxq, (uint32_t)off, 0, 0));
+    *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(xp) + off) = x_load(x_src(off, 0));
   __syncthreads();
 
-  // 4. walk the units: values r * MT + m accumulate s * sum (q - z) x over
-  //    the unit's segments
+  // 4. walk the units chunk by chunk: values r * MT + m accumulate
+  //    s * sum (q - z) x over the unit's segments of the chunk
   const UnpackConsts uc = unpack_consts<BITS>();
-  int cu = rg, cq, cs, ce;                  // compute side
-  unit_range(cu, p, p_inv, KS, cq, cs, ce);
-  const int steps = ((NU + kQRG - 1) / kQRG) * ((KS + p - 1) / p);
+  QuadWalk cw_;                             // compute side
   constexpr int NV = 4 * MT;   // partials of a unit: value r * MT + m
   float acc[NV];
 #pragma unroll
   for (int v = 0; v < NV; ++v) acc[v] = 0.f;
-  for (int i0 = 0; i0 < steps; i0 += D) {
+  for (int c = 0; c < chunks; ++c) {
+    if (CHUNKED && c > 0) {
+      // every DPP row is done with chunk c - 1's activations: load chunk c's
+      __syncthreads();
+      for (int o0 = 16 * t; o0 < xtotal; o0 += 16 * kQuadThreads * XCH) {
 #pragma unroll
-    for (int d = 0; d < D; ++d) {
-      if (cu < NU) {
-        const int slice = cs * 16 + j;
-        const bool sv = full || slice < S;
-        const int sl = sv ? slice : 0;
-        const uint32_t zi = __umul24((uint32_t)(4 * cq), (uint32_t)G) + (uint32_t)(sl >> 2);
-        float sf[4], zf[4];
+        for (int h = 0; h < XCH; ++h) xr[h] = x_load(x_src(o0 + 16 * kQuadThreads * h, c));
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float2 sz = *reinterpret_cast<const float2 *>(&szl[2 * (zi + r * G)]);
-          sf[r] = sv ? sz.x : 0.f;
-          zf[r] = sz.y;
-        }
-        // the batch rows' activation slices (all of them up to 4 rows, read
-        // before the unpack so their latency overlaps it; one at a time at 8)
-        constexpr int XR = MT <= 4 ? MT : 1;
-        uint32_t xv[XR][16];
-        float2 xq[XR];
-        auto read_x = [&](int m, int slot) {
-          const uint32_t *src = &xp[(m * S + sl) * kSliceStride];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const u32x4 v = reinterpret_cast<const u32x4 *>(src)[q];
-            xv[slot][4 * q + 0] = v.x; xv[slot][4 * q + 1] = v.y; xv[slot][4 * q + 2] = v.z; xv[slot][4 * q + 3] = v.w;
-          }
-          xq[slot] = *reinterpret_cast<const float2 *>(src + 16);
-        };
-        if constexpr (MT <= 4) {
-#pragma unroll
-          for (int m = 0; m < MT; ++m) read_x(m, m);
-        }
-        uint32_t pr[4][16];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) unpack_pairs<BITS>(cw[d][r], uc, pr[r]);
-        // s * (sum (1024+q') x' - 1024 XS - z X) = s * sum (q - z) x
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-          const int xs = MT <= 4 ? m : 0;
-          if constexpr (MT > 4) read_x(m, 0);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float dd = fmaf(-zf[r], xq[xs].x, -xq[xs].y);
-#pragma unroll
-            for (int q = 0; q < 16; ++q) dd = dot2(pr[r][q], xv[xs][q], dd);
-            acc[r * MT + m] = fmaf(sf[r], dd, acc[r * MT + m]);
-          }
-        }
-        if (cs + 1 == ce) {
-          // the unit is done: its row parts over the 16 lanes, NV / 16 per lane
-          reduce_scatter16<NV>(acc, j);
-          const int sub = cu - cq * p;
-          if constexpr (NV == 8) {
-            const int vi = j >> 1;
-            if ((j & 1) == 0) part[((4 * cq + vi / MT) * p + sub) * MT + vi % MT] = acc[0];
-          } else {
-#pragma unroll
-            for (int e = 0; e < NV / 16; ++e) {
-              const int vi = (NV / 16) * j + e;
-              part[((4 * cq + vi / MT) * p + sub) * MT + vi % MT] = acc[e];
-            }
-          }
-#pragma unroll
-          for (int v2 = 0; v2 < NV; ++v2) acc[v2] = 0.f;
-          cu += kQRG;
-          unit_range(cu, p, p_inv, KS, cq, cs, ce);
-        } else {
-          ++cs;
+        for (int h = 0; h < XCH; ++h) {
+          const int off = o0 + 16 * kQuadThreads * h;
+          if (off < xtotal) *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(xp) + off) = xr[h];
         }
       }
-      // refill this buffer with the task D steps ahead
-      const bool ok = lu < NU && (full || ls * 16 + j < S);
-      const uint32_t co = __umul24((uint32_t)lq, quad_bytes) + (uint32_t)ls * seg_step + lane_off;
+      __syncthreads();
+    }
+    const int xbase = 16 * geo.kc * c;      // the chunk's first slice
+    walk_start(geo, cw_, c);
+    for (int i0 = 0; i0 < geo.T; i0 += D) {
+      // the refills of a chunk's last D steps issue the next chunk's first
+      // (with one chunk the walk is idle past its units anyway)
+      if (CHUNKED && i0 + D == geo.T) walk_start(geo, lw, c + 1);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) load_slice<BITS>(rc, ok ? co + r * row_bytes : kOOB, cw[d][r]);
-      if (++ls == le) { lu += kQRG; unit_range(lu, p, p_inv, KS, lq, ls, le); }
+      for (int d = 0; d < D; ++d) {
+        if (cw_.u < NU) {
+          const int slice = cw_.s * 16 + j;
+          const bool sv = full || slice < S;
+          const int sl = sv ? slice : xbase;
+          const uint32_t zi = __umul24((uint32_t)(4 * cw_.q), (uint32_t)G) + (uint32_t)(sl >> 2);
+          float sf[4], zf[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float2 sz = *reinterpret_cast<const float2 *>(&szl[2 * (zi + r * G)]);
+            sf[r] = sv ? sz.x : 0.f;
+            zf[r] = sz.y;
+          }
+          // the batch rows' activation slices (all of them up to 4 rows, read
+          // before the unpack so their latency overlaps it; one at a time at 8)
+          constexpr int XR = MT <= 4 ? MT : 1;
+          uint32_t xv[XR][16];
+          float2 xq[XR];
+          auto read_x = [&](int m, int slot) {
+            const uint32_t *src = &xp[(m * sc + sl - xbase) * kSliceStride];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const u32x4 v = reinterpret_cast<const u32x4 *>(src)[q];
+              xv[slot][4 * q + 0] = v.x; xv[slot][4 * q + 1] = v.y; xv[slot][4 * q + 2] = v.z; xv[slot][4 * q + 3] = v.w;
+            }
+            xq[slot] = *reinterpret_cast<const float2 *>(src + 16);
+          };
+          if constexpr (MT <= 4) {
+#pragma unroll
+            for (int m = 0; m < MT; ++m) read_x(m, m);
+          }
+          uint32_t pr[4][16];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) unpack_pairs<BITS>(cw[d][r], uc, pr[r]);
+          // s * (sum (1024+q') x' - 1024 XS - z X) = s * sum (q - z) x
+#pragma unroll
+          for (int m = 0; m < MT; ++m) {
+            const int xs = MT <= 4 ? m : 0;
+            if constexpr (MT > 4) read_x(m, 0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              float dd = fmaf(-zf[r], xq[xs].x, -xq[xs].y);
+#pragma unroll
+              for (int q = 0; q < 16; ++q) dd = dot2(pr[r][q], xv[xs][q], dd);
+              acc[r * MT + m] = fmaf(sf[r], dd, acc[r * MT + m]);
+            }
+          }
+          if (cw_.s + 1 == cw_.e) {
+            // the unit's share of the chunk is done: its row parts over the
+            // 16 lanes, NV / 16 per lane (one per lane pair at NV = 8)
+            reduce_scatter16<NV>(acc, j);
+            const int slot = c * p + (cw_.u - cw_.q * p);
+            if constexpr (NV == 8) {
+              const int vi = j >> 1;
+              if ((j & 1) == 0) part[((4 * cw_.q + vi / MT) * PC + slot) * MT + vi % MT] = acc[0];
+            } else {
+#pragma unroll
+              for (int e = 0; e < NV / 16; ++e) {
+                const int vi = (NV / 16) * j + e;
+                part[((4 * cw_.q + vi / MT) * PC + slot) * MT + vi % MT] = acc[e];
+              }
+            }
+#pragma unroll
+            for (int v2 = 0; v2 < NV; ++v2) acc[v2] = 0.f;
+          }
+        }
+        walk_next(geo, cw_);
+        // refill this buffer with the task D steps ahead
+        issue(cw[d]);
+      }
     }
   }
   __syncthreads();
 
-  // 5. add each row's parts in order, store
+  // 5. add each row's parts in order (chunk, then part), store
   for (int e = t; e < rows * m_valid; e += kQuadThreads) {
     const int row = e / m_valid, m = e % m_valid;
     float sum = 0.f;
-    for (int u = 0; u < p; ++u) sum += part[(row * p + u) * MT + m];
+    for (int u = 0; u < PC; ++u) sum += part[(row * PC + u) * MT + m];
     store_out(L, m, r0 + row, sum);
   }
 }
@@ -1404,14 +1497,28 @@ struct QDepth {
   static constexpr int d = 2;
 };
 
-template <int BITS, int MT>
+template <int BITS, int MT, bool CHUNKED>
 __global__ __launch_bounds__(kQuadThreads) void gemv_quad_kernel(GemvArgs a) {
   extern __shared__ uint32_t smem[];
   const int w = blockIdx.x;
   const LinDesc L = fetch_desc(a, w);
+  asm volatile("" ::"s"(L.q_chunks), "s"(L.q_kc), "s"(L.q_p), "s"(L.q_spu), "s"(L.q_pinv), "s"(L.q_sc),
+               "s"(L.q_xinv), "s"(L.q_part), "s"(L.q_szl));
   const int r0 = (w - L.tile_begin) * L.rows_per_wg;
   if (r0 >= L.n) return;
-  stream_quads<BITS, MT, QDepth<BITS>::d>(L, a.m, r0, min(L.rows_per_wg, L.n - r0), smem);
+  stream_quads<BITS, MT, QDepth<BITS>::d, CHUNKED>(L, a.m, r0, min(L.rows_per_wg, L.n - r0), smem);
+}
+
+// the chunk-walking kernel only where some linear's activations need chunks
+template <int BITS, int MT>
+hipError_t launch_quad(const GemvArgs &a, hipStream_t s) {
+  bool chunked = false;
+  for (int i = 0; i < a.count; ++i) chunked = chunked || a.lin[i].q_chunks > 1;
+  if (chunked)
+    hipLaunchKernelGGL((gemv_quad_kernel<BITS, MT, true>), dim3(a.tiles), dim3(kQuadThreads), a.lds_bytes, s, a);
+  else
+    hipLaunchKernelGGL((gemv_quad_kernel<BITS, MT, false>), dim3(a.tiles), dim3(kQuadThreads), a.lds_bytes, s, a);
+  return hipGetLastError();
 }
 
 template <int BITS>
@@ -1430,15 +1537,9 @@ hipError_t launch_bits(int mt, const GemvArgs &a, hipStream_t s) {
     case 1:
       hipLaunchKernelGGL((gemv_stream_kernel<BITS, 1>), dim3(a.tiles), dim3(kStreamThreads), a.lds_bytes, s, a);
       break;
-    case 2:
-      hipLaunchKernelGGL((gemv_quad_kernel<BITS, 2>), dim3(a.tiles), dim3(kQuadThreads), a.lds_bytes, s, a);
-      break;
-    case 4:
-      hipLaunchKernelGGL((gemv_quad_kernel<BITS, 4>), dim3(a.tiles), dim3(kQuadThreads), a.lds_bytes, s, a);
-      break;
-    case 8:
-      hipLaunchKernelGGL((gemv_quad_kernel<BITS, 8>), dim3(a.tiles), dim3(kQuadThreads), a.lds_bytes, s, a);
-      break;
+    case 2: return launch_quad<BITS, 2>(a, s);
+    case 4: return launch_quad<BITS, 4>(a, s);
+    case 8: return launch_quad<BITS, 8>(a, s);
     default:
       return hipErrorInvalidValue;
   }
@@ -1508,11 +1609,38 @@ hipError_t launch_gemv_stream(int bits, int mt, const GemvArgs &a, hipStream_t s
       hipLaunchKernelGGL((gemv_ring_mixed_kernel<false>), dim3(a.tiles), dim3(kStreamThreads), a.lds_bytes, s, a);
     return hipGetLastError();
   }
+  if (a.ring || mt < 2) {
+    switch (bits) {
+      case 3: return launch_bits<3>(mt, a, s);
+      case 4: return launch_bits<4>(mt, a, s);
+      case 6: return launch_bits<6>(mt, a, s);
+      case 8: return launch_bits<8>(mt, a, s);
+    }
+    return hipErrorInvalidValue;
+  }
+  // batch tiles: each linear's layout of a full workgroup, which must fit
+  // in the LDS the launch gives
+  GemvArgs b = a;
+  for (int i = 0; i < a.count; ++i) {
+    LinDesc &L = b.lin[i];
+    const int S = L.k / kSlice, KS = (L.k + kSeg - 1) / kSeg, G = L.k / kGroup;
+    const QuadLds l = quad_lds(mt, S, KS, G, (L.rows_per_wg + 3) / 4);
+    if (l.total > kLdsWords || l.total * 4 > a.lds_bytes) return hipErrorInvalidValue;
+    L.q_chunks = l.chunks;
+    L.q_kc = l.kc;
+    L.q_p = l.p;
+    L.q_spu = (l.kc + l.p - 1) / l.p;
+    L.q_pinv = (65536u + (uint32_t)l.p - 1u) / (uint32_t)l.p;
+    L.q_sc = l.sc;
+    L.q_xinv = 0xFFFFFFFFu / (5u * (uint32_t)l.sc) + 1u;
+    L.q_part = l.part;
+    L.q_szl = l.szl;
+  }
   switch (bits) {
-    case 3: return launch_bits<3>(mt, a, s);
-    case 4: return launch_bits<4>(mt, a, s);
-    case 6: return launch_bits<6>(mt, a, s);
-    case 8: return launch_bits<8>(mt, a, s);
+    case 3: return launch_bits<3>(mt, b, s);
+    case 4: return launch_bits<4>(mt, b, s);
+    case 6: return launch_bits<6>(mt, b, s);
+    case 8: return launch_bits<8>(mt, b, s);
   }
   return hipErrorInvalidValue;
 }

@@ -42,6 +42,14 @@ struct LinDesc {
   int32_t tile_begin;           // first workgroup of this linear in the grid
   int32_t out_f32;
   int32_t ks_inv;               // ceil(2^16 / KS), KS = ceil(k / 512): x / KS = (x * ks_inv) >> 16 for x <= 64
+  // batch-tile (row-quad) kernel, set by its launcher: the LDS layout of a
+  // full workgroup and its walk over K (no divisions left to the kernel)
+  int32_t q_chunks, q_kc;       // K chunks of q_kc 512-wide segments (the last one shorter)
+  int32_t q_p, q_spu;           // DPP rows per quad (K parts); segments per part, at most
+  uint32_t q_pinv;              // ceil(2^16 / q_p)
+  int32_t q_sc;                 // slices per batch row in the activation block
+  uint32_t q_xinv;              // ceil(2^32 / (5 q_sc)): 16-byte pieces per batch row
+  int32_t q_part, q_szl;        // word offsets of the row parts and of the scales and zeros
 };
 
 struct GemvArgs {

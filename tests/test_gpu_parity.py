@@ -158,12 +158,21 @@ def test_linear_shapes(n, k, rht, out_f32, m):
 
 
 @pytest.mark.parametrize("m", [2, 4, 7])
-def test_batch_tiles_long_k_fall_back(m):
-    # K = 16384 arranged activations of a 4-row tile need 160 KB of LDS, more
-    # than a CU has: the call falls back to the tiled kernel, which rotates
-    # for itself; the result must be the same layer
-    say(f"linear long K m={m}")
+def test_batch_tiles_k_chunks(m):
+    # K = 16384: the arranged activations of a 2-row tile fit in LDS whole,
+    # a 4-row tile's (160 KB) in 2 chunks of K, an 8-row tile's in 3; each
+    # workgroup walks its units chunk by chunk
+    say(f"linear K chunks m={m}")
     _run_case(96, 16384, m, 4, True, False, 50 + m)
+
+
+@pytest.mark.parametrize("m", [4, 7])
+def test_batch_tiles_long_k_fall_back(m):
+    # K = 65536: a 4-row tile's activations do not fit in LDS even in 4
+    # chunks of K: the call falls back to the tiled kernel, which rotates for
+    # itself; the result must be the same layer
+    say(f"linear long K m={m}")
+    _run_case(96, 65536, m, 4, True, False, 55 + m)
 
 
 @pytest.mark.parametrize("n", [1, 5, 129])
@@ -174,12 +183,20 @@ def test_batch_tiles_few_rows(n):
     _run_case(n, 2560, 4, 4, True, False, 60 + n)
 
 
+@pytest.mark.parametrize("m", [4, 8])
+def test_batch_tiles_short_last_workgroup(m):
+    # n = 17336 over 256 CUs: 255 workgroups of 68 rows (17 quads, one DPP
+    # row each), the last with 64 (16 quads); the last keeps the split of a
+    # full workgroup, whose LDS layout the launch sized
+    say(f"linear short last workgroup m={m}")
+    _run_case(17336, 1024, m, 4, True, False, 80 + m)
+
+
 @pytest.mark.parametrize("m", [6, 16])
 @pytest.mark.parametrize("long_k", [False, True])
-def test_batch_tiles_of_eight_and_four(m, long_k):
-    # a call whose linears all fit 8 rows of arranged activations in LDS runs
-    # in tiles of 8 batch rows; with K = 9728 (8 rows take 190 KB) the whole
-    # call runs in tiles of 4; either way every output is its layer
+def test_batch_tiles_of_eight(m, long_k):
+    # tiles of 8 batch rows over linears of K 2560 and 4096 (activations
+    # whole in LDS) and 9728 (8 rows take 190 KB: 2 chunks of K) in one call
     shapes = [(256, 2560), (130, 4096)] + ([(64, 9728)] if long_k else [])
     say(f"linear batch tiles m={m} long_k={long_k}")
     qs, xs, refs = [], [], []
