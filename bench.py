@@ -202,6 +202,7 @@ class _ReadCeiling:
         copies = self.buf.numel() // stride
         if copies < 2:
             raise ValueError(f"read ceiling: {nbytes} bytes need a pool of at least {2 * stride} bytes")
+        copies = min(copies, 4096)   # one graph node per copy: keep the graph small
         lib, base, sink = dq.lib(), self.buf.data_ptr(), self.sink.data_ptr()
 
         def one(i):
@@ -332,7 +333,60 @@ def sweep(args) -> None:
                      ceiling.us(sb, stream), sf, None, None)
             del qws, xs, ys, hosts
             torch.cuda.empty_cache()
+    if not args.sweep_only or "f2" in args.sweep_only.split(","):
+        _sweep_embed(stream, ceiling, emit)
     log(f"sweep done: {len(rows_out)} rows; host threads {threads_all}")
+
+
+def _sweep_embed(stream, ceiling, emit) -> None:
+    """The head table of the int6 block config (151936 x 2560 int8, no
+    rotation) as the tied token embedding: wq_embed of T token ids to fp16.
+    Call c gathers ids perm[c T : (c + 1) T] of one random permutation of the
+    table's rows (up to 1024 calls), so a graph replay touches every row at
+    most once (T = 1 and 64: 1024 and 65536 rows, 2.6 and 170 MB, which may
+    stay in the last-level cache)."""
+    import ctypes
+    import torch
+    import dequant_gemv_rht_amd as dq
+    from oracle import embed as OE
+    from oracle import rtn as OR
+    wl = W.WORKLOADS["block_int6_head_int8"]
+    idx = len(wl.linears) - 1
+    lin = wl.linears[idx]
+    log(f"sweep f2 embedding gather: {lin.n} x {lin.k} int8 table")
+    w, _, _, _ = W.linear_inputs(0, wl.wid, idx, lin, 1)
+    qw = dq.quantize_weight(torch.from_numpy(w).cuda(), 8, None)
+    rng = np.random.default_rng(21)
+    sample = np.sort(rng.choice(lin.n, 512, replace=False))
+    q, sc, z = OR.rtn(w[sample], 8)
+    del w
+    perm = torch.from_numpy(rng.permutation(lin.n).astype(np.int32)).cuda()
+    st = qw.c_struct()
+    lib = dq.lib()
+    for T in (1, 64, 512):
+        out = torch.empty((T, lin.k), dtype=torch.float16, device="cuda")
+        ncalls = min(1024, lin.n // T)
+
+        def one(c, T=T, out=out):
+            ids = perm.data_ptr() + 4 * c * T
+            return lambda sp: dq._check("wq_embed", lib.wq_embed(ctypes.byref(st), ids, T, out.data_ptr(),
+                                                                 dq.WQ_F16, lin.k, sp))
+        log(f"f2 T={T}: {ncalls} gathers in a graph")
+        us = _time_launches([one(c) for c in range(ncalls)], stream)
+        # codes, scales and zeros of T rows, the ids, the fp16 rows out
+        nbytes = T * (lin.k + 4 * (lin.k // 128) + 4 + 2 * lin.k)
+        log(f"f2 T={T}: read ceiling, oracle")
+        ids = rng.integers(0, len(sample), T)
+        t0 = time.perf_counter()
+        reps = 0
+        while reps < 3 or time.perf_counter() - t0 < 0.2:
+            OE.embed(q, sc, z, ids)
+            reps += 1
+        o1 = (time.perf_counter() - t0) / reps * 1e3
+        emit("f2", "embed_gather", T, 8, f"{lin.n}x{lin.k} table, {T} ids", nbytes, us,
+             ceiling.us(nbytes, stream), 0, o1, None)
+    del qw, perm
+    torch.cuda.empty_cache()
 
 
 def main():
@@ -347,7 +401,7 @@ def main():
     ap.add_argument("--pool-bytes", type=int, default=POOL_BYTES)
     ap.add_argument("--sweep", action="store_true",
                     help="print the per-config, per-linear table instead of the headline JSON line")
-    ap.add_argument("--sweep-only", default="", help="comma-separated configs for --sweep (c1..c5)")
+    ap.add_argument("--sweep-only", default="", help="comma-separated configs for --sweep (c1..c5; f2: the embedding gather)")
     ap.add_argument("--cpu-rows", type=int, default=256,
                     help="output rows the oracle computes per linear in --sweep (scaled to all rows)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",

@@ -13,6 +13,7 @@ Functions mirror the C ABI in ``include/wq.h``:
   rht_apply(x, signs, out=None)                      -> rotated fp16 activations
   wq_linear(weight, x, out_dtype=float16, fuse_rht=True, workspace=None) -> y
   wq_linear_batch(weights, xs, out_dtypes=None, fuse_rht=True, workspace=None) -> [y]
+  wq_embed(table, ids, out_dtype=float16, out=None)  -> dequantised table rows
 """
 
 from __future__ import annotations
@@ -60,6 +61,7 @@ SIGNATURES = {
                                _u32, _vp, _sz, _vp]),
     "wq_last_error": (ctypes.c_char_p, []),
     "wq_stream_read": (_i32, [_vp, _sz, _vp, _vp]),
+    "wq_embed": (_i32, [ctypes.POINTER(WqWeight), _vp, _i64, _vp, _i32, _i64, _vp]),
 }
 
 _lib = None
@@ -267,6 +269,18 @@ def wq_linear_batch(weights: Sequence[QWeight], xs: Sequence[torch.Tensor], out_
         workspace = new_workspace(wq_linear_batch_workspace(weights, m), xs[0].device)
     BatchCall(weights, xs, ys, fuse_rht, workspace)()
     return ys
+
+
+def wq_embed(table: QWeight, ids: torch.Tensor, out_dtype=torch.float16, out: Optional[torch.Tensor] = None):
+    """Rows ``ids`` of the quantised ``table``, dequantised: [len(ids)][k]."""
+    _dev(ids, torch.int32, "ids")
+    count = ids.numel()
+    y = torch.empty((count, table.k), dtype=out_dtype, device=ids.device) if out is None else out
+    st = table.c_struct()
+    _check("wq_embed", lib().wq_embed(ctypes.byref(st), _ptr(ids), count, _ptr(y),
+                                      WQ_F32 if out_dtype == torch.float32 else WQ_F16,
+                                      y.stride(0) if count else table.k, _stream()))
+    return y
 
 
 def stream_read(src: torch.Tensor, sink: torch.Tensor, nbytes: Optional[int] = None) -> None:

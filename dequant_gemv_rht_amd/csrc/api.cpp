@@ -501,6 +501,26 @@ wq_status wq_unpack(int32_t bits, int64_t n, int64_t k, const uint32_t *packed, 
                     "wq_unpack");
 }
 
+wq_status wq_embed(const wq_weight *w, const int32_t *ids, int64_t count, void *out, wq_dtype out_dtype,
+                   int64_t ldo, void *stream) {
+  clear_err();
+  wq_status st = check_weight(w, "wq_embed");
+  if (st != WQ_OK) return st;
+  if (w->bits == 0) return fail(WQ_E_UNSUPPORTED, "wq_embed: mixed width tables are not supported");
+  if (w->rht_signs) return fail(WQ_E_UNSUPPORTED, "wq_embed: the table must not be rotated (rht_signs NULL)");
+  if (out_dtype != WQ_F16 && out_dtype != WQ_F32) return fail(WQ_E_ARG, "wq_embed: out_dtype=%d", (int)out_dtype);
+  if (count < 0) return fail(WQ_E_ARG, "wq_embed: count=%lld", (long long)count);
+  if (count > (int64_t)INT32_MAX) return fail(WQ_E_UNSUPPORTED, "wq_embed: count above 2^31-1");
+  if (count == 0) return WQ_OK;
+  if (!ids || !out) return fail(WQ_E_ARG, "wq_embed: ids and out must be non-NULL");
+  if (ldo < w->k) return fail(WQ_E_ARG, "wq_embed: ldo=%lld < k=%lld", (long long)ldo, (long long)w->k);
+  if (ldo % (out_dtype == WQ_F32 ? 4 : 8))
+    return fail(WQ_E_ALIGN, "wq_embed: ldo must be a multiple of %d", out_dtype == WQ_F32 ? 4 : 8);
+  if (!aligned16(out) || ((uintptr_t)ids & 3u)) return fail(WQ_E_ALIGN, "wq_embed: out 16-byte, ids 4-byte aligned");
+  return hip_status(wq::launch_embed(*w, ids, count, out, out_dtype == WQ_F32, ldo, (hipStream_t)stream),
+                    "wq_embed");
+}
+
 wq_status rht_apply(const uint16_t *x, uint16_t *y, const uint32_t *signs, int64_t m, int64_t k, int64_t ldx,
                     int64_t ldy, int32_t block, void *stream) {
   clear_err();

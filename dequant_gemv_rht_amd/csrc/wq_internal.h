@@ -101,6 +101,10 @@ hipError_t launch_pack(int bits, int64_t n, int64_t k, const uint8_t *codes,
 hipError_t launch_unpack(int bits, int64_t n, int64_t k, const uint32_t *packed,
                          const uint8_t *block_bits, const uint64_t *block_off, uint8_t *codes,
                          hipStream_t s);
+// Rows ids[0..count) of a uniform-width table, dequantised to fp16 or fp32
+// [count][ldo] (embed.hip); ids outside [0, n) give rows of zeros.
+hipError_t launch_embed(const wq_weight &w, const int32_t *ids, int64_t count, void *out, bool f32, int64_t ldo,
+                        hipStream_t s);
 
 // MFMA GEMM for m >= 64 (gemm.hip), one launch for up to kMaxBatch linears
 // of one code width.  xr[i]: fp16 activations already rotated (or used as

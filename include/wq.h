@@ -215,6 +215,28 @@ wq_status wq_linear_batch(int32_t count, const wq_weight *w,
                           uint32_t flags, void *workspace, size_t workspace_bytes,
                           void *stream);
 
+/* Tied-embedding gather: rows ids[0..count) of a quantised table,
+ * dequantised,
+ *   out[i][k] = (q[ids[i]][k] - z[ids[i]][k/128]) * s[ids[i]][k/128],
+ * computed exactly and rounded once (nearest even) to fp16 or fp32.  The
+ * table of the output head serves as the token embedding (model card
+ * "24B0978 - Week 02 - Track 2, 40% target", section "Recipe": embed_tokens
+ * tied to lm_head, RTN 8-bit, group 128; the dequantisation is the
+ * grouped-affine form of "24B0978 - Week 01 - Track 2").
+ *   w          the table: uniform width (3, 4, 6 or 8), group 128, not
+ *              rotated (rht_signs NULL; a rotated table would need its rows
+ *              rotated back, which this call does not do)
+ *   ids        device int32 [count]; an id outside [0, w->n) gives a row
+ *              of zeros (the table is not read for it)
+ *   out        device fp16 or fp32 (out_dtype) [count][ldo], 16-byte
+ *              aligned; ldo >= k, a multiple of 8 (fp16) or 4 (fp32);
+ *              columns past k are not written
+ * count 0 does nothing.  Errors: WQ_E_ARG (NULL pointer, count < 0, ldo <
+ * k), WQ_E_UNSUPPORTED (mixed width, a rotated table, count >= 2^31),
+ * WQ_E_ALIGN, WQ_E_HIP (launch failure). */
+wq_status wq_embed(const wq_weight *w, const int32_t *ids, int64_t count, void *out,
+                   wq_dtype out_dtype, int64_t ldo, void *stream);
+
 /* Message for the last failed call on this thread ("" if none). */
 const char *wq_last_error(void);
 

@@ -28,8 +28,9 @@ Modules:
   rtn       - weight-side rotation and round-to-nearest quantisation
   pack      - bit placement of codes into 32-bit words (uniform and mixed)
   linear    - dequantisation and the plain triple-loop contraction (C)
+  embed     - rows of a quantised table, dequantised (tied-embedding gather)
 
 Every function carries a pin in ``tests/test_oracle_*.py``.
 """
 
-from . import hadamard, rtn, pack, linear  # noqa: F401
+from . import hadamard, rtn, pack, linear, embed  # noqa: F401

@@ -204,6 +204,27 @@ def test_stream_read_rejects_bad_arguments(lib):
     assert lib.wq_stream_read(8, 16, 16, None) == dq.WQ_E_ALIGN
 
 
+def test_embed_rejects_bad_arguments(lib):
+    # every check runs before anything touches the device
+    def call(w, ids=16, count=4, out=16, dt=dq.WQ_F16, ldo=2560):
+        return lib.wq_embed(ctypes.byref(w), ids, count, out, dt, ldo, None)
+    table = _weight(bits=8, n=151936, k=2560)
+    assert call(table, count=0, ids=None, out=None) == dq.WQ_OK         # nothing to do
+    assert call(table, ids=None) == dq.WQ_E_ARG
+    assert call(table, out=None) == dq.WQ_E_ARG
+    assert call(table, count=-1) == dq.WQ_E_ARG
+    assert call(table, ldo=2559) == dq.WQ_E_ARG
+    assert call(table, dt=7) == dq.WQ_E_ARG
+    assert call(table, ldo=2564) == dq.WQ_E_ALIGN                       # fp16 rows need ldo % 8 == 0
+    assert call(table, out=24) == dq.WQ_E_ALIGN
+    assert call(table, ids=18) == dq.WQ_E_ALIGN
+    assert call(table, count=1 << 31) == dq.WQ_E_UNSUPPORTED
+    assert call(_weight(bits=8, n=64, k=2560, rht_signs=16, rht_block=128)) == dq.WQ_E_UNSUPPORTED
+    assert call(_weight(bits=0, n=64, k=2560, block_bits=16, block_off=16)) == dq.WQ_E_UNSUPPORTED
+    assert call(_weight(bits=5, n=64, k=2560)) == dq.WQ_E_UNSUPPORTED
+    assert b"wq_embed" in lib.wq_last_error()
+
+
 def test_gemv_batch_rejects_small_workspace(lib):
     # above one batch row the GEMV arranges the activations in the workspace;
     # a missing or short one is refused before anything is launched

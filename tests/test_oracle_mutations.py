@@ -41,6 +41,10 @@ MUTANTS = [
     ("linear.py", "xr = rht(x64, sign_bits)", "xr = x64", "test_oracle_linear.py"),
     ("contract.c", "acc += w[j * k + t] * x[i * k + t];", "acc += w[j * k + t] * x[t];", "test_oracle_linear.py"),
     ("contract.c", "for (int64_t t = 0; t < k; ++t)", "for (int64_t t = 1; t < k; ++t)", "test_oracle_linear.py"),
+    ("embed.py", "return out.astype(out_dtype)", "return out.astype(np.float32).astype(out_dtype)",
+     "test_oracle_embed.py"),
+    ("embed.py", "if 0 <= r < n:", "if r < n:", "test_oracle_embed.py"),
+    ("embed.py", "out[i] = dequant(q[r:r + 1]", "out[i] = dequant(q[r - 1:r]", "test_oracle_embed.py"),
 ]
 
 
