@@ -331,11 +331,46 @@ def sweep(args) -> None:
                 del calls, pool
                 emit(cfg, f"**{len(same)} linears, one call**", m, lins[same[0]][1].bits, "all", sb, us,
                      ceiling.us(sb, stream), sf, None, None)
+                _sweep_shared(cfg, wl, m, lins, same, qws, xs, pooled, stream, ceiling, emit, sb, sf)
             del qws, xs, ys, hosts
             torch.cuda.empty_cache()
     if not args.sweep_only or "f2" in args.sweep_only.split(","):
         _sweep_embed(stream, ceiling, emit)
     log(f"sweep done: {len(rows_out)} rows; host threads {threads_all}")
+
+
+def _sweep_shared(cfg, wl, m, lins, same, qws, xs, pooled, stream, ceiling, emit, sb, sf) -> None:
+    """The grouped call with the inputs a decoder block shares: k and v on
+    q's activations, up on gate's, each quantised with its group's sign
+    vector, so the call rotates (and arranges) four inputs instead of seven.
+    Above one batch row only (at one row every workgroup rotates its own)."""
+    import torch
+    import dequant_gemv_rht_amd as dq
+    lead = {"k_proj": "q_proj", "v_proj": "q_proj", "up_proj": "gate_proj"}
+    names = [lins[j][1].name for j in same]
+    if m < 2 or not all(n in names for n in list(lead) + list(lead.values())):
+        return
+    sq, sx, saved = [], [], 0
+    for j in same:
+        i, lin = lins[j]
+        lj = same[names.index(lead.get(lin.name, lin.name))]
+        if lj == j:
+            sq.append(qws[j])
+            sx.append(xs[j])
+            continue
+        w, _, _, _ = W.linear_inputs(0, wl.wid, i, lin, m)
+        sq.append(dq.quantize_weight(torch.from_numpy(w).cuda(), lin.bits, qws[lj].signs))
+        sx.append(xs[lj])
+        saved += 2 * m * lin.k + lin.k // 8     # its activations and signs are the leader's
+        del w
+    pool = pooled(sq, sum(q.codes.numel() * 4 + q.scales.numel() * 4 for q in sq))
+    ws = dq.new_workspace(dq.wq_linear_batch_workspace(sq, m))
+    ys = [torch.empty((m, lins[j][1].n), dtype=torch.float16, device="cuda") for j in same]
+    calls = [dq.BatchCall(p, sx, ys, True, ws) for p in pool]
+    us = _time_launches(calls, stream)
+    del calls, pool
+    emit(cfg, f"**{len(same)} linears, one call, shared inputs**", m, lins[same[0]][1].bits, "all",
+         sb - saved, us, ceiling.us(sb - saved, stream), sf, None, None)
 
 
 def _sweep_embed(stream, ceiling, emit) -> None:

@@ -164,6 +164,18 @@ bool plan_stream(int count, const wq_weight *w, int64_t m, bool rotate, int *wg,
   return *lds <= kMaxLds;
 }
 
+// The first linear j <= i of a call whose input is linear i's: the same
+// activations (pointer and row stride), the same K and the same rotation
+// (sign vector pointer, or none).  Linears that share an input, such as the
+// query, key and value projections quantised with one sign vector, then
+// share its rotation ("24B0978 - Week 01 - Track 2", paragraph on the random
+// Hadamard transform: one rotation of the activations per input).
+int same_input(const wq_weight *w, const uint16_t *const *x, const int64_t *ldx, int i) {
+  for (int j = 0; j < i; ++j)
+    if (x[j] == x[i] && ldx[j] == ldx[i] && w[j].k == w[i].k && w[j].rht_signs == w[i].rht_signs) return j;
+  return i;
+}
+
 // Bytes of the arranged activations of m rows of a linear with k columns
 // (the batch-tile kernels' LDS slice layout: 80 bytes per 32 elements).
 size_t xprep_bytes(int64_t k, int64_t m) { return align256((size_t)m * (size_t)(k / wq::kSlice) * 80); }
@@ -205,17 +217,30 @@ wq_status run_gemv(int count, const wq_weight *w, const uint16_t *const *x, cons
     order_by_k(count, w, order, ws);
     if (plan_stream(count, ws, 8, rotate, wg, rpw, &lds, &ring)) tile = 8;
   }
+  // each distinct input arranged once (linears sharing one share its block)
   uint32_t *xq[WQ_MAX_BATCH];
+  const uint16_t *px[WQ_MAX_BATCH];
+  int64_t pld[WQ_MAX_BATCH], kk[WQ_MAX_BATCH];
   const uint32_t *sg[WQ_MAX_BATCH];
-  int64_t kk[WQ_MAX_BATCH];
+  uint32_t *pq[WQ_MAX_BATCH];
+  int np = 0;
   size_t off = 0;
   for (int i = 0; i < count; ++i) {
     xq[i] = reinterpret_cast<uint32_t *>(static_cast<char *>(workspace) + off);
     off += xprep_bytes(w[i].k, m);
-    sg[i] = rotate ? w[i].rht_signs : nullptr;
-    kk[i] = w[i].k;
+    const int j = same_input(w, x, ldx, i);
+    if (j < i) {
+      xq[i] = xq[j];
+      continue;
+    }
+    px[np] = x[i];
+    pld[np] = ldx[i];
+    sg[np] = rotate ? w[i].rht_signs : nullptr;
+    kk[np] = w[i].k;
+    pq[np] = xq[i];
+    ++np;
   }
-  wq_status st = hip_status(wq::launch_xprep(w[0].bits, count, x, ldx, sg, kk, m, xq, s), "wq_linear");
+  wq_status st = hip_status(wq::launch_xprep(w[0].bits, np, px, pld, sg, kk, m, pq, s), "wq_linear");
   if (st != WQ_OK) return st;
   const uint32_t *xt[WQ_MAX_BATCH];
   const uint16_t *xc[WQ_MAX_BATCH];
@@ -385,7 +410,12 @@ wq_status run_gemm(int count, const wq_weight *w, const uint16_t *const *x, cons
   for (int i = 0; i < count; ++i) {
     xr[i] = x[i];
     ldr[i] = ldx[i];
-    if (rotate && w[i].rht_signs) {
+    const int j = rotate && w[i].rht_signs ? same_input(w, x, ldx, i) : i;
+    if (j < i) {
+      // an earlier linear of the call rotates this same input
+      xr[i] = xr[j];
+      ldr[i] = ldr[j];
+    } else if (rotate && w[i].rht_signs) {
       uint16_t *xt = reinterpret_cast<uint16_t *>(ws + g.rot[i]);
       ldr[i] = rotated_ld(w[i]);
       rx[nr] = x[i];

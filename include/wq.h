@@ -207,7 +207,11 @@ wq_status wq_linear(const wq_weight *w, const uint16_t *x, int64_t m, int64_t ld
  * (17 <= m < 64, or the mixed 6/8-bit layout above m = 16) they run one
  * after another on the stream exactly as wq_linear would, sharing the
  * workspace.  Same math and layout as wq_linear, applied to each
- * w[i], x[i], y[i].  Arrays of length `count` are host arrays. */
+ * w[i], x[i], y[i].  In the grouped launches, linears with the same input
+ * (x and ldx equal, the same k and the same rht_signs pointer, e.g. query,
+ * key and value projections quantised with one sign vector) share one
+ * rotation and arrangement of it ("24B0978 - Week 01 - Track 2", paragraph on the random
+ * Hadamard transform).  Arrays of length `count` are host arrays. */
 size_t wq_linear_batch_workspace(int32_t count, const wq_weight *w, int64_t m);
 wq_status wq_linear_batch(int32_t count, const wq_weight *w,
                           const uint16_t *const *x, const int64_t *ldx, int64_t m,

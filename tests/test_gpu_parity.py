@@ -331,6 +331,31 @@ def test_batch_call_matches_single_calls():
         assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("m", [4, 16, 64])
+def test_batch_shared_input_rotated_once(m):
+    # q, k and v quantised with one sign vector and called on one activation
+    # tensor: the call rotates (and arranges) that input once for all three.
+    # The outputs equal those of the same call on three copies of the input,
+    # bit for bit, and the oracle's within tolerance
+    say(f"batch shared input m={m}")
+    rng = np.random.default_rng(90 + m)
+    signs, signs_o = W.sign_bits(2560, rng), W.sign_bits(4096, rng)
+    x, x_o = W.activations(m, 2560, rng), W.activations(m, 4096, rng)
+    sg = dev_u32(signs)
+    qs, refs = [], []
+    for n, k, sb in ((256, 2560, signs), (64, 2560, signs), (64, 2560, signs), (130, 4096, signs_o)):
+        w = W.weight(k, n, rng)
+        q, s_, z = OR.prepare(w, sb, 4)
+        refs.append(OL.linear(q, s_, z, x if k == 2560 else x_o, sb))
+        qs.append(dq.quantize_weight(dev(w), 4, sg if k == 2560 else dev_u32(signs_o)))
+    xd, xo = dev(x), dev(x_o)
+    shared = dq.wq_linear_batch(qs, [xd, xd, xd, xo])
+    copies = dq.wq_linear_batch(qs, [xd, xd.clone(), xd.clone(), xo])
+    for a, b, ref in zip(shared, copies, refs):
+        assert torch.equal(a, b)
+        check_close(a.float().cpu().numpy(), ref, f"shared input m={m}")
+
+
 def test_deterministic_with_uninitialised_workspace():
     # the workspace needs no initialisation: one filled with NaN bit
     # patterns gives the same bits as a zeroed one, call after call
