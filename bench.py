@@ -107,9 +107,9 @@ def kernel_name(bits: int, m: int) -> str:
         return f"gemm_kernel<{bits}> (matrix cores, all linears in one launch), after rht_batch_kernel"
     if m == 1:
         return f"gemv_ring_kernel<{bits}, true> (LDS-ring weight stream)"
-    tile = 2 if m == 2 else (4 if m <= 4 else 8)
-    return (f"gemv_quad_kernel<{bits}, {tile}> (row quads, register prefetch; batch tiles of {tile} rows, "
-            f"4 where 8 rows of activations do not fit in LDS even in K chunks), "
+    tile = 2 if m == 2 else 4 if m <= 4 else 8 if m <= 12 else 16
+    return (f"gemv_quad_kernel<{bits}, {tile}> (row quads, register prefetch; batch tiles of up to {tile} rows "
+            f"where they fit in LDS in up to 4 chunks of K, else smaller), "
             f"after xprep_kernel<{bits}> (activations rotated and arranged once)")
 
 

@@ -116,17 +116,17 @@ constexpr int kMaxLds = 160 * 1024;
 bool plan_stream(int count, const wq_weight *w, int64_t m, bool rotate, int *wg, int *rows_per_wg, int *lds,
                  bool *ring) {
   const int mt = mtile(m);
-  if (w[0].bits == 0 || mt > 8) return false;
+  if (w[0].bits == 0 || mt > 16) return false;
   const int ncu = device_cus();
   if (count > ncu) return false;
   const double round_bytes = rotate ? 8192.0 : 3072.0;
-  const int gran = mt >= 2 ? 4 : 2;   // rows per task: quads at batch tiles 2 to 8, pairs at 1
+  const int gran = mt >= 2 ? 4 : 2;   // rows per task: quads at batch tiles 2 to 16, pairs at 1
   double bytes[WQ_MAX_BATCH], prep[WQ_MAX_BATCH];
   int64_t maxwg[WQ_MAX_BATCH];
   for (int i = 0; i < count; ++i) {
     bytes[i] = (double)w[i].n * (double)w[i].k * (w[i].bits / 8.0 + 4.0 / 128.0);
     const int64_t items = mt * (w[i].k / wq::kGroup);
-    // batch 1 rotates in the workgroup; batch tiles 2 to 8 copy the
+    // batch 1 rotates in the workgroup; batch tiles 2 to 16 copy the
     // arranged activations (80 bytes per 32 elements) from L2
     prep[i] = mt == 1 ? round_bytes * (double)((items + 15) / 16) : 0.625 * (double)(mt * w[i].k);
     maxwg[i] = (w[i].n + gran - 1) / gran;
@@ -202,9 +202,10 @@ void order_by_k(int count, const wq_weight *w, int *order, wq_weight *ws) {
 // One GEMV over `count` linears with batch rows m (<= 16).  Above one row
 // (uniform width) the activations are arranged once into the workspace, then
 // each tile of batch rows is one pass of the row-quad kernel over the
-// weights: 8 rows where the 8 rows' arranged activations (80 bytes per 32
-// elements and row), the row parts and the scales fit in one workgroup's LDS
-// for every linear of the call, else 4.
+// weights: 16 rows (m > 12) or 8 (m > 4) where that many rows' arranged
+// activations (80 bytes per 32 elements and row, in up to 4 chunks of K),
+// the row parts and the scales fit in one workgroup's LDS for every linear
+// of the call, else 4.
 wq_status run_gemv(int count, const wq_weight *w, const uint16_t *const *x, const int64_t *ldx,
                    int64_t m, void *const *y, const wq_dtype *ydt, const int64_t *ldy,
                    bool rotate, void *workspace, hipStream_t s) {
@@ -215,7 +216,13 @@ wq_status run_gemv(int count, const wq_weight *w, const uint16_t *const *x, cons
     wq_weight ws[WQ_MAX_BATCH];
     bool ring = false;
     order_by_k(count, w, order, ws);
-    if (plan_stream(count, ws, 8, rotate, wg, rpw, &lds, &ring)) tile = 8;
+    // 16 rows in one pass only from 13 rows on: below that, a tile of 8 and
+    // one of up to 4 do less arithmetic than 16 rows (the VALU work grows
+    // with the rows a tile computes, valid or not)
+    if (m > 12 && plan_stream(count, ws, 16, rotate, wg, rpw, &lds, &ring))
+      tile = 16;
+    else if (plan_stream(count, ws, 8, rotate, wg, rpw, &lds, &ring))
+      tile = 8;
   }
   // each distinct input arranged once (linears sharing one share its block)
   uint32_t *xq[WQ_MAX_BATCH];
@@ -257,9 +264,9 @@ wq_status run_gemv(int count, const wq_weight *w, const uint16_t *const *x, cons
   return WQ_OK;
 }
 
-// One launch over `count` linears for a batch tile of m <= 8 rows (any m
-// for the tiled kernel).  xq: the tile's arranged activations per linear, or
-// NULL where the kernel rotates for itself.
+// One launch over `count` linears for a batch tile of m <= 16 rows.  xq:
+// the tile's arranged activations per linear, or NULL where the kernel
+// rotates for itself.
 wq_status launch_tile(int count, const wq_weight *w, const uint16_t *const *x, const int64_t *ldx, int64_t m,
                       void *const *y, const wq_dtype *ydt, const int64_t *ldy, bool rotate,
                       const uint32_t *const *xq, hipStream_t s) {

@@ -19,10 +19,10 @@
 //     64-row block of uniform width per workgroup.
 //   * gemv_stream_kernel: batch 1 when the ring does not fit in LDS: codes
 //     prefetched into registers.
-//   * xprep_kernel + gemv_quad_kernel: batch tiles of 2, 4 or 8 rows
-//     (batches up to 16 as tiles of 8, or of 4 where 8 rows of activations
-//     do not fit in LDS): activations rotated and arranged once, then row
-//     quads with register accumulation (section "Batch tiles").
+//   * xprep_kernel + gemv_quad_kernel: batch tiles of 2, 4, 8 or 16 rows
+//     (the host picks the tiles, within what fits in LDS): activations
+//     rotated and arranged once, then row quads with register accumulation
+//     (section "Batch tiles").
 //
 // Tasks.  A lane's unit of work is a 32-code slice of one or more rows in a
 // 512-wide K segment (16 lanes of a DPP row cover the segment).  Every load
@@ -1010,7 +1010,7 @@ __device__ __forceinline__ void stream_ring(const LinDesc &L, const uint32_t *co
 }
 
 // ---------------------------------------------------------------------------
-// Batch tiles (2, 4 or 8 rows): row quads, activations arranged once.
+// Batch tiles (2, 4, 8 or 16 rows): row quads, activations arranged once.
 //
 // With more than one batch row, rotating the activations in every
 // workgroup would cost more than the workgroup's share of the product (each
@@ -1037,8 +1037,8 @@ __device__ __forceinline__ void stream_ring(const LinDesc &L, const uint32_t *co
 //     (one lane pair per value at MT 2), which go to LDS; the p parts of
 //     each row are added in order at the end.
 // 512-thread workgroups (two waves per SIMD) give each lane the registers
-// for the four rows' unpacked codes and the 4 x MT partials.  At MT 8 a
-// lane reads one batch row's slice at a time (at 2 and 4 all of them ahead
+// for the four rows' unpacked codes and the 4 x MT partials.  At MT 8 and 16
+// a lane reads one batch row's slice at a time (at 2 and 4 all of them ahead
 // of the unpack).
 // ---------------------------------------------------------------------------
 
@@ -1058,13 +1058,13 @@ __device__ __forceinline__ void rs_step(float (&v)[N], bool hi) {
   }
 }
 
-// Sum V (8, 16 or 32) values over the 16 lanes of a DPP row.  Lane j ends
-// with the sums of values (V / 16) j .. (V / 16) (j + 1) - 1 in v[0 ..]
-// (V = 32: two values; V = 16: one; V = 8: value j >> 1, lanes j and j ^ 1
-// alike).
+// Sum V (8, 16, 32 or 64) values over the 16 lanes of a DPP row.  Lane j
+// ends with the sums of values (V / 16) j .. (V / 16) (j + 1) - 1 in v[0 ..]
+// (V = 64: four values; 32: two; 16: one; V = 8: value j >> 1, lanes j and
+// j ^ 1 alike).
 template <int V, int N>
 __device__ __forceinline__ void reduce_scatter16(float (&v)[N], int j) {
-  static_assert(V == 8 || V == 16 || V == 32, "4 rows x 2, 4 or 8 batch rows");
+  static_assert(V == 8 || V == 16 || V == 32 || V == 64, "4 rows x 2, 4, 8 or 16 batch rows");
   rs_step<kRowRor8, V>(v, j & 8);
   rs_step<kRowHalfMirror, V / 2>(v, j & 4);
   rs_step<kQuadXor2, V / 4>(v, j & 2);
@@ -1160,9 +1160,9 @@ __device__ __forceinline__ void walk_next(const QuadGeom &g, QuadWalk &w) {
 
 template <int BITS, int MT, int D, bool CHUNKED>
 __device__ __forceinline__ void stream_quads(const LinDesc &L, int m_valid, int r0, int rows, uint32_t *smem) {
-  static_assert(MT == 2 || MT == 4 || MT == 8, "batch tile");
+  static_assert(MT == 2 || MT == 4 || MT == 8 || MT == 16, "batch tile");
   constexpr int ZL = 2;
-  constexpr int XCH = MT <= 4 ? 3 * MT : 16;   // 8 KB copy passes held in registers
+  constexpr int XCH = MT <= 4 ? 3 * MT : MT == 8 ? 16 : 8;   // 8 KB copy passes held in registers
   const int t = threadIdx.x, rg = t >> 4, j = t & 15;
   const int K = L.k, KS = (K + kSeg - 1) / kSeg, G = K / kGroup, S = K / kSlice;
   const int wpr = S * BITS;
@@ -1540,6 +1540,7 @@ hipError_t launch_bits(int mt, const GemvArgs &a, hipStream_t s) {
     case 2: return launch_quad<BITS, 2>(a, s);
     case 4: return launch_quad<BITS, 4>(a, s);
     case 8: return launch_quad<BITS, 8>(a, s);
+    case 16: return launch_quad<BITS, 16>(a, s);
     default:
       return hipErrorInvalidValue;
   }

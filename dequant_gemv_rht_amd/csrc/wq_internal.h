@@ -30,7 +30,7 @@ struct LinDesc {
   const uint32_t *signs;        // nullptr: activations used as given
   union {
     const uint16_t *x;          // the fp16 activations [m][ldx]
-    const uint32_t *xq;         // batch tiles 2, 4, 8: the tile's arranged activations [mt][k/32][20] (xprep)
+    const uint32_t *xq;         // batch tiles 2 to 16: the tile's arranged activations [mt][k/32][20] (xprep)
   };
   void *y;
   int64_t ldx, ldy;
@@ -66,11 +66,11 @@ struct GemvArgs {
 // Host-side launchers (gemv*.hip).  `bits` 0 = mixed.  mt = 1,2,4,8,16.
 hipError_t launch_gemv(int bits, int mt, const GemvArgs &a, hipStream_t s);
 // Persistent stream kernels: one workgroup per CU, uniform code width (or
-// the mixed layout at batch 1), batch tile 1, 2, 4 or 8, the linear's whole
-// rotated K range in LDS.
+// the mixed layout at batch 1), batch tile 1, 2, 4, 8 or 16, the linear's
+// rotated K range in LDS (in up to 4 chunks at batch tiles).
 constexpr int kStreamThreads = 1024;
 hipError_t launch_gemv_stream(int bits, int mt, const GemvArgs &a, hipStream_t s);
-// Batch tiles 2 to 8: one pass arranging every linear's m activation rows
+// Batch tiles 2 to 16: one pass arranging every linear's m activation rows
 // (rotated when signs[i] is set) in the stream kernels' slice layout,
 // out[i] = [m][k/32][20] u32 (80 bytes per 32-element slice).
 hipError_t launch_xprep(int bits, int count, const uint16_t *const *x, const int64_t *ldx,

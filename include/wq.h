@@ -179,8 +179,9 @@ size_t wq_linear_workspace(const wq_weight *w, int64_t m);
  * fp16 in registers before the contraction).  The rotated activations are
  * rounded to fp16 before the product.  Above one batch row the GEMV first
  * rotates and arranges the activations into the workspace in one pass, then
- * streams the weights once per tile of up to 8 batch rows (4 where 8 rows of
- * arranged activations do not fit in a workgroup's LDS in 4 chunks of K).
+ * streams the weights once per tile of batch rows: 16 (13 <= m <= 16), 8
+ * (5 <= m <= 12) or 4, each where that many rows of arranged activations fit
+ * in a workgroup's LDS in up to 4 chunks of K (else the next smaller).
  *   w          host struct describing the device weight
  *   x          fp16 [m][ldx]
  *   y          out: fp16 or fp32 [m][ldy] (y_dtype)
@@ -197,9 +198,9 @@ wq_status wq_linear(const wq_weight *w, const uint16_t *x, int64_t m, int64_t ld
 
 /* Several independent linears (up to WQ_MAX_BATCH), each with its own
  * weight, activations and output, all at the same batch size m and code
- * width.  For m <= 16 they run as one GEMV launch per tile of up to 8 batch
- * rows, or of 4 when one linear's 8 rows of activations do not fit in LDS
- * (after, for m > 1, one launch arranging every linear's activations in the
+ * width.  For m <= 16 they run as one GEMV launch per tile of batch rows
+ * (tiles as for wq_linear, chosen so that every linear's tile fits in LDS;
+ * after, for m > 1, one launch arranging every linear's activations in the
  * workspace).  For m >= 64 with a uniform code width they run as one
  * matrix-core launch (after one launch rotating every linear's
  * activations); the workspace of wq_linear_batch_workspace bytes then holds

@@ -157,11 +157,12 @@ def test_linear_shapes(n, k, rht, out_f32, m):
     _run_case(n, k, m, 4, rht, out_f32, n + k + m)
 
 
-@pytest.mark.parametrize("m", [2, 4, 7])
+@pytest.mark.parametrize("m", [2, 4, 7, 14])
 def test_batch_tiles_k_chunks(m):
     # K = 16384: the arranged activations of a 2-row tile fit in LDS whole,
     # a 4-row tile's (160 KB) in 2 chunks of K, an 8-row tile's in 3; each
-    # workgroup walks its units chunk by chunk
+    # workgroup walks its units chunk by chunk.  16 rows do not fit even in
+    # 4 chunks: m = 14 runs a tile of 8 and one of 6
     say(f"linear K chunks m={m}")
     _run_case(96, 16384, m, 4, True, False, 50 + m)
 
@@ -183,7 +184,7 @@ def test_batch_tiles_few_rows(n):
     _run_case(n, 2560, 4, 4, True, False, 60 + n)
 
 
-@pytest.mark.parametrize("m", [4, 8])
+@pytest.mark.parametrize("m", [4, 8, 16])
 def test_batch_tiles_short_last_workgroup(m):
     # n = 17336 over 256 CUs: 255 workgroups of 68 rows (17 quads, one DPP
     # row each), the last with 64 (16 quads); the last keeps the split of a
@@ -192,11 +193,12 @@ def test_batch_tiles_short_last_workgroup(m):
     _run_case(17336, 1024, m, 4, True, False, 80 + m)
 
 
-@pytest.mark.parametrize("m", [6, 16])
+@pytest.mark.parametrize("m", [6, 13, 16])
 @pytest.mark.parametrize("long_k", [False, True])
-def test_batch_tiles_of_eight(m, long_k):
-    # tiles of 8 batch rows over linears of K 2560 and 4096 (activations
-    # whole in LDS) and 9728 (8 rows take 190 KB: 2 chunks of K) in one call
+def test_batch_tiles_of_eight_and_sixteen(m, long_k):
+    # tiles of 8 (m = 6) and 16 (m = 13, 16) batch rows over linears of K
+    # 2560, 4096 and 9728 in one call: the activations of 8 rows whole in LDS
+    # up to K = 4096 and in 2 chunks at 9728; of 16 rows in 1, 2 and 3 or 4
     shapes = [(256, 2560), (130, 4096)] + ([(64, 9728)] if long_k else [])
     say(f"linear batch tiles m={m} long_k={long_k}")
     qs, xs, refs = [], [], []
