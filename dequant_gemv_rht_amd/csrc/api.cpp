@@ -199,32 +199,27 @@ void order_by_k(int count, const wq_weight *w, int *order, wq_weight *ws) {
   for (int o = 0; o < count; ++o) ws[o] = w[order[o]];
 }
 
-// One GEMV over `count` linears with batch rows m (<= 16).  Above one row
-// (uniform width) the activations are arranged once into the workspace, then
-// each tile of batch rows is one pass of the row-quad kernel over the
-// weights: 16 rows (m > 12) or 8 (m > 4) where that many rows' arranged
-// activations (80 bytes per 32 elements and row, in up to 4 chunks of K),
-// the row parts and the scales fit in one workgroup's LDS for every linear
-// of the call, else 4.
+// One GEMV over `count` linears with batch rows m (< 64; at most 16 for the
+// mixed layout).  Above one row (uniform width) the activations are arranged
+// once into the workspace, then each tile of batch rows is one pass of the
+// row-quad kernel over the weights: 16 rows (from 13 rows left on) or 8
+// (from 5 on) where that many rows' arranged activations (80 bytes per 32
+// elements and row, in up to 4 chunks of K), the row parts and the scales
+// fit in one workgroup's LDS for every linear of the call, else 4.  Below
+// 13 rows a tile of 8 and one of up to 4 compute fewer rows than one of 16.
 wq_status run_gemv(int count, const wq_weight *w, const uint16_t *const *x, const int64_t *ldx,
                    int64_t m, void *const *y, const wq_dtype *ydt, const int64_t *ldy,
                    bool rotate, void *workspace, hipStream_t s) {
   if (!uses_xprep(w[0], m)) return launch_tile(count, w, x, ldx, m, y, ydt, ldy, rotate, nullptr, s);
-  int64_t tile = 4;
+  bool fits16 = false, fits8 = false;
   if (m > 4) {
     int order[WQ_MAX_BATCH], wg[WQ_MAX_BATCH], rpw[WQ_MAX_BATCH], lds = 0;
     wq_weight ws[WQ_MAX_BATCH];
     bool ring = false;
     order_by_k(count, w, order, ws);
-    // 16 rows in one pass only from 13 rows on: below that, a tile of 8 and
-    // one of up to 4 do less arithmetic than 16 rows (the VALU work grows
-    // with the rows a tile computes, valid or not)
-    if (m > 12 && plan_stream(count, ws, 16, rotate, wg, rpw, &lds, &ring))
-      tile = 16;
-    else if (plan_stream(count, ws, 8, rotate, wg, rpw, &lds, &ring))
-      tile = 8;
+    fits16 = m > 12 && plan_stream(count, ws, 16, rotate, wg, rpw, &lds, &ring);
+    fits8 = plan_stream(count, ws, 8, rotate, wg, rpw, &lds, &ring);
   }
-  // each distinct input arranged once (linears sharing one share its block)
   uint32_t *xq[WQ_MAX_BATCH];
   const uint16_t *px[WQ_MAX_BATCH];
   int64_t pld[WQ_MAX_BATCH], kk[WQ_MAX_BATCH];
@@ -252,13 +247,15 @@ wq_status run_gemv(int count, const wq_weight *w, const uint16_t *const *x, cons
   const uint32_t *xt[WQ_MAX_BATCH];
   const uint16_t *xc[WQ_MAX_BATCH];
   void *yc[WQ_MAX_BATCH];
-  for (int64_t m0 = 0; m0 < m; m0 += tile) {
+  for (int64_t m0 = 0, tile = 0; m0 < m; m0 += tile) {
+    const int64_t rem = m - m0;
+    tile = fits16 && rem > 12 ? 16 : fits8 && rem > 4 ? 8 : 4;
     for (int i = 0; i < count; ++i) {
       xt[i] = xq[i] + (size_t)m0 * (size_t)(w[i].k / wq::kSlice) * 20;
       xc[i] = x[i] + m0 * ldx[i];
       yc[i] = static_cast<char *>(y[i]) + (size_t)m0 * (size_t)ldy[i] * (ydt[i] == WQ_F32 ? 4 : 2);
     }
-    st = launch_tile(count, w, xc, ldx, m - m0 < tile ? m - m0 : tile, yc, ydt, ldy, rotate, xt, s);
+    st = launch_tile(count, w, xc, ldx, rem < tile ? rem : tile, yc, ydt, ldy, rotate, xt, s);
     if (st != WQ_OK) return st;
   }
   return WQ_OK;
@@ -446,11 +443,12 @@ wq_status run_gemm(int count, const wq_weight *w, const uint16_t *const *x, cons
   return hip_status(wq::launch_gemm_batch(count, w, xr, ldr, m, yo, f32, ldo, g.ksplit, part, s), who);
 }
 
-// One validated linear: matrix-core path or the GEMV in chunks of 16 batch
-// rows.
+// One validated linear: the matrix-core path, the GEMV over all m rows
+// (uniform width), or the GEMV in chunks of 16 batch rows (mixed width).
 wq_status linear_one(const wq_weight &w, const uint16_t *x, int64_t m, int64_t ldx, void *y, wq_dtype y_dtype,
                      int64_t ldy, bool rotate, void *workspace, hipStream_t s) {
   if (use_gemm(w, m)) return run_gemm(1, &w, &x, &ldx, m, &y, &y_dtype, &ldy, rotate, workspace, s, "wq_linear");
+  if (uses_xprep(w, m)) return run_gemv(1, &w, &x, &ldx, m, &y, &y_dtype, &ldy, rotate, workspace, s);
   const size_t esz = y_dtype == WQ_F32 ? 4 : 2;
   for (int64_t m0 = 0; m0 < m; m0 += 16) {
     const int64_t mc = (m - m0) < 16 ? (m - m0) : 16;
@@ -580,9 +578,8 @@ size_t wq_linear_workspace(const wq_weight *w, int64_t m) {
     return (size_t)-1;
   }
   if (use_gemm(*w, m)) return gemm_path_workspace(*w, m);
-  // the GEMV above one batch row: the arranged activations of a chunk of
-  // up to 16 rows
-  return uses_xprep(*w, m) ? xprep_bytes(w->k, m < 16 ? m : 16) : 0;
+  // the GEMV above one batch row: the arranged activations of all m rows
+  return uses_xprep(*w, m) ? xprep_bytes(w->k, m) : 0;
 }
 
 wq_status wq_linear(const wq_weight *w, const uint16_t *x, int64_t m, int64_t ldx, void *y,
@@ -613,21 +610,17 @@ size_t wq_linear_batch_workspace(int32_t count, const wq_weight *w, int64_t m) {
     return (size_t)-1;
   }
   bool gemm = m > 16;
-  size_t all = 0, largest = 0;
+  size_t all = 0;
   for (int i = 0; i < count; ++i) {
     if (check_weight(&w[i], "wq_linear_batch_workspace") != WQ_OK) return (size_t)-1;
     gemm = gemm && use_gemm(w[i], m) && w[i].bits == w[0].bits;
-    if (uses_xprep(w[i], m)) {
-      all += xprep_bytes(w[i].k, m);
-      const size_t one = xprep_bytes(w[i].k, m < 16 ? m : 16);
-      if (one > largest) largest = one;
-    }
+    if (uses_xprep(w[i], m)) all += xprep_bytes(w[i].k, m);
   }
   // m >= 64 with one uniform width: one matrix-core launch over all of them;
-  // m <= 16: every linear's arranged activations side by side; otherwise
-  // the GEMV in chunks of 16 rows, one linear after another
+  // below: every linear's arranged activations side by side (none for the
+  // mixed layout, whose GEMV needs no workspace)
   if (gemm) return gemm_layout(count, w, m, true).total;
-  return m <= 16 ? all : largest;
+  return all;
 }
 
 wq_status wq_linear_batch(int32_t count, const wq_weight *w, const uint16_t *const *x, const int64_t *ldx,
@@ -655,11 +648,12 @@ wq_status wq_linear_batch(int32_t count, const wq_weight *w, const uint16_t *con
     return fail(WQ_E_WORKSPACE, "wq_linear_batch: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
   if (workspace && !aligned16(workspace))
     return fail(WQ_E_ALIGN, "wq_linear_batch: workspace must be 16-byte aligned");
-  if (m <= 16) return run_gemv(count, w, x, ldx, m, y, y_dtype, ldy, rotate, workspace, (hipStream_t)stream);
   if (use_gemm(w[0], m))   // one width (checked above): all on the matrix cores in one launch
     return run_gemm(count, w, x, ldx, m, y, y_dtype, ldy, rotate, workspace, (hipStream_t)stream,
                     "wq_linear_batch");
-  for (int i = 0; i < count; ++i) {   // mixed width: the GEMV, one linear after another
+  if (m <= 16 || w[0].bits != 0)   // the GEMV: one launch per tile of batch rows over all the linears
+    return run_gemv(count, w, x, ldx, m, y, y_dtype, ldy, rotate, workspace, (hipStream_t)stream);
+  for (int i = 0; i < count; ++i) {   // mixed width above 16 rows: one linear after another
     const wq_status st = linear_one(w[i], x[i], m, ldx[i], y[i], y_dtype[i], ldy[i], rotate, workspace,
                                     (hipStream_t)stream);
     if (st != WQ_OK) return st;

@@ -174,14 +174,15 @@ size_t wq_linear_workspace(const wq_weight *w, int64_t m);
  * set, else x' = x[m].  The scale is applied once per group to the group's
  * partial sum and products accumulate in fp32 (source: "24B0978 - Week 01
  * - Track 2", paragraph on group-wise affine integer quantisation).
- * m <= 16 runs the dequantising GEMV; 17 <= m < 64 runs it in chunks of 16
- * rows; m >= 64 runs the matrix-core GEMM (the weight is dequantised to
- * fp16 in registers before the contraction).  The rotated activations are
- * rounded to fp16 before the product.  Above one batch row the GEMV first
- * rotates and arranges the activations into the workspace in one pass, then
- * streams the weights once per tile of batch rows: 16 (13 <= m <= 16), 8
- * (5 <= m <= 12) or 4, each where that many rows of arranged activations fit
- * in a workgroup's LDS in up to 4 chunks of K (else the next smaller).
+ * m < 64 runs the dequantising GEMV; m >= 64 runs the matrix-core GEMM (the
+ * weight is dequantised to fp16 in registers before the contraction).  The
+ * rotated activations are rounded to fp16 before the product.  Above one
+ * batch row the GEMV first rotates and arranges all m activation rows into
+ * the workspace in one pass, then streams the weights once per tile of batch
+ * rows: 16 while 13 or more rows are left, else 8 while 5 or more are, else
+ * the rest, each where that many rows of arranged activations fit in a
+ * workgroup's LDS in up to 4 chunks of K (else the next smaller).  The mixed
+ * 6/8-bit layout runs its GEMV in chunks of 16 rows without a workspace.
  *   w          host struct describing the device weight
  *   x          fp16 [m][ldx]
  *   y          out: fp16 or fp32 [m][ldy] (y_dtype)
@@ -198,21 +199,21 @@ wq_status wq_linear(const wq_weight *w, const uint16_t *x, int64_t m, int64_t ld
 
 /* Several independent linears (up to WQ_MAX_BATCH), each with its own
  * weight, activations and output, all at the same batch size m and code
- * width.  For m <= 16 they run as one GEMV launch per tile of batch rows
+ * width.  For m < 64 they run as one GEMV launch per tile of batch rows
  * (tiles as for wq_linear, chosen so that every linear's tile fits in LDS;
  * after, for m > 1, one launch arranging every linear's activations in the
  * workspace).  For m >= 64 with a uniform code width they run as one
  * matrix-core launch (after one launch rotating every linear's
  * activations); the workspace of wq_linear_batch_workspace bytes then holds
- * every linear's rotated activations and split-K partial sums.  Otherwise
- * (17 <= m < 64, or the mixed 6/8-bit layout above m = 16) they run one
- * after another on the stream exactly as wq_linear would, sharing the
- * workspace.  Same math and layout as wq_linear, applied to each
- * w[i], x[i], y[i].  In the grouped launches, linears with the same input
- * (x and ldx equal, the same k and the same rht_signs pointer, e.g. query,
- * key and value projections quantised with one sign vector) share one
- * rotation and arrangement of it ("24B0978 - Week 01 - Track 2", paragraph on the random
- * Hadamard transform).  Arrays of length `count` are host arrays. */
+ * every linear's rotated activations and split-K partial sums.  The mixed
+ * 6/8-bit layout above m = 16 runs one linear after another on the stream
+ * exactly as wq_linear would.  Same math and layout as wq_linear, applied to
+ * each w[i], x[i], y[i].  In the grouped launches, linears with the same
+ * input (x and ldx equal, the same k and the same rht_signs pointer, e.g.
+ * query, key and value projections quantised with one sign vector) share
+ * one rotation and arrangement of it ("24B0978 - Week 01 - Track 2",
+ * paragraph on the random Hadamard transform).  Arrays of length `count`
+ * are host arrays. */
 size_t wq_linear_batch_workspace(int32_t count, const wq_weight *w, int64_t m);
 wq_status wq_linear_batch(int32_t count, const wq_weight *w,
                           const uint16_t *const *x, const int64_t *ldx, int64_t m,

@@ -125,11 +125,9 @@ def test_workspace_sizes(lib):
     assert lib.wq_linear_workspace(ctypes.byref(_weight()), 1) == 0
     w = _weight(n=4096, k=2560, rht_signs=16, rht_block=128)
     assert lib.wq_linear_workspace(ctypes.byref(w), 1) == 0
-    # 2..63 rows: the arranged activations of a chunk of up to 16 rows
-    for m in (2, 3, 4, 16):
+    # 2..63 rows: the arranged activations of all m rows
+    for m in (2, 3, 4, 16, 17, 63):
         assert lib.wq_linear_workspace(ctypes.byref(w), m) == _arranged(2560, m)
-    for m in (17, 63):
-        assert lib.wq_linear_workspace(ctypes.byref(w), m) == _arranged(2560, 16)
     # without rotation the activations are still arranged (pair order, sums)
     w_plain = _weight(n=4096, k=2560)
     assert lib.wq_linear_workspace(ctypes.byref(w_plain), 4) == _arranged(2560, 4)
@@ -163,16 +161,16 @@ def test_other_entry_points_reject(lib):
 
 
 def test_batch_workspace_for_large_m(lib):
-    # m = 1: no workspace; 2 <= m <= 16: every linear's arranged activations
-    # side by side; 17 <= m < 64: the largest single linear's chunk; m >= 64:
-    # one matrix-core launch over all the linears, whose workspace holds
-    # every linear's rotated activations (fp16 [m][k]) and the fp32 partial
-    # sums of split K
+    # m = 1: no workspace; 2 <= m < 64: every linear's arranged activations
+    # side by side; m >= 64: one matrix-core launch over all the linears,
+    # whose workspace holds every linear's rotated activations (fp16 [m][k])
+    # and the fp32 partial sums of split K
     sg = dict(rht_signs=16, rht_block=128)
     arr = (dq.WqWeight * 2)(_weight(n=256, k=2560, **sg), _weight(n=128, k=9728, **sg))
     assert lib.wq_linear_batch_workspace(2, arr, 1) == 0
     assert lib.wq_linear_batch_workspace(2, arr, 16) == _arranged(2560, 16) + _arranged(9728, 16)
     assert lib.wq_linear_batch_workspace(2, arr, 5) == _arranged(2560, 5) + _arranged(9728, 5)
+    assert lib.wq_linear_batch_workspace(2, arr, 40) == _arranged(2560, 40) + _arranged(9728, 40)
     need = lib.wq_linear_batch_workspace(2, arr, 512)
     assert need >= 512 * (2560 + 9728) * 2
     assert need >= lib.wq_linear_workspace(ctypes.byref(arr[0]), 512)

@@ -264,10 +264,30 @@ def test_gemm_mixed_width_runs_on_gemv():
     check_close(dq.wq_linear(qw, dev(x)).float().cpu().numpy(), ref, "mixed m=64")
 
 
-@pytest.mark.parametrize("m", [17, 40])
-def test_linear_batch_chunks(m):
-    say(f"linear chunked m={m}")
+@pytest.mark.parametrize("m", [17, 29, 40, 63])
+def test_linear_mid_batch(m):
+    # 17..63 rows: one arrangement of all rows, then tiles of 16, 8 and the
+    # rest (63 = 16 + 16 + 16 + 8 + 4 + 3; 17 = 16 + 1, the last row on the
+    # batch-1 kernel)
+    say(f"linear mid batch m={m}")
     _run_case(96, 512, m, 4, True, False, m)
+    _run_case(300, 2560, m, 3, True, True, m + 1)
+
+
+@pytest.mark.parametrize("m", [20, 40])
+def test_linear_batch_mid_m_grouped(m):
+    # 17..63 rows in one grouped call: every linear's tiles in one launch
+    say(f"batch mid m={m}")
+    shapes = [(256, 2560), (64, 1024), (130, 9728)]
+    qs, xs, refs = [], [], []
+    for i, (n, k) in enumerate(shapes):
+        w, x, signs = _inputs(n, k, m, 140 + i + m)
+        q, s_, z = OR.prepare(w, signs, 4)
+        refs.append(OL.linear(q, s_, z, x, signs))
+        qs.append(_gpu_weight(w, signs, 4))
+        xs.append(dev(x))
+    for (n, k), y, ref in zip(shapes, dq.wq_linear_batch(qs, xs), refs):
+        check_close(y.float().cpu().numpy(), ref, f"batch mid n={n} k={k} m={m}")
 
 
 @pytest.mark.parametrize("bits", [3, 4, 6, 8])
@@ -285,7 +305,7 @@ def test_linear_trained_scales_and_zeros(bits):
     check_close(y.float().cpu().numpy(), ref, "trained s,z")
 
 
-@pytest.mark.parametrize("m", [1, 4])
+@pytest.mark.parametrize("m", [1, 4, 20])
 @pytest.mark.parametrize("rht", [True, False])
 def test_linear_mixed(m, rht):
     say(f"linear mixed m={m} rht={rht}")
