@@ -9,11 +9,15 @@ activations fused into the product, M = 1, fp16 outputs.  The seven
 linears have independent inputs, so one step is a single grouped launch.
 
 Weights are cold: a rotating pool of distinct weight copies (>= 1 GB, well
-above the 256 MB Infinity Cache) is cycled, one copy per step.  Steps are
-replayed from a HIP graph so the host launch path stays out of the timed
-region.  The kernel's own duration per launch is measured with HIP events
-around single launches on the launch stream; the roofline figure is
-algorithmic bytes per launch over that duration.
+above the 256 MB Infinity Cache) is cycled, one copy per step.  The timed
+region is K steps replayed from a HIP graph (so the host launch path stays
+out of it) on one stream, bracketed by HIP events on that stream with a
+synchronisation on both sides; it is replayed 5 times and the median taken
+(replays of the same graph differ by up to ~10% on some hosts).  At M = 1 a
+step is exactly one launch of the GEMV, so the region gives its duration
+per launch, and the roofline figure is algorithmic bytes per launch over
+it.  The same K steps launched eagerly (with the host's time to issue one)
+are printed beside it.
 
 Prints one JSON line on stdout; details go to stderr.
 
@@ -495,7 +499,7 @@ def main():
     stream = torch.cuda.Stream()
     sptr = stream.cuda_stream
 
-    # ---- warmup (eager), then the timed steps from one graph of exactly K steps
+    # ---- warmup, then the timed region: exactly K steps, eager and as a graph
     with torch.cuda.stream(stream):
         for i in range(args.warmup):
             calls[i % copies](sptr)
@@ -513,16 +517,32 @@ def main():
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):
         t0.record(stream)
-        graph.replay()
+        h0 = time.perf_counter()
+        for i in range(args.steps):
+            calls[i % copies](sptr)
+        h1 = time.perf_counter()
         t1.record(stream)
     torch.cuda.synchronize()
-    ms_total = t0.elapsed_time(t1)
-    ms_per_step = ms_total / args.steps
+    eager_ms_per_step = t0.elapsed_time(t1) / args.steps
+    host_ms_per_step = (h1 - h0) * 1e3 / args.steps
 
-    # ---- per-launch duration of the dominant kernel: a step is exactly one
-    # launch of it, so the timed region over K steps gives it directly (events
-    # recorded on the launch stream).  Single eager launches bracketed by
-    # events are reported beside it for context.
+    replays = []
+    for _ in range(5):
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            t0.record(stream)
+            graph.replay()
+            t1.record(stream)
+        torch.cuda.synchronize()
+        replays.append(t0.elapsed_time(t1) / args.steps)
+    graph_ms_per_step = float(np.median(replays))
+    ms_per_step = graph_ms_per_step
+    timing = "HIP graph of the K steps, median of 5 replays"
+
+    # ---- per-launch duration of the dominant kernel: at M = 1 a step is
+    # exactly one launch of it, so the timed region gives it directly (events
+    # recorded on the launch stream).  Single launches bracketed by events
+    # are reported beside it for context.
     launch_ms = ms_per_step
     n_single = max(50, copies * 3)
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_single)]
@@ -535,21 +555,14 @@ def main():
     torch.cuda.synchronize()
     durs = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
 
-    # ---- eager per-step time (no graph) for context
-    with torch.cuda.stream(stream):
-        t0.record(stream)
-        for i in range(args.steps):
-            calls[i % copies](sptr)
-        t1.record(stream)
-    torch.cuda.synchronize()
-    eager_ms_per_step = t0.elapsed_time(t1) / args.steps
-
     gbs = nbytes / (ms_per_step * 1e-3) / 1e9
     achieved = nbytes / (launch_ms * 1e-3) / 1e9
     flops = sum(2 * m * lin.n * lin.k for lin in lins)
     tflops = flops / (ms_per_step * 1e-3) / 1e12
-    log(f"graph: {ms_per_step * 1e3:.2f} us/step = {gbs:.0f} GB/s; eager {eager_ms_per_step * 1e3:.2f} us/step; "
-        f"single eager launch (events) mean {np.mean(durs) * 1e3:.2f} us, p10 {durs[len(durs) // 10] * 1e3:.2f}, "
+    log(f"timed ({timing}): {ms_per_step * 1e3:.2f} us/step = {gbs:.0f} GB/s (replays "
+        f"{', '.join(f'{r * 1e3:.2f}' for r in replays)}); eager {eager_ms_per_step * 1e3:.2f} "
+        f"us/step (host {host_ms_per_step * 1e3:.2f} us to issue one); "
+        f"single launch (events) mean {np.mean(durs) * 1e3:.2f} us, p10 {durs[len(durs) // 10] * 1e3:.2f}, "
         f"p90 {durs[9 * len(durs) // 10] * 1e3:.2f}")
 
     traffic = None
@@ -580,11 +593,14 @@ def main():
             "workload": wl.title + f", M={m}",
             "m": m, "bits": bits, "group": 128, "linears": len(lins),
             "algorithmic_bytes_per_step": nbytes,
-            "launch": "one grouped launch per step (7 independent linears), replayed from a HIP graph",
+            "launch": "one grouped launch per step (7 independent linears), back to back on one stream from a HIP graph",
+            "timing": timing,
             "weight_pool": f"{copies} copies, {copies * weight_bytes / 1e9:.2f} GB (cold weights)",
         },
         "us_per_linear": round(ms_per_step * 1e3 / len(lins), 4),
         "eager_us_per_step": round(eager_ms_per_step * 1e3, 3),
+        "graph_us_per_step": round(graph_ms_per_step * 1e3, 3),
+        "host_us_per_step": round(host_ms_per_step * 1e3, 3),
         "frac_of_peak_hbm": round(gbs / PEAK_HBM_GBS, 4),
         "roofline": {
             "bound": "hbm",
