@@ -12,8 +12,9 @@ Weights are cold: a rotating pool of distinct weight copies (>= 1 GB, well
 above the 256 MB Infinity Cache) is cycled, one copy per step.  The timed
 region is K steps replayed from a HIP graph (so the host launch path stays
 out of it) on one stream, bracketed by HIP events on that stream with a
-synchronisation on both sides; it is replayed 5 times and the median taken
-(replays of the same graph differ by up to ~10% on some hosts).  At M = 1 a
+synchronisation on both sides; after 9 untimed replays (graph upload, and
+the clocks settling) it is replayed 5 times and the median taken (replays
+of the same graph differ by up to ~10% on some hosts).  At M = 1 a
 step is exactly one launch of the GEMV, so the region gives its duration
 per launch, and the roofline figure is algorithmic bytes per launch over
 it.  The same K steps launched eagerly (with the host's time to issue one)
@@ -510,6 +511,10 @@ def main():
             calls[i % copies](sptr)
     with torch.cuda.stream(stream):
         graph.replay()                      # untimed replay: graph upload
+        # more untimed replays, ~20 ms of work at M = 1: the clocks settle
+        # (the first replays after idle run a few percent slower)
+        for _ in range(8):
+            graph.replay()
     torch.cuda.synchronize()
 
     t0 = torch.cuda.Event(enable_timing=True)
