@@ -165,7 +165,8 @@ def _pool_views(t, copies: int):
 
 def _time_launches(fns, stream, min_launches: int = 200, replays: int = 3) -> float:
     """Mean µs per launch over a graph of back-to-back launches cycling through
-    ``fns`` (each call launches once on ``stream``); median over replays."""
+    ``fns`` (each call launches once on ``stream``); median over replays,
+    after untimed replays that let the clocks settle."""
     import torch
     k = max(min_launches, len(fns))
     sptr = stream.cuda_stream
@@ -181,7 +182,13 @@ def _time_launches(fns, stream, min_launches: int = 200, replays: int = 3) -> fl
     t1 = torch.cuda.Event(enable_timing=True)
     times = []
     with torch.cuda.stream(stream):
+        # untimed replays, about 20 ms of work, so the clocks settle first
+        t0.record(stream)
         g.replay()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        for _ in range(min(50, int(20.0 / max(t0.elapsed_time(t1), 1e-3)))):
+            g.replay()
         for _ in range(replays):
             t0.record(stream)
             g.replay()
