@@ -107,12 +107,14 @@ constexpr int kMaxLds = 160 * 1024;
 // Persistent stream kernel plan: workgroups (one per CU) split among the
 // linears so that their estimated times match; each gets an even number of
 // rows.  A workgroup's time is its weight bytes plus its activation
-// preparation, which it does before any weight can be used: each SIMD
-// (4 waves of 4 16-lane rows) takes ceil(items / 16) rounds over the
-// linear's 128-blocks (times the batch tile), about 0.25 us per round with
-// the rotation (~185 vector instructions per block), which is what a CU
-// streams of weights in that time (~32 KB/us): 8 KB per round; without the
-// rotation ~70 instructions, 3 KB.
+// preparation, which it does before any weight can be used: rounds of
+// ceil(items / 16) over the linear's 128-blocks (times the batch tile), as
+// for 16-lane rows of 4 waves per SIMD, about 0.25 us per round with the
+// rotation (~185 vector instructions per block), which is what a CU streams
+// of weights in that time (~32 KB/us): 8 KB per round; without the rotation
+// ~70 instructions, 3 KB.  (The batch-1 rings of 3- and 4-bit codes run 2
+// waves per SIMD; the estimate is kept, as the balance it gives was measured
+// best for them too.)
 bool plan_stream(int count, const wq_weight *w, int64_t m, bool rotate, int *wg, int *rows_per_wg, int *lds,
                  bool *ring) {
   const int mt = mtile(m);

@@ -591,6 +591,10 @@ struct Ring {
   static constexpr int slot = codes + 2 * 64 * 4;                   // + scales, zeros
   static constexpr int depth = BITS == 3 ? 4 : BITS == 4 ? 3 : 2;  // steps in flight
   static constexpr int q = (flat ? ni : 2 * nc) + 2;               // vector loads per wave per step
+  // workgroup size: 8 waves for the narrow codes (their steps are short and
+  // a smaller workgroup starts sooner), 16 for int6 and int8
+  static constexpr int threads = (BITS == 3 || BITS == 4) ? 512 : 1024;
+  static constexpr int waves = threads / 64;
 };
 
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
@@ -630,7 +634,7 @@ struct RingCursor {
 
   template <int D>
   __device__ __forceinline__ void issue() {
-    const uint32_t slot = slot0 + D * (kStreamThreads / 64) * RS::slot;
+    const uint32_t slot = slot0 + D * RS::waves * RS::slot;
     if constexpr (RS::flat) {
 #if defined(__HIP_DEVICE_COMPILE__)
 #pragma unroll
@@ -673,12 +677,12 @@ struct RingLds {
   int xs, part, ring, total;
 };
 
-__host__ __device__ inline RingLds ring_lds(int S, int KS, int np, int slot, int depth) {
+__host__ __device__ inline RingLds ring_lds(int S, int KS, int np, int slot, int depth, int waves) {
   RingLds l;
   l.xs = S * kSliceStride * 4;                      // activations: [S][20] u32, sums in words 16, 17
   l.part = l.xs;                                    // partials: [2np][KS] f32
   l.ring = (l.part + 2 * np * KS * 4 + 15) & ~15;
-  l.total = l.ring + depth * (kStreamThreads / 64) * slot;
+  l.total = l.ring + depth * waves * slot;
   return l;
 }
 
@@ -829,17 +833,18 @@ __device__ __forceinline__ void stream_ring(const LinDesc &L, const uint32_t *co
                                             uint32_t *smem) {
   using RS = Ring<BITS>;
   constexpr int R = RS::depth, Q = RS::q;
+  constexpr int TH = RS::threads, RG = TH / 16;   // threads, DPP rows
   constexpr int XC = 2;
   const int t = threadIdx.x, rg = t >> 4, j = t & 15, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int K = L.k, KS = (K + kSeg - 1) / kSeg, G = K / kGroup, S = K / kSlice;
   const int wpr = S * BITS;
   const int NP = (rows + 1) >> 1, T = NP * KS;
-  const RingLds lay = ring_lds(S, KS, NP, RS::slot, R);
+  const RingLds lay = ring_lds(S, KS, NP, RS::slot, R, RS::waves);
   uint8_t *lds = reinterpret_cast<uint8_t *>(smem);
   uint32_t *xp = smem;
   float *part = reinterpret_cast<float *>(lds + lay.part);
-  const int steps = (T + kRG - 1) / kRG;   // steps of this workgroup (uniform)
+  const int steps = (T + RG - 1) / RG;   // steps of this workgroup (uniform)
   const int nb = K / kGroup, items = nb;
 
   // 1. activations and signs first: loads complete in order, so activations
@@ -853,7 +858,7 @@ __device__ __forceinline__ void stream_ring(const LinDesc &L, const uint32_t *co
   uint32_t sw[XC];
 #pragma unroll
   for (int q = 0; q < XC; ++q) {
-    const int it = rg + kRG * q;
+    const int it = rg + RG * q;
     const bool ok = it < items;
     xr[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, ok ? (uint32_t)(256 * it + 16 * j) : kOOB, 0, 0));
     sw[q] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsg, ok ? (uint32_t)(16 * it + 4 * (j >> 2)) : kOOB, 0, 0);
@@ -866,7 +871,7 @@ __device__ __forceinline__ void stream_ring(const LinDesc &L, const uint32_t *co
   //    zeros, no traffic), which keeps the compiler's wait for the
   //    activations exact (it counts the stream's loads as younger).
   const int cp0 = (int)(__umul24((uint32_t)rg, (uint32_t)L.ks_inv) >> 16), cs0 = rg - cp0 * KS;
-  const int dp = (kRG * L.ks_inv) >> 16, ds = kRG - dp * KS;
+  const int dp = (RG * L.ks_inv) >> 16, ds = RG - dp * KS;
   RingCursor<BITS> cur;
   {
     const uint32_t row_bytes = (uint32_t)wpr * 4, pair_bytes = 2 * row_bytes;
@@ -913,9 +918,9 @@ __device__ __forceinline__ void stream_ring(const LinDesc &L, const uint32_t *co
 #pragma unroll
   for (int q = 0; q < XC; ++q) {
     consume(xr[q], sw[q]);
-    rotate_item<BITS, 1, true>(rotate, xr[q], sw[q], nb, items, rg + kRG * q, j, xp, nullptr, S);
+    rotate_item<BITS, 1, true>(rotate, xr[q], sw[q], nb, items, rg + RG * q, j, xp, nullptr, S);
   }
-  for (int it0 = kRG * XC; it0 < items; it0 += kRG) {
+  for (int it0 = RG * XC; it0 < items; it0 += RG) {
     const int it = it0 + rg;
     const bool ok = it < items;
     const u32x4 raw = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, ok ? (uint32_t)(256 * it + 16 * j) : kOOB, 0, 0));
@@ -941,14 +946,14 @@ __device__ __forceinline__ void stream_ring(const LinDesc &L, const uint32_t *co
   const uint32_t sza_l = cur.slot0 + RS::codes + (lane & 48) * 4 + (j >> 2) * 4;
   const uint32_t ca16_l = cur.slot0 + lane * 16;
   const uint32_t ca4_l = cur.slot0 + (uint32_t)((lane >> 4) * (64 * BITS) + j * (4 * BITS));   // flat layouts
-  constexpr uint32_t kStage = (kStreamThreads / 64) * RS::slot;   // bytes between ring stages
+  constexpr uint32_t kStage = (TH / 64) * RS::slot;   // bytes between ring stages
   // one step i in ring slot D (a compile-time constant, so slot addresses fold)
   auto step = [&](auto dconst, int i) {
     constexpr int d = decltype(dconst)::value;
     {
       // wait for step i; the loads of steps i+1 .. min(i+R, steps)-1 may stay in flight
       wait_vmcnt_younger<R, Q>(min(R - 1, steps - 1 - i));
-      if (rg + kRG * i < T) {
+      if (rg + RG * i < T) {
         const bool sv = FULL || cs * 16 + j < S;
         TaskOps o;
         uint32_t cw[2][BITS];
@@ -1002,7 +1007,7 @@ __device__ __forceinline__ void stream_ring(const LinDesc &L, const uint32_t *co
   __syncthreads();
 
   // 4. add each row's partials in segment order, store
-  for (int e = t; e < rows; e += kStreamThreads) {
+  for (int e = t; e < rows; e += TH) {
     float sum = 0.f;
     for (int s = 0; s < KS; ++s) sum += part[e * KS + s];
     store_out(L, 0, r0 + e, sum);
@@ -1437,7 +1442,7 @@ __global__ __launch_bounds__(256) void xprep_kernel(XprepBatch a) {
 }
 
 template <int BITS, bool FULL>
-__global__ __launch_bounds__(kStreamThreads) void gemv_ring_kernel(GemvArgs a) {
+__global__ __launch_bounds__(Ring<BITS>::threads) void gemv_ring_kernel(GemvArgs a) {
   extern __shared__ uint32_t smem[];
   const int w = blockIdx.x;
   const LinDesc L = fetch_desc(a, w);
@@ -1474,6 +1479,7 @@ __global__ __launch_bounds__(kStreamThreads) void gemv_stream_kernel(GemvArgs a)
 // a compute unit has).
 template <bool FULL>
 __global__ __launch_bounds__(kStreamThreads) void gemv_ring_mixed_kernel(GemvArgs a) {
+  static_assert(Ring<6>::threads == kStreamThreads, "the 6-bit ring runs in this kernel's workgroup");
   extern __shared__ uint32_t smem[];
   const int w = blockIdx.x;
   const LinDesc L = fetch_desc(a, w);
@@ -1528,9 +1534,9 @@ hipError_t launch_bits(int mt, const GemvArgs &a, hipStream_t s) {
     bool full = true;
     for (int i = 0; i < a.count; ++i) full = full && a.lin[i].k % kSeg == 0;
     if (full)
-      hipLaunchKernelGGL((gemv_ring_kernel<BITS, true>), dim3(a.tiles), dim3(kStreamThreads), a.lds_bytes, s, a);
+      hipLaunchKernelGGL((gemv_ring_kernel<BITS, true>), dim3(a.tiles), dim3(Ring<BITS>::threads), a.lds_bytes, s, a);
     else
-      hipLaunchKernelGGL((gemv_ring_kernel<BITS, false>), dim3(a.tiles), dim3(kStreamThreads), a.lds_bytes, s, a);
+      hipLaunchKernelGGL((gemv_ring_kernel<BITS, false>), dim3(a.tiles), dim3(Ring<BITS>::threads), a.lds_bytes, s, a);
     return hipGetLastError();
   }
   switch (mt) {
@@ -1558,14 +1564,14 @@ int gemv_stream_lds_bytes(int bits, int mt, int64_t k, int rows_per_wg, bool rin
   if (mt != 1) return 1 << 30;
   switch (bits) {
     case 0: {   // mixed 6/8: room for the 6-bit ring and the 8-bit stream
-      const int l6 = ring_lds((int)S, (int)KS, (int)np, Ring<6>::slot, Ring<6>::depth).total;
+      const int l6 = ring_lds((int)S, (int)KS, (int)np, Ring<6>::slot, Ring<6>::depth, Ring<6>::waves).total;
       const int l8 = stream_lds(1, (int)S, (int)KS, (int)G, (int)np).total * 4;
       return l6 > l8 ? l6 : l8;
     }
-    case 3: return ring_lds((int)S, (int)KS, (int)np, Ring<3>::slot, Ring<3>::depth).total;
-    case 4: return ring_lds((int)S, (int)KS, (int)np, Ring<4>::slot, Ring<4>::depth).total;
-    case 6: return ring_lds((int)S, (int)KS, (int)np, Ring<6>::slot, Ring<6>::depth).total;
-    case 8: return ring_lds((int)S, (int)KS, (int)np, Ring<8>::slot, Ring<8>::depth).total;
+    case 3: return ring_lds((int)S, (int)KS, (int)np, Ring<3>::slot, Ring<3>::depth, Ring<3>::waves).total;
+    case 4: return ring_lds((int)S, (int)KS, (int)np, Ring<4>::slot, Ring<4>::depth, Ring<4>::waves).total;
+    case 6: return ring_lds((int)S, (int)KS, (int)np, Ring<6>::slot, Ring<6>::depth, Ring<6>::waves).total;
+    case 8: return ring_lds((int)S, (int)KS, (int)np, Ring<8>::slot, Ring<8>::depth, Ring<8>::waves).total;
   }
   return 1 << 30;
 }
