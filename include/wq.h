@@ -163,10 +163,10 @@ wq_status rht_apply(const uint16_t *x, uint16_t *y, const uint32_t *signs,
 
 /* Bytes of workspace wq_linear needs for this weight and batch size m.
  * 0 means none is needed: m = 1, or the mixed 6/8-bit layout below m = 64.
- * For 2 <= m < 64 with one code width it is the arranged activations of up
- * to 16 batch rows (80 bytes per 32 elements per row); for m >= 64 the
- * matrix-core path's rotated activations and split-K partials.  Returns
- * (size_t)-1 for an invalid request. */
+ * For 2 <= m < 64 with one code width it is the arranged activations of all
+ * m batch rows (80 bytes per 32 elements per row, rounded up to 256 bytes);
+ * for m >= 64 the matrix-core path's rotated activations and split-K
+ * partials.  Returns (size_t)-1 for an invalid request. */
 size_t wq_linear_workspace(const wq_weight *w, int64_t m);
 
 /* The layer: y[m][n] = sum_k (q[n][k] - z[n][g]) * s[n][g] * x'[m][k],
