@@ -107,12 +107,15 @@ def test_block_int6():
     _block("block_int6_head_int8", 1)
 
 
-def test_head_int8_fp32_logits():
-    say("head int8 151936x2560 m=1 fp32 out, no rotation")
+@pytest.mark.parametrize("m", [1, 4])
+def test_head_int8_fp32_logits(m):
+    # m = 1 is the configured case; m = 4 runs the head on the batch tiles
+    # (594 rows per workgroup, fp32 outputs)
+    say(f"head int8 151936x2560 m={m} fp32 out, no rotation")
     wl = W.WORKLOADS["block_int6_head_int8"]
     idx = len(wl.linears) - 1
     lin = wl.linears[idx]
-    w, x, _, _ = W.linear_inputs(SEED, wl.wid, idx, lin, 1)
+    w, x, _, _ = W.linear_inputs(SEED, wl.wid, idx, lin, m)
     qw = dq.quantize_weight(dev(w), 8, None)
     y = dq.wq_linear(qw, dev(x), torch.float32, fuse_rht=False)
     torch.cuda.synchronize()
