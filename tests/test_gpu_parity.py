@@ -167,6 +167,14 @@ def test_batch_tiles_k_chunks(m):
     _run_case(96, 16384, m, 4, True, False, 50 + m)
 
 
+@pytest.mark.parametrize("k,m", [(16512, 4), (16512, 7), (9856, 16)])
+def test_batch_tiles_k_chunks_ragged_tail(k, m):
+    # K not a multiple of 512: the last segment holds 4 of 16 slices and
+    # falls in the last chunk of K (2, 3 and 3 chunks here)
+    say(f"linear K chunks, ragged K={k} m={m}")
+    _run_case(96, k, m, 4, True, False, 70 + m)
+
+
 @pytest.mark.parametrize("m", [4, 7])
 def test_batch_tiles_long_k_fall_back(m):
     # K = 65536: a 4-row tile's activations do not fit in LDS even in 4
