@@ -282,7 +282,7 @@ def test_linear_mid_batch(m):
     _run_case(300, 2560, m, 3, True, True, m + 1)
 
 
-@pytest.mark.parametrize("m", [20, 40])
+@pytest.mark.parametrize("m", [20, 40, 63])
 def test_linear_batch_mid_m_grouped(m):
     # 17..63 rows in one grouped call: every linear's tiles in one launch
     say(f"batch mid m={m}")
