@@ -34,14 +34,19 @@
 // Unpacking.  A code pair becomes two fp16 values with one v_and_or_b32
 // against 1024.0's bit pattern; codes that sit at bit s of a 16-bit half are
 // used in place, reading as 1024 + 2^s q, and the activations they meet are
-// stored pre-multiplied by 2^-s (exact in fp16).  int8 uses one v_perm_b32
-// per pair.  The offsets are removed with two per-slice activation sums: X
-// (the sum of the values meant, for the zero point) and XS (1024 times the
-// sum of the values stored, for the 1024 offsets).
+// stored pre-multiplied by 2^-s.  int8 uses one v_perm_b32 per pair.  The
+// offsets are removed with two per-slice activation sums: X (the sum of the
+// values meant, for the zero point) and XS (1024 times the sum of the values
+// stored, for the 1024 offsets).  The stored activations also carry a power
+// of two 2^E that puts their largest magnitude (per 128-block at batch 1,
+// per batch row in the batch tiles) in [2^14, 2^15), so no value becomes an
+// fp16 subnormal through the 2^-s factors, whatever the activations' scale;
+// the partials are multiplied by 2^-E before blocks of different E meet.
 //
 // LDS layout.  Each 32-code activation slice occupies 80 bytes (64 of pairs,
-// the two sums, 8 spare): with that stride the 16 lanes of a DPP row
-// reading their slices with ds_read_b128 hit 16 distinct 4-bank groups.
+// the two sums, the factor 2^-E, 4 spare): with that stride the 16 lanes of
+// a DPP row reading their slices with ds_read_b128 hit 16 distinct 4-bank
+// groups.
 #include "wq_internal.h"
 
 #include <climits>
@@ -98,7 +103,8 @@ struct UnpackConsts {
 // one code in each 16-bit half of a 32-bit window of the packed bits, in
 // place, and 1024.0's exponent is OR-ed in.  A code sitting at bit s of its
 // half (s + bits <= 10) reads as 1024 + 2^s q, so the activation it meets is
-// stored pre-multiplied by 2^-s (exact in fp16 barring underflow).  Windows
+// stored pre-multiplied by 2^-s (exact: the activation exponent keeps the
+// stored values normal fp16 numbers).  Windows
 // are the packed words themselves or funnel shifts of two of them.
 //   int4: word i: (codes 8i+r, 8i+r+4) at s = 0 (r = 0, 2) or 4 (r = 1, 3),
 //         r = 2, 3 from the word shifted right by 8.
@@ -272,16 +278,45 @@ __device__ __forceinline__ u32x4 load8_h(rsrc_t rs, int e0, int n) {
 
 // Rotate one item into LDS.  Only DPP rows that hold an item do any work
 // (the branch is uniform across the 16 lanes of a row).
-// With SUMS_IN_SLICE the two slice sums go into the slice's spare bytes
-// (words 16 and 17 of its 20), so one LDS address serves both.
+//
+// Activation scale.  The stored values are x' 2^E (and 2^-s on top where a
+// code is read in place at bit s), with E chosen from the largest |x'| of
+// the block (or of the batch row, in the batch-tile pre-pass) so that this
+// maximum lands in [2^14, 2^15): whatever the activations' magnitude, the
+// fp16 values are normal numbers well clear of overflow, and the
+// in-place factors 2^-s (down to 2^-7) cost no precision.  The slice keeps
+// 2^-E as an fp32 in word 18, and the consumer multiplies a partial by it
+// once the partial no longer mixes blocks of different E (exact: a power
+// of two).
+//
+// Slice words: 0..15 the fp16 pairs, 16 the sum X of the values meant (for
+// the zero point), 17 1024 times the sum XS of the values stored (for the
+// 1024 offsets), 18 the factor 2^-E, 19 spare.
+
+// E for a largest magnitude mx: mx 2^E in [2^14, 2^15) (0 for mx = 0).
+__device__ __forceinline__ int act_exponent(float mx) {
+  return mx > 0.f ? 15 - __builtin_amdgcn_frexp_expf(mx) : 0;
+}
+
+__device__ __forceinline__ float absmax8(const float (&v)[8]) {
+  float a = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fabsf(v[2]));
+  float b = fmaxf(fmaxf(fabsf(v[3]), fabsf(v[4])), fabsf(v[5]));
+  return fmaxf(fmaxf(a, b), fmaxf(fabsf(v[6]), fabsf(v[7])));
+}
+
+// Largest value over the 16 lanes of a DPP row; every lane gets it.
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp<kQuadXor1>(v));
+  v = fmaxf(v, dpp<kQuadXor2>(v));
+  v = fmaxf(v, dpp<kRowHalfMirror>(v));
+  return fmaxf(v, dpp<kRowMirror>(v));
+}
+
 // Lane jj's eight activations of a 128-block (element kk = 128 b + 8 jj
-// onwards): signs, butterflies and 1/sqrt(128) when rotating, then fp16
-// pairs in dot order and the two slice sums (summed over the 4 lanes of the
-// slice).
-template <int BITS>
-__device__ __forceinline__ void arrange8(bool rotate, u32x4 raw, uint32_t sword, int kk, int jj, uint32_t (&o)[4],
-                                         float &xe, float &xt) {
-  float v[8];
+// onwards) as fp32, with the signs and the butterflies applied when
+// rotating (unscaled: each lane's values carry the sign (-1)^popcount(jj)
+// and the factor sqrt(128), removed by rot_scale).
+__device__ __forceinline__ void load_rotated8(bool rotate, u32x4 raw, uint32_t sword, int kk, int jj, float (&v)[8]) {
   v[0] = half_bits_to_float(raw.x & 0xFFFF); v[1] = half_bits_to_float(raw.x >> 16);
   v[2] = half_bits_to_float(raw.y & 0xFFFF); v[3] = half_bits_to_float(raw.y >> 16);
   v[4] = half_bits_to_float(raw.z & 0xFFFF); v[5] = half_bits_to_float(raw.z >> 16);
@@ -291,10 +326,21 @@ __device__ __forceinline__ void arrange8(bool rotate, u32x4 raw, uint32_t sword,
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = ((sb >> e) & 1u) ? -v[e] : v[e];
     fwht128_row16_signed(v, jj);
-    const float sc = fwht_lane_sign(jj) * kInvSqrt128;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] *= sc;
   }
+}
+
+// What turns load_rotated8's values into x' (magnitudes: 1/sqrt(128) or 1).
+__device__ __forceinline__ float rot_scale(bool rotate) { return rotate ? kInvSqrt128 : 1.0f; }
+
+// The values of load_rotated8 stored for the dot products with exponent E:
+// fp16 pairs in dot order and the two slice sums (summed over the 4 lanes
+// of the slice).
+template <int BITS>
+__device__ __forceinline__ void arrange8(bool rotate, float (&v)[8], int jj, int E, uint32_t (&o)[4], float &xe,
+                                         float &xt) {
+  const float sc = __builtin_amdgcn_ldexpf(rotate ? fwht_lane_sign(jj) * kInvSqrt128 : 1.0f, E);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] *= sc;
   pairs_in_dot_order<BITS>(v, o, xe, xt);
   xe += dpp<kQuadXor1>(xe);
   xe += dpp<kQuadXor2>(xe);
@@ -302,28 +348,33 @@ __device__ __forceinline__ void arrange8(bool rotate, u32x4 raw, uint32_t sword,
   xt += dpp<kQuadXor2>(xt);
 }
 
-template <int BITS, int MT, bool SUMS_IN_SLICE = false>
+// One slice's four lanes: their pairs, and (lane 0 of the four) the sums
+// and the factor 2^-E in words 16..18.
+__device__ __forceinline__ void store_slice_part(uint32_t *slice, int jj, const uint32_t (&o)[4], float xe, float xt,
+                                                 int E) {
+  *reinterpret_cast<u32x4 *>(slice + 4 * (jj & 3)) = u32x4{o[0], o[1], o[2], o[3]};
+  if ((jj & 3) == 0)
+    *reinterpret_cast<u32x4 *>(slice + 16) =
+        u32x4{__builtin_bit_cast(uint32_t, xe), __builtin_bit_cast(uint32_t, 1024.0f * xt),
+              __builtin_bit_cast(uint32_t, __builtin_amdgcn_ldexpf(1.0f, -E)), 0u};
+}
+
+// Item it (batch row m, block b) of a batch-1 or stream workgroup into its
+// LDS slices [m][S][20], with the block's own exponent.
+template <int BITS, int MT>
 __device__ __forceinline__ void rotate_item(bool rotate, u32x4 raw, uint32_t sword, int nb, int items, int it,
-                                            int jj, uint32_t *xp, float *xs, int S) {
+                                            int jj, uint32_t *xp, int S) {
   if (it >= items) return;
   int m, b;
   item_mb<MT>(it, nb, m, b);
   const int kk = 128 * b + 8 * jj;
+  float v[8];
+  load_rotated8(rotate, raw, sword, kk, jj, v);
+  const int E = act_exponent(row16_max(absmax8(v)) * rot_scale(rotate));
   uint32_t o[4];
   float xe, xt;
-  arrange8<BITS>(rotate, raw, sword, kk, jj, o, xe, xt);
-  const int slice = 4 * b + (jj >> 2);
-  *reinterpret_cast<u32x4 *>(&xp[(m * S + slice) * kSliceStride + 4 * (jj & 3)]) = u32x4{o[0], o[1], o[2], o[3]};
-  if ((jj & 3) == 0) {
-    if constexpr (SUMS_IN_SLICE) {
-      float *sums = reinterpret_cast<float *>(&xp[(m * S + slice) * kSliceStride + 16]);
-      sums[0] = xe;
-      sums[1] = 1024.0f * xt;
-    } else {
-      xs[2 * (m * S + slice)] = xe;
-      xs[2 * (m * S + slice) + 1] = 1024.0f * xt;
-    }
-  }
+  arrange8<BITS>(rotate, v, jj, E, o, xe, xt);
+  store_slice_part(&xp[(m * S + 4 * b + (jj >> 2)) * kSliceStride], jj, o, xe, xt, E);
 }
 
 // Code loads of task (row pair p, segment s): rows 2p and 2p+1, this lane's
@@ -345,8 +396,8 @@ struct StreamLds {
 
 __host__ __device__ inline StreamLds stream_lds(int mt, int S, int KS, int G, int np) {
   StreamLds l;
-  l.xs = mt * S * kSliceStride;                  // activations: [mt][S][20]
-  l.part = l.xs + mt * S * 2;                    // slice sums: [mt][S][2]
+  l.xs = mt * S * kSliceStride;                  // activations: [mt][S][20], sums and factor in words 16..18
+  l.part = l.xs;
   l.szl = (l.part + 2 * np * KS * mt + 3) & ~3;  // partials: [2np][KS][mt]
   l.total = l.szl + ((2 * np * G + 7) & ~7) * 2; // scale, zero as fp32: [2np][G][2]
   return l;
@@ -364,7 +415,6 @@ __device__ __forceinline__ void stream_rows(const LinDesc &L, const uint32_t *co
   const bool full = (K % kSeg) == 0;        // every lane's slice exists in every segment
   const StreamLds lay = stream_lds(MT, S, KS, G, NP);
   uint32_t *xp = smem;
-  float *xs = reinterpret_cast<float *>(smem + lay.xs);
   float *part = reinterpret_cast<float *>(smem + lay.part);
   float *szl = reinterpret_cast<float *>(smem + lay.szl);
 
@@ -442,13 +492,13 @@ __device__ __forceinline__ void stream_rows(const LinDesc &L, const uint32_t *co
                       half_bits_to_float(av[h] >> 16), half_bits_to_float(bv[h] >> 16));
   }
 #pragma unroll
-  for (int q = 0; q < XC; ++q) rotate_item<BITS, MT>(rotate, xr[q], sw[q], nb, items, rg + kRG * q, j, xp, xs, S);
+  for (int q = 0; q < XC; ++q) rotate_item<BITS, MT>(rotate, xr[q], sw[q], nb, items, rg + kRG * q, j, xp, S);
   for (int it0 = kRG * XC; it0 < items; it0 += kRG) {
     uint32_t xo, so;
     item_offsets<MT>(L, nb, items, it0 + rg, j, xo, so);
     const u32x4 raw = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, xo, 0, 0));
     const uint32_t w1 = rotate ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsg, so, 0, 0) : 0u;
-    rotate_item<BITS, MT>(rotate, raw, w1, nb, items, it0 + rg, j, xp, xs, S);
+    rotate_item<BITS, MT>(rotate, raw, w1, nb, items, it0 + rg, j, xp, S);
   }
   __syncthreads();
 
@@ -485,13 +535,14 @@ __device__ __forceinline__ void stream_rows(const LinDesc &L, const uint32_t *co
               const u32x4 v = src[q];
               xv[4 * q + 0] = v.x; xv[4 * q + 1] = v.y; xv[4 * q + 2] = v.z; xv[4 * q + 3] = v.w;
             }
-            const float2 xq = *reinterpret_cast<const float2 *>(&xs[2 * (m * S + sl)]);
+            // the slice's sums X and 1024 XS, and its factor 2^-E
+            const float4 xq = *reinterpret_cast<const float4 *>(&xp[(m * S + sl) * kSliceStride + 16]);
 #pragma unroll
             for (int r = 0; r < 2; ++r) {
               float dd = 0.f;
 #pragma unroll
               for (int q = 0; q < 16; ++q) dd = dot2(pr[r][q], xv[q], dd);
-              acc[r][m] = sf[r] * fmaf(-zf[r], xq.x, dd - xq.y);
+              acc[r][m] = (sf[r] * xq.z) * fmaf(-zf[r], xq.x, dd - xq.y);
             }
           }
         } else {
@@ -509,11 +560,11 @@ __device__ __forceinline__ void stream_rows(const LinDesc &L, const uint32_t *co
                 const u32x4 v = src[q];
                 xv[4 * q + 0] = v.x; xv[4 * q + 1] = v.y; xv[4 * q + 2] = v.z; xv[4 * q + 3] = v.w;
               }
-              const float2 xq = *reinterpret_cast<const float2 *>(&xs[2 * (m * S + sl)]);
+              const float4 xq = *reinterpret_cast<const float4 *>(&xp[(m * S + sl) * kSliceStride + 16]);
               float dd = 0.f;
 #pragma unroll
               for (int q = 0; q < 16; ++q) dd = dot2(pr[q], xv[q], dd);
-              acc[r][m] = sf[r] * fmaf(-zf[r], xq.x, dd - xq.y);
+              acc[r][m] = (sf[r] * xq.z) * fmaf(-zf[r], xq.x, dd - xq.y);
             }
           }
         }
@@ -711,14 +762,16 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 }
 
 // A task's LDS operands, read in one asm statement that also waits for
-// them: the activation slice (4 x 16 bytes) and its two sums (bytes 64..71
-// of the slice), the scales and
+// them: the activation slice (4 x 16 bytes) and its sums and factor (bytes
+// 64..79 of the slice), the scales and
 // zeros of the lane's group (rows 0, 1), and the lane's code words of both
 // rows from the ring slot.  Keeping these reads out of the compiler's view
 // keeps it from tying them to the ring's direct loads with waits of its own.
 struct TaskOps {
   u32x4 x[4];
-  uint64_t xq;   // the slice's two sums (a 64-bit scalar: a two-element vector output is not bound as a pair)
+  uint64_t xq;   // the slice's sums X and 1024 XS, as one 64-bit scalar (a vector output whose
+                 // elements were reinterpreted as floats came back from its first register only)
+  uint32_t xf;   // the slice's factor 2^-E
   uint32_t s0, s1, z0, z1;
 };
 
@@ -731,12 +784,13 @@ __device__ __forceinline__ void read_task(uint32_t xa, uint32_t sza, uint32_t ca
   "ds_read_b128 %[x2], %[xa] offset:32\n\t" \
   "ds_read_b128 %[x3], %[xa] offset:48\n\t" \
   "ds_read_b64 %[xq], %[xa] offset:64\n\t" \
+  "ds_read_b32 %[xf], %[xa] offset:72\n\t" \
   "ds_read_u16 %[s0], %[sza]\n\t"       \
   "ds_read_u16 %[s1], %[sza] offset:16\n\t" \
   "ds_read_u16 %[z0], %[sza] offset:256\n\t" \
   "ds_read_u16 %[z1], %[sza] offset:272\n\t"
 #define WQ_OPS_OUT                                                                                      \
-  [x0] "=&v"(o.x[0]), [x1] "=&v"(o.x[1]), [x2] "=&v"(o.x[2]), [x3] "=&v"(o.x[3]), [xq] "=&v"(o.xq),     \
+  [x0] "=&v"(o.x[0]), [x1] "=&v"(o.x[1]), [x2] "=&v"(o.x[2]), [x3] "=&v"(o.x[3]), [xq] "=&v"(o.xq), [xf] "=&v"(o.xf), \
       [s0] "=&v"(o.s0), [s1] "=&v"(o.s1), [z0] "=&v"(o.z0), [z1] "=&v"(o.z1)
 #define WQ_OPS_IN [xa] "v"(xa), [sza] "v"(sza), [ca16] "v"(ca16), [ca4] "v"(ca4)
   if constexpr (BITS == 4) {
@@ -921,7 +975,7 @@ __device__ __forceinline__ void stream_ring(const LinDesc &L, const uint32_t *co
 #pragma unroll
   for (int q = 0; q < XC; ++q) {
     consume(xr[q], sw[q]);
-    rotate_item<BITS, 1, true>(rotate, xr[q], sw[q], nb, items, rg + RG * q, j, xp, nullptr, S);
+    rotate_item<BITS, 1>(rotate, xr[q], sw[q], nb, items, rg + RG * q, j, xp, S);
   }
   for (int it0 = RG * XC; it0 < items; it0 += RG) {
     const int it = it0 + rg;
@@ -929,7 +983,7 @@ __device__ __forceinline__ void stream_ring(const LinDesc &L, const uint32_t *co
     const u32x4 raw = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, ok ? (uint32_t)(256 * it + 16 * j) : kOOB, 0, 0));
     const uint32_t w1 = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsg, ok ? (uint32_t)(16 * it + 4 * (j >> 2)) : kOOB, 0, 0);
     consume(raw, w1);
-    rotate_item<BITS, 1, true>(rotate, raw, w1, nb, items, it0 + rg, j, xp, nullptr, S);
+    rotate_item<BITS, 1>(rotate, raw, w1, nb, items, it0 + rg, j, xp, S);
   }
   lds_barrier();
 
@@ -969,6 +1023,7 @@ __device__ __forceinline__ void stream_ring(const LinDesc &L, const uint32_t *co
           xv[4 * q + 0] = o.x[q].x; xv[4 * q + 1] = o.x[q].y; xv[4 * q + 2] = o.x[q].z; xv[4 * q + 3] = o.x[q].w;
         }
         const float xsum = __builtin_bit_cast(float, (uint32_t)o.xq), xoff = __builtin_bit_cast(float, (uint32_t)(o.xq >> 32));
+        const float xf = __builtin_bit_cast(float, o.xf);
         const float sc[2] = {half_bits_to_float(o.s0), half_bits_to_float(o.s1)};
         const float zc[2] = {half_bits_to_float(o.z0), half_bits_to_float(o.z1)};
         float a[2];
@@ -987,6 +1042,8 @@ __device__ __forceinline__ void stream_ring(const LinDesc &L, const uint32_t *co
         const bool odd = j & 1;
         float v = (odd ? a[1] : a[0]) + dpp<kQuadXor1>(odd ? a[0] : a[1]);
         v += dpp<kQuadXor2>(v);
+        // the 4 lanes of a quad hold one 128-block, so one exponent: back to x' units
+        v *= xf;
         v += dpp<kRowRor4>(v);
         v += dpp<kRowRor8>(v);
         if (j < 2) lds_store(pa, v);
@@ -1392,19 +1449,30 @@ __device__ __forceinline__ void stream_quads(const LinDesc &L, int m_valid, int 
   }
   __syncthreads();
 
-  // 5. add each row's parts in order (chunk, then part), store
+  // 5. add each row's parts in order (chunk, then part), remove the batch
+  //    row's activation exponent (the factor 2^-E in word 18 of each of its
+  //    slices), store
   for (int e = t; e < rows * m_valid; e += kQuadThreads) {
     const int row = e / m_valid, m = e % m_valid;
     float sum = 0.f;
     for (int u = 0; u < PC; ++u) sum += part[(row * PC + u) * MT + m];
-    store_out(L, m, r0 + row, sum);
+    store_out(L, m, r0 + row, sum * __builtin_bit_cast(float, L.xq[(size_t)m * S * kSliceStride + 18]));
   }
 }
 
 // The pre-pass of the batch-tile kernels: every linear's activations, all m
-// rows, rotated (when the linear has signs) and arranged in the LDS slice
-// layout [m][K/32][20 words].  16 blocks of 128 per 256-thread workgroup;
-// workgroups dealt to the linears by a packed table of first workgroups.
+// rows, rotated (when the linear has signs) and arranged in the slice layout
+// [m][K/32][20 words].  One exponent per batch row, from the largest |x'| of
+// the whole row, so that the batch-tile kernel removes it from each output
+// once (its partials add slices of many blocks in registers).  One
+// 512-thread workgroup per (linear, batch row), dealt by a packed table of
+// first workgroups; DPP row rg takes blocks rg + 32 i, the first
+// kXprepHeld of them held in registers between the maximum and the stores,
+// any further ones (K above 12288) rotated twice: for the maximum, then to
+// store.
+constexpr int kXprepThreads = 512;
+constexpr int kXprepHeld = 3;
+
 struct XprepMat {
   const uint16_t *x;
   uint32_t *out;
@@ -1419,29 +1487,66 @@ struct XprepBatch {
 };
 
 template <int BITS>
-__global__ __launch_bounds__(256) void xprep_kernel(XprepBatch a) {
+__global__ __launch_bounds__(kXprepThreads) void xprep_kernel(XprepBatch a) {
+  constexpr int RG = kXprepThreads / 16;
+  __shared__ __align__(16) float red[RG];
   const int w = blockIdx.x;
   int l = 0;
 #pragma unroll
   for (int i = 1; i < kMaxBatch; ++i)
     if (w >= a.first_wg[i]) l = i;
   const XprepMat M = a.mat[l];
-  const int nb = M.k / kGroup;
-  const int item = (w - M.wg_begin) * 16 + (int)(threadIdx.x >> 4);
-  if (item >= M.m * nb) return;   // whole 16-lane rows leave together
-  const int m = item / nb, b = item - m * nb, jj = threadIdx.x & 15;
-  const int kk = 128 * b + 8 * jj;
-  const u32x4 raw = *reinterpret_cast<const u32x4 *>(M.x + (size_t)m * M.ldx + kk);
-  const uint32_t sword = M.signs ? M.signs[kk >> 5] : 0u;
-  uint32_t o[4];
-  float xe, xt;
-  arrange8<BITS>(M.signs != nullptr, raw, sword, kk, jj, o, xe, xt);
-  const int S = M.k / kSlice, slice = 4 * b + (jj >> 2);
-  uint32_t *dst = M.out + ((size_t)m * S + slice) * kSliceStride;
-  *reinterpret_cast<u32x4 *>(dst + 4 * (jj & 3)) = u32x4{o[0], o[1], o[2], o[3]};
-  if ((jj & 3) == 0)
-    *reinterpret_cast<u32x4 *>(dst + 16) =
-        u32x4{__builtin_bit_cast(uint32_t, xe), __builtin_bit_cast(uint32_t, 1024.0f * xt), 0u, 0u};
+  const int m = w - M.wg_begin;
+  const int nb = M.k / kGroup, S = M.k / kSlice;
+  const int t = threadIdx.x, rg = t >> 4, jj = t & 15;
+  const bool rotate = M.signs != nullptr;
+  const uint16_t *xrow = M.x + (size_t)m * M.ldx;
+  uint32_t *orow = M.out + (size_t)m * S * kSliceStride;
+  // branches on the block index are uniform across the 16 lanes of a DPP row
+  auto load = [&](int b, float (&v)[8]) {
+    const int kk = 128 * b + 8 * jj;
+    const u32x4 raw = *reinterpret_cast<const u32x4 *>(xrow + kk);
+    const uint32_t sword = rotate ? M.signs[kk >> 5] : 0u;
+    load_rotated8(rotate, raw, sword, kk, jj, v);
+  };
+  float v[kXprepHeld][8];
+  float mx = 0.f;
+#pragma unroll
+  for (int i = 0; i < kXprepHeld; ++i) {
+    if (rg + RG * i < nb) {
+      load(rg + RG * i, v[i]);
+      mx = fmaxf(mx, absmax8(v[i]));
+    }
+  }
+  for (int b = rg + RG * kXprepHeld; b < nb; b += RG) {
+    float u[8];
+    load(b, u);
+    mx = fmaxf(mx, absmax8(u));
+  }
+  mx = row16_max(mx);
+  if (jj == 0) red[rg] = mx;
+  __syncthreads();
+  float g = 0.f;
+#pragma unroll
+  for (int q = 0; q < RG; q += 4) {
+    const float4 r4 = *reinterpret_cast<const float4 *>(&red[q]);
+    g = fmaxf(g, fmaxf(fmaxf(r4.x, r4.y), fmaxf(r4.z, r4.w)));
+  }
+  const int E = act_exponent(g * rot_scale(rotate));
+  auto put = [&](int b, float (&u)[8]) {
+    uint32_t o[4];
+    float xe, xt;
+    arrange8<BITS>(rotate, u, jj, E, o, xe, xt);
+    store_slice_part(orow + (size_t)(4 * b + (jj >> 2)) * kSliceStride, jj, o, xe, xt, E);
+  };
+#pragma unroll
+  for (int i = 0; i < kXprepHeld; ++i)
+    if (rg + RG * i < nb) put(rg + RG * i, v[i]);
+  for (int b = rg + RG * kXprepHeld; b < nb; b += RG) {
+    float u[8];
+    load(b, u);
+    put(b, u);
+  }
 }
 
 template <int BITS, bool FULL>
@@ -1597,14 +1702,15 @@ hipError_t launch_xprep(int bits, int count, const uint16_t *const *x, const int
     M.m = (int32_t)m;
     M.wg_begin = (int32_t)wgs;
     a.first_wg[i] = (int32_t)wgs;
-    wgs += (m * (k[i] / kGroup) + 15) / 16;
+    wgs += m;   // one workgroup per batch row
   }
   if (wgs > INT32_MAX) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)wgs), block(kXprepThreads);
   switch (bits) {
-    case 3: hipLaunchKernelGGL(xprep_kernel<3>, dim3((unsigned)wgs), dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL(xprep_kernel<4>, dim3((unsigned)wgs), dim3(256), 0, s, a); break;
-    case 6: hipLaunchKernelGGL(xprep_kernel<6>, dim3((unsigned)wgs), dim3(256), 0, s, a); break;
-    case 8: hipLaunchKernelGGL(xprep_kernel<8>, dim3((unsigned)wgs), dim3(256), 0, s, a); break;
+    case 3: hipLaunchKernelGGL(xprep_kernel<3>, grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL(xprep_kernel<4>, grid, block, 0, s, a); break;
+    case 6: hipLaunchKernelGGL(xprep_kernel<6>, grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL(xprep_kernel<8>, grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -53,12 +53,6 @@ def signs_from_bits(bits: np.ndarray, k: int) -> np.ndarray:
     return d
 
 
-def rotation_matrix(d_block: np.ndarray) -> np.ndarray:
-    """``R = H . diag(d) / sqrt(b)`` for one block, fp64."""
-    b = len(d_block)
-    return (hadamard(b).astype(np.float64) * np.asarray(d_block, np.float64)[None, :]) / np.sqrt(float(b))
-
-
 def rht(x: np.ndarray, sign_bits: np.ndarray, block: int = BLOCK) -> np.ndarray:
     """Rotate each length-``block`` slice of every row of ``x`` (fp64 result).
 

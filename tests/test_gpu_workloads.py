@@ -147,12 +147,7 @@ def test_prefill_int4_m512():
     for i, lin in enumerate(wl.linears[:-1]):
         w, x, signs, _ = W.linear_inputs(SEED, wl.wid, i, lin, m)
         qw = dq.quantize_weight(dev(w), 4, dev_u32(signs))
-        try:
-            y = dq.wq_linear(qw, dev(x))
-        except dq.WqError as e:
-            if e.status == dq.WQ_E_UNSUPPORTED:
-                pytest.skip("matrix-core path not built yet")
-            raise
+        y = dq.wq_linear(qw, dev(x))
         torch.cuda.synchronize()
         rows = _sample_rows(lin.n, rng)
         mrows = np.sort(rng.choice(m, 24, replace=False))

@@ -65,3 +65,14 @@ def test_trained_scale_zero_stay_valid():
     s2, z2 = W.trained_scale_zero(s, z, rng, 15)
     assert np.all(s2 > 0) and np.all((z2 >= 0) & (z2 <= 15))
     assert np.any(z2.astype(np.float32) != np.round(z2.astype(np.float32)))
+
+
+def test_scaled_activations_recipe():
+    rng = W.rng_for(0, 9, 3)
+    x = W.scaled_activations(3, 4096, rng, [1e-3, 1.0, 300.0])
+    assert x.dtype == np.float16 and x.shape == (3, 4096)
+    rms = np.sqrt((x.astype(np.float64) ** 2).mean(axis=1))
+    assert np.allclose(rms, [1e-3, 1.0, 300.0], rtol=0.05)
+    y = W.scaled_activations(1, 4096, W.rng_for(0, 9, 4), 1.0, outlier_frac=0.01, outlier_scale=50.0)
+    big = np.abs(y[0].astype(np.float64)) > 12.0   # beyond any plain N(0, 1) draw of this size
+    assert 20 <= int(big.sum()) <= 41

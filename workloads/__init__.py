@@ -70,6 +70,21 @@ def activations(m: int, k: int, rng: np.random.Generator) -> np.ndarray:
     return rng.standard_normal((m, k)).astype(np.float16)
 
 
+def scaled_activations(m: int, k: int, rng: np.random.Generator, rms, outlier_frac: float = 0.0,
+                       outlier_scale: float = 1.0) -> np.ndarray:
+    """fp16 [m][k] activations ``rms * N(0, 1)`` (``rms`` a number, or one per
+    batch row), with ``round(outlier_frac * k)`` input channels, chosen without
+    replacement, multiplied by ``outlier_scale``.  Rounded to fp16 once, after
+    scaling, so small values may be fp16 subnormals, as they would be in a
+    real fp16 activation tensor."""
+    x = rng.standard_normal((m, k))
+    x *= np.broadcast_to(np.asarray(rms, dtype=np.float64).reshape(-1, 1), (m, 1))
+    n_out = int(round(outlier_frac * k))
+    if n_out:
+        x[:, rng.choice(k, n_out, replace=False)] *= outlier_scale
+    return x.astype(np.float16)
+
+
 def sign_bits(k: int, rng: np.random.Generator) -> np.ndarray:
     """``k`` random sign bits packed into ``uint32 [k/32]`` (bit set => -1)."""
     if k % 32:
@@ -88,7 +103,7 @@ def block_selector(n: int, rng: np.random.Generator, frac8: float = 0.2) -> np.n
 
 
 def trained_scale_zero(s16: np.ndarray, z16: np.ndarray, rng: np.random.Generator,
-                       qmax: int) -> tuple[np.ndarray, np.ndarray]:
+                       qmax) -> tuple[np.ndarray, np.ndarray]:
     """Scales and zeros moved off their round-to-nearest values.
 
     Stands in for scales and zero points that were trained after
@@ -99,7 +114,7 @@ def trained_scale_zero(s16: np.ndarray, z16: np.ndarray, rng: np.random.Generato
     """
     s = s16.astype(np.float32) * rng.uniform(0.9, 1.1, size=s16.shape).astype(np.float32)
     z = z16.astype(np.float32) + rng.uniform(-0.5, 0.5, size=z16.shape).astype(np.float32)
-    z = np.clip(z, 0.0, float(qmax))
+    z = np.clip(z, 0.0, np.asarray(qmax, dtype=np.float32))   # qmax: a number, or one per row
     return s.astype(np.float16), z.astype(np.float16)
 
 
