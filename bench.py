@@ -12,13 +12,19 @@ Weights are cold: a rotating pool of distinct weight copies (>= 1 GB, well
 above the 256 MB Infinity Cache) is cycled, one copy per step.  The timed
 region is K steps replayed from a HIP graph (so the host launch path stays
 out of it) on one stream, bracketed by HIP events on that stream with a
-synchronisation on both sides; after 9 untimed replays (graph upload, and
-the clocks settling) it is replayed 5 times and the median taken (replays
-of the same graph differ by up to ~10% on some hosts).  At M = 1 a
-step is exactly one launch of the GEMV, so the region gives its duration
-per launch, and the roofline figure is algorithmic bytes per launch over
-it.  The same K steps launched eagerly (with the host's time to issue one)
-are printed beside it.
+synchronisation on both sides; after untimed replays for at least
+WARMUP_MS of GPU time, whatever K is (graph upload, and the clocks
+settling: the first replays after idle run up to ~15% slower), it is
+replayed TIMED_REPLAYS times and the median taken.  At M = 1 a step is
+exactly one launch of the GEMV, so the region gives its duration per
+launch, and the roofline figure is algorithmic bytes per launch over it.
+The same K steps launched eagerly (with the host's time to issue one) are
+printed beside it.
+
+The read ceiling of the same run: a plain streaming read of the step's
+algorithmic bytes (wq_stream_read, cold: a 1 GB pool cycled), K reads in a
+graph timed the same way, so that the line separates a slower host from a
+slower kernel (frac_of_read_ceiling = ceiling time / step time).
 
 Prints one JSON line on stdout; details go to stderr.
 
@@ -45,6 +51,8 @@ import workloads as W  # noqa: E402
 METRIC = "batch-1 RHT+W4A16 dequant GEMV: µs/linear and achieved HBM GB/s vs peak"
 PEAK_HBM_GBS = 8000.0
 POOL_BYTES = 1 << 30
+WARMUP_MS = 50.0      # untimed GPU work before any timed replay
+TIMED_REPLAYS = 7
 COUNTERS = os.path.join(ROOT, "profiles", "gemv_traffic_counters.json")
 
 
@@ -181,14 +189,8 @@ def _time_launches(fns, stream, min_launches: int = 200, replays: int = 3) -> fl
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     times = []
+    warm_graph(g, stream)
     with torch.cuda.stream(stream):
-        # untimed replays, about 20 ms of work, so the clocks settle first
-        t0.record(stream)
-        g.replay()
-        t1.record(stream)
-        torch.cuda.synchronize()
-        for _ in range(min(50, int(20.0 / max(t0.elapsed_time(t1), 1e-3)))):
-            g.replay()
         for _ in range(replays):
             t0.record(stream)
             g.replay()
@@ -199,6 +201,27 @@ def _time_launches(fns, stream, min_launches: int = 200, replays: int = 3) -> fl
     return float(np.median(times))
 
 
+def warm_graph(g, stream, ms: float = WARMUP_MS) -> int:
+    """Untimed replays of ``g`` on ``stream`` until at least ``ms`` of GPU
+    time has passed (the first replay, which uploads the graph, included);
+    returns the number of replays."""
+    import torch
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    done, spent = 0, 0.0
+    with torch.cuda.stream(stream):
+        while spent < ms:
+            batch = 1 if done == 0 else max(1, min(1000, math.ceil((ms - spent) / max(spent / done, 1e-3))))
+            t0.record(stream)
+            for _ in range(batch):
+                g.replay()
+            t1.record(stream)
+            torch.cuda.synchronize()
+            spent += t0.elapsed_time(t1)
+            done += batch
+    return done
+
+
 class _ReadCeiling:
     """The plain streaming-read kernel over cold data of a given size."""
 
@@ -207,7 +230,7 @@ class _ReadCeiling:
         self.buf = torch.empty(pool_bytes, dtype=torch.uint8, device="cuda").fill_(7)
         self.sink = torch.zeros(4, dtype=torch.int32, device="cuda")
 
-    def us(self, nbytes: int, stream) -> float:
+    def us(self, nbytes: int, stream, launches: int = 200, replays: int = 3) -> float:
         import dequant_gemv_rht_amd as dq
         nb = (nbytes + 15) // 16 * 16
         stride = (nb + 255) // 256 * 256
@@ -220,7 +243,7 @@ class _ReadCeiling:
         def one(i):
             off = base + (i % copies) * stride
             return lambda sp: dq._check("wq_stream_read", lib.wq_stream_read(off, nb, sink, sp))
-        return _time_launches([one(i) for i in range(copies)], stream)
+        return _time_launches([one(i) for i in range(copies)], stream, launches, replays)
 
 
 def _oracle_ms(w_rows, x, signs, bits_rows, lin, threads: int) -> float:
@@ -516,13 +539,7 @@ def main():
     with torch.cuda.graph(graph, stream=stream):
         for i in range(args.steps):
             calls[i % copies](sptr)
-    with torch.cuda.stream(stream):
-        graph.replay()                      # untimed replay: graph upload
-        # more untimed replays, ~20 ms of work at M = 1: the clocks settle
-        # (the first replays after idle run a few percent slower)
-        for _ in range(8):
-            graph.replay()
-    torch.cuda.synchronize()
+    n_warm = warm_graph(graph, stream)   # graph upload, then the clocks settle
 
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
@@ -539,7 +556,7 @@ def main():
     host_ms_per_step = (h1 - h0) * 1e3 / args.steps
 
     replays = []
-    for _ in range(5):
+    for _ in range(TIMED_REPLAYS):
         torch.cuda.synchronize()
         with torch.cuda.stream(stream):
             t0.record(stream)
@@ -549,7 +566,8 @@ def main():
         replays.append(t0.elapsed_time(t1) / args.steps)
     graph_ms_per_step = float(np.median(replays))
     ms_per_step = graph_ms_per_step
-    timing = "HIP graph of the K steps, median of 5 replays"
+    timing = (f"HIP graph of the K steps, median of {TIMED_REPLAYS} replays after {n_warm} untimed replays "
+              f"(>= {WARMUP_MS:.0f} ms of GPU time)")
 
     # ---- per-launch duration of the dominant kernel: at M = 1 a step is
     # exactly one launch of it, so the timed region gives it directly (events
@@ -576,6 +594,11 @@ def main():
         f"us/step (host {host_ms_per_step * 1e3:.2f} us to issue one); "
         f"single launch (events) mean {np.mean(durs) * 1e3:.2f} us, p10 {durs[len(durs) // 10] * 1e3:.2f}, "
         f"p90 {durs[9 * len(durs) // 10] * 1e3:.2f}")
+
+    # the same run's read ceiling: a plain read of the step's bytes, timed the same way
+    ceiling_us = _ReadCeiling(args.pool_bytes).us(nbytes, stream, launches=args.steps, replays=TIMED_REPLAYS)
+    log(f"read ceiling (plain streaming read of {nbytes} bytes, cold, same protocol): {ceiling_us:.2f} us "
+        f"= {nbytes / ceiling_us / 1e3:.0f} GB/s; the step runs at {ceiling_us / (ms_per_step * 1e3):.1%} of it")
 
     traffic = None
     digest = source_digest()
@@ -614,6 +637,9 @@ def main():
         "graph_us_per_step": round(graph_ms_per_step * 1e3, 3),
         "host_us_per_step": round(host_ms_per_step * 1e3, 3),
         "frac_of_peak_hbm": round(gbs / PEAK_HBM_GBS, 4),
+        "read_ceiling_us_per_step": round(ceiling_us, 3),
+        "read_ceiling_gbs": round(nbytes / ceiling_us / 1e3, 2),
+        "frac_of_read_ceiling": round(ceiling_us / (ms_per_step * 1e3), 4),
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 2),

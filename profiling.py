@@ -1,14 +1,14 @@
 """Summaries of rocprofv3 output for the committed profiles.
 
-    python -m dequant_gemv_rht_amd.profiling trace DIR [--match gemv]
+    python3 profiling.py trace DIR [--match gemv]
         per-kernel calls and durations from a `--kernel-trace --stats` run
 
-    python -m dequant_gemv_rht_amd.profiling traffic --fetch DIR --write DIR \\
+    python3 profiling.py traffic --fetch DIR --write DIR \\
         --copy-fetch DIR --copy-write DIR --copy-bytes N --key block_int4/m1 --out FILE
         HBM bytes per launch of the GEMV from FETCH_SIZE / WRITE_SIZE, each
         scaled by what the same counter reads for a plain copy of N bytes
 
-    python -m dequant_gemv_rht_amd.profiling counters DIR --match gemm_kernel
+    python3 profiling.py counters DIR --match gemm_kernel
         every counter of a `--pmc` run, per dispatch of the matching kernels
         (summed over the counter's instances: XCDs, SEs, channels)
 
@@ -22,13 +22,12 @@ import argparse
 import collections
 import csv
 import glob
-import importlib.util
 import json
 import os
 import sqlite3
 import sys
 
-ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+ROOT = os.path.dirname(os.path.abspath(__file__))
 
 
 def _files(d: str, suffix: str):
@@ -80,10 +79,9 @@ def counter_values(d: str, counter: str, match: str = ""):
 
 
 def _source_digest() -> str:
-    spec = importlib.util.spec_from_file_location("_bench", os.path.join(ROOT, "bench.py"))
-    mod = importlib.util.module_from_spec(spec)
-    spec.loader.exec_module(mod)
-    return mod.source_digest()
+    sys.path.insert(0, ROOT)
+    import bench
+    return bench.source_digest()
 
 
 def traffic(a) -> dict:
