@@ -13,6 +13,7 @@ Functions mirror the C ABI in ``include/wq.h``:
   rht_apply(x, signs, out=None)                      -> rotated fp16 activations
   wq_linear(weight, x, out_dtype=float16, fuse_rht=True, workspace=None) -> y
   wq_linear_batch(weights, xs, out_dtypes=None, fuse_rht=True, workspace=None) -> [y]
+  wq_linear_batch_noalloc(weights, xs, out_dtypes=None, fuse_rht=True, out=None) -> [y]
   wq_embed(table, ids, out_dtype=float16, out=None)  -> dequantised table rows
 """
 
@@ -62,7 +63,11 @@ SIGNATURES = {
     "wq_last_error": (ctypes.c_char_p, []),
     "wq_stream_read": (_i32, [_vp, _sz, _vp, _vp]),
     "wq_embed": (_i32, [ctypes.POINTER(WqWeight), _vp, _i64, _vp, _i32, _i64, _vp]),
+    "wq_linear_batch_noalloc": (_i32, [_i32, ctypes.POINTER(WqWeight), ctypes.POINTER(_vp),
+                                       ctypes.POINTER(_i64), _i64, ctypes.POINTER(_vp), ctypes.POINTER(_i32),
+                                       ctypes.POINTER(_i64), _u32, _vp]),
 }
+NOALLOC_SCRATCH_BYTES = 64 << 20   # WQ_NOALLOC_SCRATCH_BYTES
 
 _lib = None
 
@@ -268,6 +273,24 @@ def wq_linear_batch(weights: Sequence[QWeight], xs: Sequence[torch.Tensor], out_
     if workspace is None:
         workspace = new_workspace(wq_linear_batch_workspace(weights, m), xs[0].device)
     BatchCall(weights, xs, ys, fuse_rht, workspace)()
+    return ys
+
+
+def wq_linear_batch_noalloc(weights: Sequence[QWeight], xs: Sequence[torch.Tensor], out_dtypes=None,
+                            fuse_rht: bool = True, out: Optional[Sequence[torch.Tensor]] = None):
+    """wq_linear_batch on the library's static scratch: no workspace argument,
+    and the call allocates no device memory (outputs are allocated here
+    unless given in ``out``)."""
+    m = xs[0].shape[0]
+    out_dtypes = out_dtypes or [torch.float16] * len(weights)
+    ys = list(out) if out is not None else [torch.empty((m, w.n), dtype=dt, device=xs[0].device)
+                                            for w, dt in zip(weights, out_dtypes)]
+    c = len(weights)
+    _check("wq_linear_batch_noalloc", lib().wq_linear_batch_noalloc(
+        c, (WqWeight * c)(*[w.c_struct() for w in weights]), (_vp * c)(*[x.data_ptr() for x in xs]),
+        (_i64 * c)(*[x.stride(0) for x in xs]), m, (_vp * c)(*[y.data_ptr() for y in ys]),
+        (_i32 * c)(*[WQ_F32 if y.dtype == torch.float32 else WQ_F16 for y in ys]),
+        (_i64 * c)(*[y.stride(0) for y in ys]), WQ_FUSE_RHT if fuse_rht else 0, _stream()))
     return ys
 
 

@@ -25,6 +25,21 @@ wq_status fail(wq_status st, const char *fmt, ...) {
 
 void clear_err() { g_err[0] = 0; }
 
+}  // namespace
+
+// The thread's error message, for entry points in other translation units.
+wq_status wq::set_error(wq_status st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+void wq::clear_error() { clear_err(); }
+
+namespace {
+
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 bool uniform_bits(int b) { return b == 3 || b == 4 || b == 6 || b == 8; }

@@ -63,6 +63,11 @@ struct GemvArgs {
   int32_t mixed_wpb;            // batch-1 ring over the mixed 6/8-bit layout: workgroups per 64-row block
 };
 
+// The calling thread's message for wq_last_error (api.cpp): set_error
+// formats it and returns st; clear_error empties it.
+wq_status set_error(wq_status st, const char *fmt, ...);
+void clear_error();
+
 // Host-side launchers (gemv*.hip).  `bits` 0 = mixed.  mt = 1,2,4,8,16.
 hipError_t launch_gemv(int bits, int mt, const GemvArgs &a, hipStream_t s);
 // Persistent stream kernels: one workgroup per CU, uniform code width (or

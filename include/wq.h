@@ -221,6 +221,27 @@ wq_status wq_linear_batch(int32_t count, const wq_weight *w,
                           uint32_t flags, void *workspace, size_t workspace_bytes,
                           void *stream);
 
+/* wq_linear_batch for callers that cannot allocate device memory (code
+ * under stream capture, tight serving loops, harnesses that forbid
+ * allocation): the same call, arguments and results, with no workspace
+ * argument.  Its workspace is a static scratch array inside the library,
+ * WQ_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU, which each GPU the library
+ * runs on holds until the process ends.  The call itself allocates and
+ * frees nothing.  The scratch needs no initialisation and keeps the last
+ * call's contents; calls that overlap on one GPU (several streams or host
+ * threads at once) share it and race: serialise them.  64 MiB covers, for
+ * example, the seven projections of a 4B-class decoder block up to 512
+ * batch rows (58.8 MB).
+ * Errors: those of wq_linear_batch, and WQ_E_WORKSPACE (nothing launched)
+ * when wq_linear_batch_workspace for the same arguments exceeds
+ * WQ_NOALLOC_SCRATCH_BYTES; WQ_E_HIP if the scratch's address cannot be
+ * looked up on the current device. */
+#define WQ_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+wq_status wq_linear_batch_noalloc(int32_t count, const wq_weight *w,
+                                  const uint16_t *const *x, const int64_t *ldx, int64_t m,
+                                  void *const *y, const wq_dtype *y_dtype, const int64_t *ldy,
+                                  uint32_t flags, void *stream);
+
 /* Tied-embedding gather: rows ids[0..count) of a quantised table,
  * dequantised,
  *   out[i][k] = (q[ids[i]][k] - z[ids[i]][k/128]) * s[ids[i]][k/128],

@@ -240,3 +240,16 @@ def test_gemv_batch_rejects_small_workspace(lib):
     ldy = (ctypes.c_int64 * 1)(256)
     st = lib.wq_linear_batch(1, arr, xs, lds, 4, ys, dts, ldy, dq.WQ_FUSE_RHT, None, 0, None)
     assert st == dq.WQ_E_WORKSPACE
+
+
+def test_noalloc_refuses_a_call_beyond_its_scratch(lib):
+    # the size check runs on the host before the scratch or any kernel is
+    # touched: 4096 rows of K = 9728 need ~80 MB of rotated activations
+    w = _weight(n=256, k=9728, rht_signs=16, rht_block=128)
+    need = lib.wq_linear_batch_workspace(1, ctypes.byref(w), 4096)
+    assert need > dq.NOALLOC_SCRATCH_BYTES
+    xs, lds, ys = (ctypes.c_void_p * 1)(16), (ctypes.c_int64 * 1)(9728), (ctypes.c_void_p * 1)(16)
+    dts, ldys = (ctypes.c_int32 * 1)(dq.WQ_F16), (ctypes.c_int64 * 1)(256)
+    st = lib.wq_linear_batch_noalloc(1, ctypes.byref(w), xs, lds, 4096, ys, dts, ldys, dq.WQ_FUSE_RHT, None)
+    assert st == dq.WQ_E_WORKSPACE
+    assert "static scratch" in lib.wq_last_error().decode()
