@@ -116,8 +116,10 @@ PEAK_MFMA_F16_TFLOPS = 2500.0
 
 def kernel_name(bits: int, m: int) -> str:
     """The kernel one step launches (the planner's choice for these shapes)."""
-    if m >= 64:
-        return f"gemm_kernel<{bits}> (matrix cores, all linears in one launch), after rht_batch_kernel"
+    if m >= 17:
+        mb, nb = (1, 1) if m <= 32 else (2, 1) if m <= 64 else (4, 2)
+        return (f"gemm_kernel<{bits}, {mb}, {nb}> (matrix cores, all linears in one launch), after "
+                f"rht_batch_kernel (and gemm_finalize_kernel where K is split)")
     if m == 1:
         return f"gemv_ring_kernel<{bits}, true> (LDS-ring weight stream)"
     tile = 2 if m == 2 else 4 if m <= 4 else 8 if m <= 12 else 16

@@ -384,9 +384,13 @@ size_t rotated_bytes(const wq_weight &w, int64_t m) {
   return w.rht_signs ? align256((size_t)m * (size_t)rotated_ld(w) * sizeof(uint16_t)) : 0;
 }
 
-// Batch sizes from 64 up run on the matrix cores (uniform code widths); the
-// mixed-width layout stays on the GEMV, in chunks of 16 batch rows.
-bool use_gemm(const wq_weight &w, int64_t m) { return m >= 64 && wq::gemm_available(w.bits); }
+// Batch sizes above 16 run on the matrix cores (uniform code widths): from
+// 17 rows on the product is a dense contraction that the GEMV, bound by its
+// vector work per weight and batch row, runs slower (the int4 decoder block:
+// 72 against 38 us at 17 rows, 226 against 47 us at 63).  The mixed-width
+// layout stays on the GEMV, in chunks of 16 batch rows.
+constexpr int64_t kGemmMinRows = 17;
+bool use_gemm(const wq_weight &w, int64_t m) { return m >= kGemmMinRows && wq::gemm_available(w.bits); }
 
 // Workspace of a matrix-core launch over `count` linears: each linear's
 // rotated activations (when rotating), then each split linear's fp32
@@ -630,14 +634,14 @@ size_t wq_linear_batch_workspace(int32_t count, const wq_weight *w, int64_t m) {
     fail(WQ_E_ARG, "wq_linear_batch_workspace: m must be positive");
     return (size_t)-1;
   }
-  bool gemm = m > 16;
+  bool gemm = true;   // use_gemm alone decides which path, and so which workspace, the call takes
   size_t all = 0;
   for (int i = 0; i < count; ++i) {
     if (check_weight(&w[i], "wq_linear_batch_workspace") != WQ_OK) return (size_t)-1;
     gemm = gemm && use_gemm(w[i], m) && w[i].bits == w[0].bits;
     if (uses_xprep(w[i], m)) all += xprep_bytes(w[i].k, m);
   }
-  // m >= 64 with one uniform width: one matrix-core launch over all of them;
+  // above 16 rows with one uniform width: one matrix-core launch over all of them;
   // below: every linear's arranged activations side by side (none for the
   // mixed layout, whose GEMV needs no workspace)
   if (gemm) return gemm_layout(count, w, m, true).total;

@@ -1,4 +1,4 @@
-// Matrix-core path for batch sizes M >= 64 (gfx950): y = x' . W^T with the
+// Matrix-core path for batch sizes M >= 17 (gfx950): y = x' . W^T with the
 // weight dequantised in registers and multiplied on MFMA
 // (v_mfma_f32_32x32x16_f16, fp32 accumulate).  Same layer as the GEMV:
 // w = (q - z) s per group of 128 along K (model card "24B0978 - Week 01 -
@@ -10,14 +10,17 @@
 // One launch serves every linear of a batch: workgroups are dealt to the
 // linears by a packed table of first tiles, like the GEMV.
 //
-// Tiling.  A workgroup of 4 waves owns a 128 (batch rows) x 256 (outputs)
-// tile of y and a range of K in steps of 64 (half a group, so a step never
-// straddles two scales); each wave owns 128 x 64 of the tile: 4 x 2 blocks
-// of 32 x 32, 128 fp32 accumulators per lane.  A long K is split over
-// several workgroups whose fp32 partial tiles a second kernel adds.
+// Tiling (Tile below).  A workgroup of 4 waves owns a tile of y and a range
+// of K in steps of 64 (half a group, so a step never straddles two scales).
+// From 65 batch rows the tile is 128 (batch rows) x 256 (outputs), each wave
+// 128 x 64: 4 x 2 blocks of 32 x 32, 128 fp32 accumulators per lane.  From
+// 17 to 64 rows, where the weights dominate the traffic, it is 32 or 64 x
+// 128, each wave one or two blocks of one 32-wide column block, with more
+// steps in flight.  A long K is split over several workgroups whose fp32
+// partial tiles a second kernel adds.
 //
 // Activations (A operand) travel HBM -> LDS by direct buffer-to-LDS loads,
-// kAhead steps in flight; every wave loads 32 of the tile's 128 rows and a
+// kAhead steps in flight; every wave loads a quarter of the tile's rows and a
 // barrier per step publishes them.  In LDS a row is 128 bytes (64 fp16) in
 // eight 16-byte chunks, chunk c of row r stored at slot c ^ (r & 7): the 32
 // lanes reading one chunk of 32 rows then spread over all banks.
@@ -54,16 +57,29 @@ typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
 
-constexpr int kTM = 128, kTN = 256, kBK = 64;
+constexpr int kBK = 64;
 constexpr int kWaves = 4, kGemmThreads = 64 * kWaves;
-constexpr int kStages = 3;                    // steps in flight + 1: activation stages in LDS, weight register sets
-constexpr int kAhead = kStages - 1;           // steps loaded ahead of the one computed
+// Tile shapes: each wave owns MB x NB blocks of 32 x 32 outputs, the four
+// waves side by side along N: a workgroup tile of 32 MB batch rows x 128 NB
+// outputs.  MB = 4, NB = 2 (128 x 256) for long batches; MB = 1 or 2 with
+// NB = 1 (32 or 64 x 128) from 17 to 64 rows, where the weights dominate
+// the traffic and narrower tiles give enough workgroups without cutting K.
+template <int MB, int NB>
+struct Tile {
+  static constexpr int TM = 32 * MB, TN = 32 * NB * kWaves;
+  static constexpr int AStage = TM * kBK * 2;   // bytes of one step's activations in LDS
+  // steps in flight + 1 (activation stages in LDS, weight register sets);
+  // for the narrow tiles 3, 5 and 8 stages measured alike (3 marginally best)
+  static constexpr int Stages = 3;
+  // workgroups per CU: three narrow tiles fit (LDS: Stages x AStage of
+  // activations plus the scale table; registers), two wide ones
+  static constexpr int PerCU = MB == 4 ? 2 : 3;
+};
 constexpr int kMaxSteps = 48;                 // 64-k steps per workgroup at most (longer K is split)
 constexpr int kMaxGroups = kMaxSteps / 2 + 1; // groups of 128 a workgroup's K range touches at most
 
 // LDS slot of 16-byte chunk c of activation row r
 __device__ __forceinline__ int a_slot(int c, int r) { return c ^ (r & 7); }
-constexpr int kAStage = kTM * kBK * 2;        // 16 KB per step
 constexpr uint32_t kMagic = 0x64006400u;      // two fp16 1024.0
 
 struct GemmLin {
@@ -185,46 +201,111 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // The same wait, also taking a step's weight registers as operands, so that
 // no arithmetic on them is scheduled above it.
-template <int N, int BITS>
-__device__ __forceinline__ void wait_vmcnt_regs(uint32_t (&w)[2][BITS]) {
+template <int N, int BITS, int NB>
+__device__ __forceinline__ void wait_vmcnt_regs(uint32_t (&w)[NB][BITS]) {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < NB; ++j)
 #pragma unroll
     for (int e = 0; e < BITS; ++e) asm volatile("" : "+v"(w[j][e]));
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void *p) { return (uint32_t)(uintptr_t)(lds_ptr_t)p; }
 
-// The A operands of one 16-k block for the 4 m blocks (32 rows apart, 4096
-// bytes) of stage ST, read and waited for in one statement.  Reading the
-// direct-loaded tile in asm keeps the compiler from tying these reads to the
-// outstanding direct loads of other stages with waits of its own.
-template <int ST>
-__device__ __forceinline__ void read_a(uint32_t addr, half8 (&a)[4]) {
-  asm volatile(
-      "ds_read_b128 %0, %4 offset:%5\n\t"
-      "ds_read_b128 %1, %4 offset:%6\n\t"
-      "ds_read_b128 %2, %4 offset:%7\n\t"
-      "ds_read_b128 %3, %4 offset:%8\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3])
-      : "v"(addr), "i"(ST * kAStage), "i"(ST * kAStage + 4096), "i"(ST * kAStage + 8192),
-        "i"(ST * kAStage + 12288)
-      : "memory");
+// The A operands of one 16-k block for the MB m blocks (32 rows apart, 4096
+// bytes) of a stage at byte offset OFF, read and waited for in one
+// statement.  Reading the direct-loaded tile in asm keeps the compiler from
+// tying these reads to the outstanding direct loads of other stages with
+// waits of its own.
+template <int OFF, int MB>
+__device__ __forceinline__ void read_a(uint32_t addr, half8 (&a)[MB]) {
+  if constexpr (MB == 4) {
+    asm volatile(
+        "ds_read_b128 %0, %4 offset:%5\n\t"
+        "ds_read_b128 %1, %4 offset:%6\n\t"
+        "ds_read_b128 %2, %4 offset:%7\n\t"
+        "ds_read_b128 %3, %4 offset:%8\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3])
+        : "v"(addr), "i"(OFF), "i"(OFF + 4096), "i"(OFF + 8192), "i"(OFF + 12288)
+        : "memory");
+  } else if constexpr (MB == 2) {
+    asm volatile(
+        "ds_read_b128 %0, %2 offset:%3\n\t"
+        "ds_read_b128 %1, %2 offset:%4\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(a[0]), "=&v"(a[1])
+        : "v"(addr), "i"(OFF), "i"(OFF + 4096)
+        : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b128 %0, %1 offset:%2\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(a[0])
+        : "v"(addr), "i"(OFF)
+        : "memory");
+  }
 }
 
-// The packed scale and zero (s | z << 16) of the lane's two rows for one
+// The packed scale and zero (s | z << 16) of the lane's NB rows for one
 // step, read from LDS and waited for in one statement (kept out of the
 // compiler's view like read_a).
-__device__ __forceinline__ void read_sz(uint32_t a0, uint32_t a1, uint32_t &v0, uint32_t &v1) {
-  asm volatile(
-      "ds_read_b32 %0, %2\n\t"
-      "ds_read_b32 %1, %3\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(v0), "=&v"(v1)
-      : "v"(a0), "v"(a1)
-      : "memory");
+template <int NB>
+__device__ __forceinline__ void read_sz(uint32_t a0, uint32_t a1, uint32_t (&v)[NB]) {
+  if constexpr (NB == 2) {
+    asm volatile(
+        "ds_read_b32 %0, %2\n\t"
+        "ds_read_b32 %1, %3\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1])
+        : "v"(a0), "v"(a1)
+        : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b32 %0, %1\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0])
+        : "v"(a0)
+        : "memory");
+  }
+}
+
+// The step's LDS operands of a narrow tile (NB = 1, MB <= 2): the packed
+// scale and zero of the lane's row and the A fragments of all four 16-k
+// blocks, in one statement with one wait (with few products per step, LDS
+// round trips waited on one by one would set the step's length).
+template <int OFF, int MB>
+__device__ __forceinline__ void read_step_narrow(uint32_t sza, const uint32_t (&ard)[4], uint32_t &sz,
+                                                 half8 (&a)[4][MB]) {
+  if constexpr (MB == 1) {
+    asm volatile(
+        "ds_read_b32 %0, %5\n\t"
+        "ds_read_b128 %1, %6 offset:%10\n\t"
+        "ds_read_b128 %2, %7 offset:%10\n\t"
+        "ds_read_b128 %3, %8 offset:%10\n\t"
+        "ds_read_b128 %4, %9 offset:%10\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(sz), "=&v"(a[0][0]), "=&v"(a[1][0]), "=&v"(a[2][0]), "=&v"(a[3][0])
+        : "v"(sza), "v"(ard[0]), "v"(ard[1]), "v"(ard[2]), "v"(ard[3]), "i"(OFF)
+        : "memory");
+  } else {
+    static_assert(MB == 2, "narrow tiles have one or two m blocks");
+    asm volatile(
+        "ds_read_b32 %0, %9\n\t"
+        "ds_read_b128 %1, %10 offset:%14\n\t"
+        "ds_read_b128 %2, %10 offset:%15\n\t"
+        "ds_read_b128 %3, %11 offset:%14\n\t"
+        "ds_read_b128 %4, %11 offset:%15\n\t"
+        "ds_read_b128 %5, %12 offset:%14\n\t"
+        "ds_read_b128 %6, %12 offset:%15\n\t"
+        "ds_read_b128 %7, %13 offset:%14\n\t"
+        "ds_read_b128 %8, %13 offset:%15\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(sz), "=&v"(a[0][0]), "=&v"(a[0][1]), "=&v"(a[1][0]), "=&v"(a[1][1]), "=&v"(a[2][0]),
+          "=&v"(a[2][1]), "=&v"(a[3][0]), "=&v"(a[3][1])
+        : "v"(sza), "v"(ard[0]), "v"(ard[1]), "v"(ard[2]), "v"(ard[3]), "i"(OFF), "i"(OFF + 4096)
+        : "memory");
+  }
 }
 
 // Logical tile of workgroup b: runs of consecutive tiles (the m tiles of one
@@ -235,11 +316,15 @@ __device__ __forceinline__ int logical_tile(int b, int nb) {
   return (xcd < rem ? xcd * (q + 1) : rem * (q + 1) + (xcd - rem) * q) + slot;
 }
 
-template <int BITS>
-__global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmBatch a) {
+template <int BITS, int MB, int NB>
+__global__ __launch_bounds__(kGemmThreads, (Tile<MB, NB>::PerCU)) void gemm_kernel(GemmBatch a) {
+  using TL = Tile<MB, NB>;
+  constexpr int kTM = TL::TM, kTN = TL::TN, kAStage = TL::AStage;
+  constexpr int kStages = TL::Stages, kAhead = kStages - 1;   // kAhead: steps loaded ahead of the one computed
+  constexpr int WR = 32 * NB;   // weight rows (outputs) per wave
   __shared__ __attribute__((aligned(16))) uint8_t As[kStages * kAStage];
-  // scale and zero of each wave's 64 rows over the workgroup's groups, (s | z << 16)
-  __shared__ uint32_t SZ[kWaves * 64 * kMaxGroups];
+  // scale and zero of each wave's WR rows over the workgroup's groups, (s | z << 16)
+  __shared__ uint32_t SZ[kWaves * WR * kMaxGroups];
   const int tile = logical_tile(blockIdx.x, a.tiles);
   int l = 0;
 #pragma unroll
@@ -262,61 +347,61 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmBatch a) {
   // row's end.  Steps past the range reload the range's last step, so every
   // step issues the same loads and the counts waited on are constants.
   //
-  // activations: rows m0 .. m0 + 127; this wave loads rows 32 wave + 8 i +
-  // lane / 8 (i = 0..3), chunk slot lane % 8
+  // activations: rows m0 .. m0 + kTM - 1; this wave loads rows 8 MB wave +
+  // 8 i + lane / 8 (i < MB), chunk slot lane % 8
   const rsrc_t rx = make_rsrc(L.x + (size_t)m0 * L.ldx, (uint32_t)((size_t)min(kTM, L.m - m0) * L.ldx * 2));
-  const int arow = 32 * wave + (lane >> 3), aslot = lane & 7;
-  uint32_t a_vo[4];
+  const int arow = 8 * MB * wave + (lane >> 3), aslot = lane & 7;
+  uint32_t a_vo[MB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MB; ++i)
     a_vo[i] = (uint32_t)((size_t)(arow + 8 * i) * L.ldx * 2) + (uint32_t)(a_slot(aslot, arow + 8 * i) * 16);
-  const uint32_t as0 = lds_addr(As) + (uint32_t)(wave * 4 * 1024);
+  const uint32_t as0 = lds_addr(As) + (uint32_t)(wave * MB * 1024);
   // weights: rows nw0 + 32 j + lane % 32, slice 2 kt + lane / 32 of the row
-  const int nw0 = n0 + 64 * wave;
+  const int nw0 = n0 + WR * wave;
   // (uniform: a clamp would otherwise become a vector med3 and the resources divergent)
-  const int nrows = __builtin_amdgcn_readfirstlane(max(0, min(64, L.n - nw0)));
+  const int nrows = __builtin_amdgcn_readfirstlane(max(0, min(WR, L.n - nw0)));
   const rsrc_t rc = make_rsrc(L.codes + (size_t)nw0 * wpr, (uint32_t)nrows * wpr * 4);
   const rsrc_t rs = make_rsrc(L.scales + (size_t)nw0 * G, (uint32_t)nrows * G * 2);
   const rsrc_t rz = make_rsrc(L.zeros + (size_t)nw0 * G, (uint32_t)nrows * G * 2);
   const int bn = lane & 31, bh = lane >> 5;
   const uint32_t b_vo0 = (uint32_t)(bn * wpr * 4 + bh * BITS * 4), b_vo1 = b_vo0 + (uint32_t)(32 * wpr * 4);
 
-  // scales and zeros of this wave's rows (lane = row) over the split's
-  // groups g0 .. g0 + ng - 1: loaded once here, written to LDS once the
-  // first steps' loads are out; rows past N read zero
+  // scales and zeros of this wave's rows (lane = row, lanes < WR) over the
+  // split's groups g0 .. g0 + ng - 1: loaded once here, written to LDS once
+  // the first steps' loads are out; rows past N read zero
   const int g0 = kt0 >> 1, ng = ((kt0 + T - 1) >> 1) - g0 + 1;
   uint32_t szs[kMaxGroups], szz[kMaxGroups];
 #pragma unroll
   for (int g = 0; g < kMaxGroups; ++g) {
-    const uint32_t off = g < ng ? (uint32_t)((lane * G + g0 + g) * 2) : kOOB;
+    const uint32_t off = g < ng && lane < WR ? (uint32_t)((lane * G + g0 + g) * 2) : kOOB;
     szs[g] = __builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0);
     szz[g] = __builtin_amdgcn_raw_buffer_load_b16(rz, off, 0, 0);
   }
-  uint32_t *szw = SZ + wave * 64 * kMaxGroups;
+  uint32_t *szw = SZ + wave * WR * kMaxGroups;
   const uint32_t sz_rd0 = lds_addr(szw) + (uint32_t)(bn * kMaxGroups * 4), sz_rd1 = sz_rd0 + 32 * kMaxGroups * 4;
 
-  uint32_t cw[kStages][2][BITS];
+  uint32_t cw[kStages][NB][BITS];
   auto issue = [&](auto sconst, int kt) {
     constexpr int st = decltype(sconst)::value;
     const int kc = min(kt, kt0 + T - 1);
     const uint32_t so_a = (uint32_t)kc * (kBK * 2), so_b = (uint32_t)kc * (2 * BITS * 4);
 #if defined(__HIP_DEVICE_COMPILE__)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MB; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr_t)(as0 + st * kAStage + i * 1024), 16, a_vo[i], so_a, 0, 0);
 #endif
     load_slice<BITS>(rc, b_vo0, so_b, cw[st][0]);
-    load_slice<BITS>(rc, b_vo1, so_b, cw[st][1]);
+    if constexpr (NB == 2) load_slice<BITS>(rc, b_vo1, so_b, cw[st][1]);
   };
   // vector-memory operations of one issue, the count waited on
   constexpr int kLoadsB = BITS == 3 || BITS == 4 ? 1 : 2;
-  constexpr int kIssue = 4 + 2 * kLoadsB;
+  constexpr int kIssue = MB + NB * kLoadsB;
 
-  f32x16 acc[4][2];
+  f32x16 acc[MB][NB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MB; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < NB; ++j) acc[i][j] = f32x16{};
 
   // A fragment of m block i, 16-k block kk: row 32 i + lane % 32, k 32 (lane / 32) + 8 kk,
   // i.e. chunk 4 (lane / 32) + kk of the row at slot chunk ^ (row & 7)
@@ -336,16 +421,21 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmBatch a) {
     constexpr int nx = (st + kAhead) % kStages;
     // this step's activations (this wave's rows) and weights: the younger
     // loads are those of the kAhead - 1 steps issued after it
-    wait_vmcnt_regs<(kAhead - 1) * kIssue, BITS>(cw[st]);
+    wait_vmcnt_regs<(kAhead - 1) * kIssue, BITS, NB>(cw[st]);
     __builtin_amdgcn_s_barrier();   // every wave's rows are in; step kt - 1's stage is free
     issue(std::integral_constant<int, nx>{}, kt + kAhead);
     if (!active) return;
-    uint32_t szv[2];
+    uint32_t szv[NB];
     const uint32_t gofs = (uint32_t)(((kt >> 1) - g0) * 4);
-    read_sz(sz_rd0 + gofs, sz_rd1 + gofs, szv[0], szv[1]);
-    half8 bop[2][4];
+    constexpr bool kNarrow = NB == 1 && MB <= 2;
+    half8 aall[4][kNarrow ? MB : 1];
+    if constexpr (kNarrow)
+      read_step_narrow<st * kAStage, MB>(sz_rd0 + gofs, a_rd, szv[0], aall);
+    else
+      read_sz<NB>(sz_rd0 + gofs, sz_rd1 + gofs, szv);
+    half8 bop[NB][4];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < NB; ++j) {
       const half2v s = as_h2((szv[j] & 0xFFFFu) * 0x10001u);
       const half2v z = as_h2((szv[j] >> 16) * 0x10001u);
       const half2v c = {(_Float16)1.0f, kHi};
@@ -357,12 +447,17 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmBatch a) {
     }
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      half8 aop[4];
-      read_a<st>(a_rd[kk], aop);
+      half8 aop[MB];
+      if constexpr (kNarrow) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < MB; ++i) aop[i] = aall[kk][i];
+      } else {
+        read_a<st * kAStage, MB>(a_rd[kk], aop);
+      }
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
 #if defined(__HIP_DEVICE_COMPILE__)   // the 32x32x16 f16 MFMA exists only in the gfx950 pass
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aop[i], bop[j][kk], acc[i][j], 0, 0, 0);
 #endif
@@ -387,12 +482,20 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmBatch a) {
     asm volatile("" ::: "memory");
     issue(std::integral_constant<int, 4>{}, kt0 + 4);
   }
+  if constexpr (kAhead > 5) {
+    asm volatile("" ::: "memory");
+    issue(std::integral_constant<int, 5>{}, kt0 + 5);
+  }
+  if constexpr (kAhead > 6) {
+    asm volatile("" ::: "memory");
+    issue(std::integral_constant<int, 6>{}, kt0 + 6);
+  }
   // the scales and zeros into LDS (each wave reads back only its own rows)
 #pragma unroll
   for (int g = 0; g < kMaxGroups; ++g)
-    if (g < ng) szw[lane * kMaxGroups + g] = (szs[g] & 0xFFFFu) | (szz[g] << 16);
+    if (g < ng && lane < WR) szw[lane * kMaxGroups + g] = (szs[g] & 0xFFFFu) | (szz[g] << 16);
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  static_assert(kStages >= 3 && kStages <= 6, "the loop below unrolls up to 6 stages");
+  static_assert(kStages >= 3 && kStages <= 8, "the loop below unrolls up to 8 stages");
   for (int i0 = 0; i0 < T; i0 += kStages) {
     step(std::integral_constant<int, 0>{}, kt0 + i0, true);
     step(std::integral_constant<int, 1>{}, kt0 + i0 + 1, i0 + 1 < T);
@@ -400,14 +503,16 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmBatch a) {
     if constexpr (kStages > 3) step(std::integral_constant<int, 3>{}, kt0 + i0 + 3, i0 + 3 < T);
     if constexpr (kStages > 4) step(std::integral_constant<int, 4>{}, kt0 + i0 + 4, i0 + 4 < T);
     if constexpr (kStages > 5) step(std::integral_constant<int, 5>{}, kt0 + i0 + 5, i0 + 5 < T);
+    if constexpr (kStages > 6) step(std::integral_constant<int, 6>{}, kt0 + i0 + 6, i0 + 6 < T);
+    if constexpr (kStages > 7) step(std::integral_constant<int, 7>{}, kt0 + i0 + 7, i0 + 7 < T);
   }
   wait_vmcnt<0>();   // the trailing out-of-range loads still write LDS
 
   // epilogue: accumulator register v of lane l is C[8 (v/4) + 4 (l/32) + v%4][l % 32]
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MB; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < NB; ++j) {
       const int col = nw0 + 32 * j + (lane & 31);
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
@@ -483,17 +588,42 @@ __global__ __launch_bounds__(256) void gemm_finalize_kernel(GemmBatch a) {
 
 bool gemm_available(int bits) { return bits == 3 || bits == 4 || bits == 6 || bits == 8; }
 
+namespace {
+
+// The tile shape for a batch of m rows: MB m blocks and NB n blocks of 32
+// per wave (see Tile).
+struct Shape {
+  int mb, nb;
+  int tm() const { return 32 * mb; }
+  int tn() const { return 32 * nb * kWaves; }
+};
+
+// Up to 64 rows one n block per wave: two (tiles of 256 outputs, half as
+// many workgroups) measured 8% slower for a decoder block's projections.
+Shape shape_for(int64_t m) {
+  if (m <= 32) return {1, 1};
+  if (m <= 64) return {2, 1};
+  return {4, 2};
+}
+
+}  // namespace
+
 // K splits per linear: long K is cut so that the workgroups of a launch have
 // similar lengths; a split costs 8 M N bytes of fp32 partial traffic, so
-// short linears stay whole.
+// short linears stay whole.  Up to 64 batch rows the narrow tiles already
+// give a workgroup per CU or so for a decoder block's projections: only K
+// longer than about 40 steps (2560) is cut there, as the weights, not the
+// partials, must dominate the traffic.
 void gemm_plan(int count, const wq_weight *w, int64_t m, int *ksplit) {
+  const Shape sh = shape_for(m);
   int64_t units = 0;
   for (int i = 0; i < count; ++i) {
-    const int64_t tiles = ((m + kTM - 1) / kTM) * ((w[i].n + kTN - 1) / kTN);
+    const int64_t tiles = ((m + sh.tm() - 1) / sh.tm()) * ((w[i].n + sh.tn() - 1) / sh.tn());
     units += tiles * (w[i].k / kBK);
   }
-  const int64_t slots = 2 * 256;   // two workgroups per CU
-  const int64_t target = std::max<int64_t>(24, (units + slots - 1) / slots);
+  const int64_t slots = (sh.mb == 4 ? 2 : 3) * 256;   // workgroups resident per CU (Tile::PerCU)
+  const int64_t floor_steps = sh.mb == 4 ? 24 : 40;   // narrow tiles: 24 measured 3% slower than 40
+  const int64_t target = std::max<int64_t>(floor_steps, (units + slots - 1) / slots);
   for (int i = 0; i < count; ++i) {
     const int64_t kt = w[i].k / kBK;
     int64_t s = (kt + target - 1) / target;
@@ -503,6 +633,19 @@ void gemm_plan(int count, const wq_weight *w, int64_t m, int *ksplit) {
     ksplit[i] = (int)s;
   }
 }
+
+namespace {
+template <int BITS>
+hipError_t launch_shape(Shape sh, dim3 grid, dim3 block, const GemmBatch &a, hipStream_t s) {
+  if (sh.mb == 1)
+    hipLaunchKernelGGL((gemm_kernel<BITS, 1, 1>), grid, block, 0, s, a);
+  else if (sh.mb == 2)
+    hipLaunchKernelGGL((gemm_kernel<BITS, 2, 1>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((gemm_kernel<BITS, 4, 2>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+}  // namespace
 
 size_t gemm_partial_bytes(const wq_weight &w, int64_t m, int ksplit) {
   return ksplit > 1 ? (size_t)ksplit * (size_t)m * (size_t)w.n * sizeof(float) : 0;
@@ -516,6 +659,7 @@ hipError_t launch_gemm_batch(int count, const wq_weight *w, const uint16_t *cons
   memset(&a, 0, sizeof a);
   for (int i = 0; i < kMaxBatch; ++i) a.first_tile[i] = INT32_MAX;
   a.count = count;
+  const Shape sh = shape_for(m);
   int64_t tiles = 0, fin_blocks = 0;
   for (int i = 0; i < count; ++i) {
     if (!gemm_available(w[i].bits) || w[i].bits != w[0].bits || w[i].k % kBK) return hipErrorInvalidValue;
@@ -535,8 +679,8 @@ hipError_t launch_gemm_batch(int count, const wq_weight *w, const uint16_t *cons
     L.n = (int32_t)w[i].n;
     L.k = (int32_t)w[i].k;
     L.out_f32 = out_f32[i];
-    L.mtiles = (int32_t)((m + kTM - 1) / kTM);
-    L.ntiles = (int32_t)((w[i].n + kTN - 1) / kTN);
+    L.mtiles = (int32_t)((m + sh.tm() - 1) / sh.tm());
+    L.ntiles = (int32_t)((w[i].n + sh.tn() - 1) / sh.tn());
     const int kt = (int)(w[i].k / kBK);
     L.ksplit = ksplit[i];
     L.ksteps = (kt + ksplit[i] - 1) / ksplit[i];
@@ -549,13 +693,14 @@ hipError_t launch_gemm_batch(int count, const wq_weight *w, const uint16_t *cons
   }
   if (tiles > INT32_MAX) return hipErrorInvalidValue;
   a.tiles = (int32_t)tiles;
+  const dim3 grid((unsigned)tiles), block(kGemmThreads);
+  hipError_t e = hipSuccess;
   switch (w[0].bits) {
-    case 3: hipLaunchKernelGGL(gemm_kernel<3>, dim3((unsigned)tiles), dim3(kGemmThreads), 0, s, a); break;
-    case 4: hipLaunchKernelGGL(gemm_kernel<4>, dim3((unsigned)tiles), dim3(kGemmThreads), 0, s, a); break;
-    case 6: hipLaunchKernelGGL(gemm_kernel<6>, dim3((unsigned)tiles), dim3(kGemmThreads), 0, s, a); break;
-    case 8: hipLaunchKernelGGL(gemm_kernel<8>, dim3((unsigned)tiles), dim3(kGemmThreads), 0, s, a); break;
+    case 3: e = launch_shape<3>(sh, grid, block, a, s); break;
+    case 4: e = launch_shape<4>(sh, grid, block, a, s); break;
+    case 6: e = launch_shape<6>(sh, grid, block, a, s); break;
+    case 8: e = launch_shape<8>(sh, grid, block, a, s); break;
   }
-  hipError_t e = hipGetLastError();
   if (e != hipSuccess || fin_blocks == 0) return e;
   hipLaunchKernelGGL(gemm_finalize_kernel, dim3((unsigned)fin_blocks), dim3(256), 0, s, a);
   return hipGetLastError();

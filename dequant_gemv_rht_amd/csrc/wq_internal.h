@@ -111,7 +111,7 @@ hipError_t launch_unpack(int bits, int64_t n, int64_t k, const uint32_t *packed,
 hipError_t launch_embed(const wq_weight &w, const int32_t *ids, int64_t count, void *out, bool f32, int64_t ldo,
                         hipStream_t s);
 
-// MFMA GEMM for m >= 64 (gemm.hip), one launch for up to kMaxBatch linears
+// MFMA GEMM for m >= 17 (gemm.hip), one launch for up to kMaxBatch linears
 // of one code width.  xr[i]: fp16 activations already rotated (or used as
 // given), [m][ldx[i]].  ksplit[i] > 1 cuts K over that many workgroups whose
 // fp32 partials go to part[i] ([ksplit][m][n], gemm_partial_bytes) and are

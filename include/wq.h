@@ -162,11 +162,11 @@ wq_status rht_apply(const uint16_t *x, uint16_t *y, const uint32_t *signs,
                     void *stream);
 
 /* Bytes of workspace wq_linear needs for this weight and batch size m.
- * 0 means none is needed: m = 1, or the mixed 6/8-bit layout below m = 64.
- * For 2 <= m < 64 with one code width it is the arranged activations of all
- * m batch rows (80 bytes per 32 elements per row, rounded up to 256 bytes);
- * for m >= 64 the matrix-core path's rotated activations and split-K
- * partials.  Returns (size_t)-1 for an invalid request. */
+ * 0 means none is needed: m = 1, or the mixed 6/8-bit layout (any m).
+ * For 2 <= m <= 16 with one code width it is the arranged activations of
+ * all m batch rows (80 bytes per 32 elements per row, rounded up to 256
+ * bytes); for m >= 17 the matrix-core path's rotated activations and
+ * split-K partials.  Returns (size_t)-1 for an invalid request. */
 size_t wq_linear_workspace(const wq_weight *w, int64_t m);
 
 /* The layer: y[m][n] = sum_k (q[n][k] - z[n][g]) * s[n][g] * x'[m][k],
@@ -174,15 +174,17 @@ size_t wq_linear_workspace(const wq_weight *w, int64_t m);
  * set, else x' = x[m].  The scale is applied once per group to the group's
  * partial sum and products accumulate in fp32 (source: "24B0978 - Week 01
  * - Track 2", paragraph on group-wise affine integer quantisation).
- * m < 64 runs the dequantising GEMV; m >= 64 runs the matrix-core GEMM (the
- * weight is dequantised to fp16 in registers before the contraction).  The
+ * m <= 16 runs the dequantising GEMV; m >= 17 runs the matrix-core GEMM
+ * (the weight is dequantised to fp16 in registers before the contraction;
+ * tiles of 32 batch rows up to m = 32, of 64 up to 64, of 128 above).  The
  * rotated activations are rounded to fp16 before the product.  Above one
  * batch row the GEMV first rotates and arranges all m activation rows into
  * the workspace in one pass, then streams the weights once per tile of batch
  * rows: 16 while 13 or more rows are left, else 8 while 5 or more are, else
  * the rest, each where that many rows of arranged activations fit in a
  * workgroup's LDS in up to 4 chunks of K (else the next smaller).  The mixed
- * 6/8-bit layout runs its GEMV in chunks of 16 rows without a workspace.
+ * 6/8-bit layout runs its GEMV (any m, in chunks of 16 rows) without a
+ * workspace.
  *   w          host struct describing the device weight
  *   x          fp16 [m][ldx]
  *   y          out: fp16 or fp32 [m][ldy] (y_dtype)
@@ -199,10 +201,10 @@ wq_status wq_linear(const wq_weight *w, const uint16_t *x, int64_t m, int64_t ld
 
 /* Several independent linears (up to WQ_MAX_BATCH), each with its own
  * weight, activations and output, all at the same batch size m and code
- * width.  For m < 64 they run as one GEMV launch per tile of batch rows
+ * width.  For m <= 16 they run as one GEMV launch per tile of batch rows
  * (tiles as for wq_linear, chosen so that every linear's tile fits in LDS;
  * after, for m > 1, one launch arranging every linear's activations in the
- * workspace).  For m >= 64 with a uniform code width they run as one
+ * workspace).  For m >= 17 with a uniform code width they run as one
  * matrix-core launch (after one launch rotating every linear's
  * activations); the workspace of wq_linear_batch_workspace bytes then holds
  * every linear's rotated activations and split-K partial sums.  The mixed

@@ -125,8 +125,8 @@ def test_workspace_sizes(lib):
     assert lib.wq_linear_workspace(ctypes.byref(_weight()), 1) == 0
     w = _weight(n=4096, k=2560, rht_signs=16, rht_block=128)
     assert lib.wq_linear_workspace(ctypes.byref(w), 1) == 0
-    # 2..63 rows: the arranged activations of all m rows
-    for m in (2, 3, 4, 16, 17, 63):
+    # 2..16 rows: the arranged activations of all m rows
+    for m in (2, 3, 4, 16):
         assert lib.wq_linear_workspace(ctypes.byref(w), m) == _arranged(2560, m)
     # without rotation the activations are still arranged (pair order, sums)
     w_plain = _weight(n=4096, k=2560)
@@ -134,8 +134,9 @@ def test_workspace_sizes(lib):
     # the mixed 6/8-bit layout runs the tiled GEMV, which needs none
     w_mixed = _weight(bits=0, n=128, k=256, block_bits=16, block_off=16)
     assert lib.wq_linear_workspace(ctypes.byref(w_mixed), 16) == 0
-    # the matrix-core path (m >= 64) stages the rotated activations, fp16 [m][k]
-    assert lib.wq_linear_workspace(ctypes.byref(w), 64) >= 64 * 2560 * 2
+    # the matrix-core path (m >= 17) stages the rotated activations, fp16 [m][k]
+    for m in (17, 63, 64):
+        assert lib.wq_linear_workspace(ctypes.byref(w), m) >= m * 2560 * 2
     assert lib.wq_linear_workspace(ctypes.byref(w), 0) == ctypes.c_size_t(-1).value
 
 
@@ -161,8 +162,8 @@ def test_other_entry_points_reject(lib):
 
 
 def test_batch_workspace_for_large_m(lib):
-    # m = 1: no workspace; 2 <= m < 64: every linear's arranged activations
-    # side by side; m >= 64: one matrix-core launch over all the linears,
+    # m = 1: no workspace; 2 <= m <= 16: every linear's arranged activations
+    # side by side; m >= 17: one matrix-core launch over all the linears,
     # whose workspace holds every linear's rotated activations (fp16 [m][k])
     # and the fp32 partial sums of split K
     sg = dict(rht_signs=16, rht_block=128)
@@ -170,7 +171,7 @@ def test_batch_workspace_for_large_m(lib):
     assert lib.wq_linear_batch_workspace(2, arr, 1) == 0
     assert lib.wq_linear_batch_workspace(2, arr, 16) == _arranged(2560, 16) + _arranged(9728, 16)
     assert lib.wq_linear_batch_workspace(2, arr, 5) == _arranged(2560, 5) + _arranged(9728, 5)
-    assert lib.wq_linear_batch_workspace(2, arr, 40) == _arranged(2560, 40) + _arranged(9728, 40)
+    assert lib.wq_linear_batch_workspace(2, arr, 40) >= 40 * (2560 + 9728) * 2
     need = lib.wq_linear_batch_workspace(2, arr, 512)
     assert need >= 512 * (2560 + 9728) * 2
     assert need >= lib.wq_linear_workspace(ctypes.byref(arr[0]), 512)
@@ -184,7 +185,7 @@ def test_batch_workspace_for_large_m(lib):
 
 
 def test_matrix_core_path_workspace_covers_rotated_activations(lib):
-    # m >= 64 rotates the activations into the workspace before the product,
+    # the matrix-core path rotates the activations into the workspace first,
     # so the workspace must hold fp16 [m][k] and a smaller one is refused
     # before anything is launched.
     w = _weight(n=256, k=2560, rht_signs=16, rht_block=128)
@@ -253,3 +254,19 @@ def test_noalloc_refuses_a_call_beyond_its_scratch(lib):
     st = lib.wq_linear_batch_noalloc(1, ctypes.byref(w), xs, lds, 4096, ys, dts, ldys, dq.WQ_FUSE_RHT, None)
     assert st == dq.WQ_E_WORKSPACE
     assert "static scratch" in lib.wq_last_error().decode()
+
+
+@pytest.mark.parametrize("bits", [0, 4])
+def test_grouped_workspace_matches_single_linear(lib, bits):
+    # one linear through the grouped call takes the same path as wq_linear,
+    # so it must reserve the same workspace, at every batch size (a grouped
+    # workspace sized for the GEMV while the call ran the matrix-core path
+    # would be written past its end)
+    kw = dict(bits=bits, n=2560, k=9728, rht_signs=16, rht_block=128)
+    if bits == 0:
+        kw.update(block_bits=16, block_off=16)
+    w = _weight(**kw)
+    for m in (1, 2, 8, 16, 17, 31, 32, 33, 63, 64, 65, 128, 512):
+        single = lib.wq_linear_workspace(ctypes.byref(w), m)
+        group = lib.wq_linear_batch_workspace(1, ctypes.byref(w), m)
+        assert single == group, (bits, m, single, group)

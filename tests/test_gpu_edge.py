@@ -4,7 +4,7 @@
   point, not only an integer) on every kernel that runs a product: the
   batch-1 LDS ring (every width, whole and partial last K segments), the
   batch-1 register stream (K too long for the ring), the batch tiles of 2,
-  8 and 16 rows, the 17..63-row tiles, the tiled kernel (K too long for the
+  8 and 16 rows, the 17..64-row matrix-core tiles, the tiled kernel (K too long for the
   batch tiles), the mixed 6/8 layout at 1, 4, 20 and 64 rows, and the
   matrix-core path.  The model card "24B0978 - Week 01 - Track 2, 20%
   target", section "How these techniques accelerate inference on CUDA",

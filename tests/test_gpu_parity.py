@@ -225,7 +225,8 @@ def test_batch_tiles_of_eight_and_sixteen(m, long_k):
 @pytest.mark.parametrize("bits", [3, 4, 6, 8])
 @pytest.mark.parametrize("m,n,k", [(64, 256, 512), (100, 200, 384), (256, 130, 1024)])
 def test_gemm_bits_and_ragged_shapes(bits, m, n, k):
-    # M >= 64 runs on MFMA; ragged M and N exercise the partial tiles
+    # M >= 17 runs on MFMA (64 rows: tiles of 64; more: of 128); ragged M and
+    # N exercise the partial tiles
     say(f"gemm bits={bits} m={m} n={n} k={k}")
     _run_case(n, k, m, bits, True, False, 7000 + 100 * bits + m)
 
@@ -259,7 +260,7 @@ def test_gemm_trained_scales_and_zeros(bits):
 
 
 def test_gemm_mixed_width_runs_on_gemv():
-    # the mixed-width layout has no matrix-core kernel: M >= 64 takes the
+    # the mixed-width layout has no matrix-core kernel: M >= 17 takes the
     # GEMV in chunks and needs no workspace
     say("mixed m=64")
     n, k, m = 192, 512, 64
@@ -272,11 +273,20 @@ def test_gemm_mixed_width_runs_on_gemv():
     check_close(dq.wq_linear(qw, dev(x)).float().cpu().numpy(), ref, "mixed m=64")
 
 
+@pytest.mark.parametrize("bits", [3, 4, 6, 8])
+@pytest.mark.parametrize("m", [17, 32, 33, 64])
+@pytest.mark.parametrize("k", [640, 9728])
+def test_gemm_mid_batch_tiles(bits, m, k):
+    # 17..32 rows: tiles of 32 batch rows x 128 outputs; 33..64: 64 x 128.
+    # N = 130 leaves a partial last tile (two outputs of a 32-wide block) and
+    # K = 9728 is cut over workgroups (split-K partials added afterwards)
+    say(f"gemm mid batch bits={bits} m={m} k={k}")
+    _run_case(130, k, m, bits, True, k == 9728, 8000 + 10 * bits + m + k)
+
+
 @pytest.mark.parametrize("m", [17, 29, 40, 63])
 def test_linear_mid_batch(m):
-    # 17..63 rows: one arrangement of all rows, then tiles of 16, 8 and the
-    # rest (63 = 16 + 16 + 16 + 8 + 4 + 3; 17 = 16 + 1, the last row on the
-    # batch-1 kernel)
+    # 17..63 rows: the matrix-core path (narrow tiles of 32 or 64 rows)
     say(f"linear mid batch m={m}")
     _run_case(96, 512, m, 4, True, False, m)
     _run_case(300, 2560, m, 3, True, True, m + 1)
@@ -284,7 +294,8 @@ def test_linear_mid_batch(m):
 
 @pytest.mark.parametrize("m", [20, 40, 63])
 def test_linear_batch_mid_m_grouped(m):
-    # 17..63 rows in one grouped call: every linear's tiles in one launch
+    # 17..63 rows in one grouped call: every linear's tiles in one
+    # matrix-core launch
     say(f"batch mid m={m}")
     shapes = [(256, 2560), (64, 1024), (130, 9728)]
     qs, xs, refs = [], [], []
