@@ -171,16 +171,6 @@ __device__ __forceinline__ void unpack_pairs(const uint32_t (&w)[BITS], UnpackCo
   if constexpr (P + 1 < 16) unpack_pairs<BITS, P + 1>(w, c, p);
 }
 
-// int3 and int6: the factor 2^s of the low and high half of pair e
-template <int BITS>
-__host__ __device__ constexpr float up_lo(int e) {
-  return BITS == 3 ? ((e & 1) ? 128.f : 16.f) : 16.f;
-}
-template <int BITS>
-__host__ __device__ constexpr float up_hi(int e) {
-  return BITS == 3 ? ((e & 1) ? 8.f : 1.f) : 1.f;
-}
-
 // fp16 activation pairs in the order unpack_pairs produces code pairs (the
 // lane's 8 values are codes 8o..8o+7 of its 32-code slice, octet o), each
 // pre-multiplied by 2^-s of its code's position, and their contribution to
@@ -193,39 +183,25 @@ __device__ __forceinline__ void pairs_in_dot_order(const float (&v)[8], uint32_t
     constexpr float k16 = 0.0625f;
     o[0] = pack_half2(v[0], v[4]); o[1] = pack_half2(v[1] * k16, v[5] * k16);
     o[2] = pack_half2(v[2], v[6]); o[3] = pack_half2(v[3] * k16, v[7] * k16);
-    const float a = half_bits_to_float(o[0] & 0xFFFF) + half_bits_to_float(o[0] >> 16) +
-                    half_bits_to_float(o[2] & 0xFFFF) + half_bits_to_float(o[2] >> 16);
-    const float b = half_bits_to_float(o[1] & 0xFFFF) + half_bits_to_float(o[1] >> 16) +
-                    half_bits_to_float(o[3] & 0xFFFF) + half_bits_to_float(o[3] >> 16);
-    x_eff = a + 16.0f * b;
-    x_st = a + b;
   } else if constexpr (BITS == 8) {
     o[0] = pack_half2(v[0], v[2]); o[1] = pack_half2(v[1], v[3]);
     o[2] = pack_half2(v[4], v[6]); o[3] = pack_half2(v[5], v[7]);
-    float a = 0.f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) a += half_bits_to_float(o[e] & 0xFFFF) + half_bits_to_float(o[e] >> 16);
-    x_eff = a;
-    x_st = a;
+  } else if constexpr (BITS == 3) {
+    o[0] = pack_half2(v[0] * 0.0625f, v[4]); o[1] = pack_half2(v[1] * 0.0078125f, v[5] * 0.125f);
+    o[2] = pack_half2(v[2] * 0.0625f, v[6]); o[3] = pack_half2(v[3] * 0.0078125f, v[7] * 0.125f);
   } else {
-    if constexpr (BITS == 3) {
-      o[0] = pack_half2(v[0] * 0.0625f, v[4]); o[1] = pack_half2(v[1] * 0.0078125f, v[5] * 0.125f);
-      o[2] = pack_half2(v[2] * 0.0625f, v[6]); o[3] = pack_half2(v[3] * 0.0078125f, v[7] * 0.125f);
-    } else {
-      o[0] = pack_half2(v[0] * 0.0625f, v[2]); o[1] = pack_half2(v[1] * 0.0625f, v[3]);
-      o[2] = pack_half2(v[4] * 0.0625f, v[6]); o[3] = pack_half2(v[5] * 0.0625f, v[7]);
-    }
-    // sums of the stored halves that share one factor 2^s back to the
-    // values meant: low halves of the even and odd pairs, high halves likewise
-    float lo[2] = {0.f, 0.f}, hi[2] = {0.f, 0.f};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      lo[e & 1] += half_bits_to_float(o[e] & 0xFFFF);
-      hi[e & 1] += half_bits_to_float(o[e] >> 16);
-    }
-    x_eff = up_lo<BITS>(0) * lo[0] + up_lo<BITS>(1) * lo[1] + up_hi<BITS>(0) * hi[0] + up_hi<BITS>(1) * hi[1];
-    x_st = (lo[0] + lo[1]) + (hi[0] + hi[1]);
+    o[0] = pack_half2(v[0] * 0.0625f, v[2]); o[1] = pack_half2(v[1] * 0.0625f, v[3]);
+    o[2] = pack_half2(v[4] * 0.0625f, v[6]); o[3] = pack_half2(v[5] * 0.0625f, v[7]);
   }
+  // The sums of the stored values, as stored (XS) and times each one's 2^s
+  // back to the values meant (X), by v_dot2 against fp16 pairs of those
+  // powers of two: the products are exact, the sums fp32.
+  // Factors (low half, high half) of the even pairs 0, 2 and the odd pairs 1, 3:
+  constexpr uint32_t f_even = BITS == 3 || BITS == 6 ? 0x3C004C00u : 0x3C003C00u;   // (16, 1) or (1, 1)
+  constexpr uint32_t f_odd = BITS == 4 ? 0x4C004C00u : BITS == 3 ? 0x48005800u : f_even;   // (16, 16), (128, 8)
+  constexpr uint32_t one = 0x3C003C00u, fe = f_even, fo = f_odd;
+  x_st = dot2(o[3], one, dot2(o[2], one, dot2(o[1], one, dot2(o[0], one, 0.0f))));
+  x_eff = dot2(o[3], fo, dot2(o[2], fe, dot2(o[1], fo, dot2(o[0], fe, 0.0f))));
 }
 
 __device__ __forceinline__ void store_out(const LinDesc &L, int m, int row, float v) {
@@ -640,7 +616,9 @@ struct Ring {
   static constexpr int codes = 2 * row;                             // code bytes per wave per step
   static constexpr int ni = (codes + 1023) / 1024;                  // loads per step (flat)
   static constexpr int slot = codes + 2 * 64 * 4;                   // + scales, zeros
-  static constexpr int depth = BITS == 3 ? 4 : BITS == 4 ? 3 : 2;  // steps in flight
+  // steps in flight (deeper rings measured slower: int4 depth 4, 5, 6 took
+  // 13.7, 14.2, 14.9 us against 12.2 us for the seven-projection block)
+  static constexpr int depth = BITS == 3 ? 4 : BITS == 4 ? 3 : 2;
   static constexpr int q = (flat ? ni : 2 * nc) + 2;               // vector loads per wave per step
   // workgroup size: 8 waves for the narrow codes (their steps are short and
   // a smaller workgroup starts sooner), 16 for int6 and int8
@@ -743,16 +721,14 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // Wait until at most n * Q vector loads are outstanding (n < R, uniform).
-template <int R, int Q>
+template <int R, int Q, int J = R - 1>
 __device__ __forceinline__ void wait_vmcnt_younger(int n) {
-  if constexpr (R > 3) {
-    if (n >= 3) { wait_vmcnt<3 * Q>(); return; }
+  if constexpr (J == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (n >= J) { wait_vmcnt<J * Q>(); return; }
+    wait_vmcnt_younger<R, Q, J - 1>(n);
   }
-  if constexpr (R > 2) {
-    if (n == 2) { wait_vmcnt<2 * Q>(); return; }
-  }
-  if (n == 1) { wait_vmcnt<Q>(); return; }
-  wait_vmcnt<0>();
 }
 
 __device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
@@ -970,8 +946,17 @@ __device__ __forceinline__ void stream_ring(const LinDesc &L, const uint32_t *co
   if constexpr (R > 1) cur.template issue<1>();
   if constexpr (R > 2) cur.template issue<2>();
   if constexpr (R > 3) cur.template issue<3>();
+  if constexpr (R > 4) cur.template issue<4>();
+  if constexpr (R > 5) cur.template issue<5>();
+  static_assert(R <= 6, "ring depth");
 
-  // 3. the rotation into LDS
+  // 3. the rotation into LDS.  (A compute unit holds a limited number of
+  // outstanding vector memory instructions, so the second wave on each SIMD
+  // meets the first waves' ring loads and starts rotating about a memory
+  // latency later.  Letting those waves rotate before issuing their steps,
+  // or a barrier between every wave's activation loads and the ring loads,
+  // measured slower for the int3 and int4 blocks, and much slower for the
+  // 16-wave int6 ring.)
 #pragma unroll
   for (int q = 0; q < XC; ++q) {
     consume(xr[q], sw[q]);
@@ -1062,6 +1047,8 @@ __device__ __forceinline__ void stream_ring(const LinDesc &L, const uint32_t *co
     if constexpr (R > 1) if (i0 + 1 < steps) step(std::integral_constant<int, 1>{}, i0 + 1);
     if constexpr (R > 2) if (i0 + 2 < steps) step(std::integral_constant<int, 2>{}, i0 + 2);
     if constexpr (R > 3) if (i0 + 3 < steps) step(std::integral_constant<int, 3>{}, i0 + 3);
+    if constexpr (R > 4) if (i0 + 4 < steps) step(std::integral_constant<int, 4>{}, i0 + 4);
+    if constexpr (R > 5) if (i0 + 5 < steps) step(std::integral_constant<int, 5>{}, i0 + 5);
   }
   wait_vmcnt<0>();    // no load may still be writing LDS when the workgroup ends
   __syncthreads();

@@ -234,6 +234,54 @@ __device__ __forceinline__ void xstage_fma(float (&v)[8], float beta) {
   for (int e = 0; e < 8; ++e) v[e] = fmaf(dpp<CTRL>(v[e]), beta, v[e]);
 }
 
+// The four cross-lane stages as fused DPP multiply-adds in one statement:
+// v_fmac_f32_dpp takes the partner lane's value as its first source, so a
+// stage is 8 instructions (the lane ^ 4 stage 16: two DPP moves make that
+// partner).  Written with separate moves the compiler needs a move and a
+// wait state per element and stage.  Hazards: a DPP source must be written
+// at least two instructions before it is read; inside the statement every
+// value is read 8 instructions after its write, the leading s_nop covers
+// the writes just before it and the trailing one a DPP read of an output
+// right after it.
+__device__ __forceinline__ void fwht_xstages_dpp(float (&v)[8], float b1, float b2, float b4, float b8) {
+#define WQ_X8(CTRL, B)                                                   \
+  "v_fmac_f32_dpp %0, %0, " B " " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
+  "v_fmac_f32_dpp %1, %1, " B " " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
+  "v_fmac_f32_dpp %2, %2, " B " " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
+  "v_fmac_f32_dpp %3, %3, " B " " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
+  "v_fmac_f32_dpp %4, %4, " B " " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
+  "v_fmac_f32_dpp %5, %5, " B " " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
+  "v_fmac_f32_dpp %6, %6, " B " " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
+  "v_fmac_f32_dpp %7, %7, " B " " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+  float t[8];
+  asm volatile(
+      "s_nop 1\n\t"
+      WQ_X8("quad_perm:[1,0,3,2]", "%16")
+      WQ_X8("quad_perm:[2,3,0,1]", "%17")
+      "v_mov_b32_dpp %8, %0 row_half_mirror row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_mov_b32_dpp %9, %1 row_half_mirror row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_mov_b32_dpp %10, %2 row_half_mirror row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_mov_b32_dpp %11, %3 row_half_mirror row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_mov_b32_dpp %12, %4 row_half_mirror row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_mov_b32_dpp %13, %5 row_half_mirror row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_mov_b32_dpp %14, %6 row_half_mirror row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_mov_b32_dpp %15, %7 row_half_mirror row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_fmac_f32_dpp %0, %8, %18 quad_perm:[3,2,1,0] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_fmac_f32_dpp %1, %9, %18 quad_perm:[3,2,1,0] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_fmac_f32_dpp %2, %10, %18 quad_perm:[3,2,1,0] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_fmac_f32_dpp %3, %11, %18 quad_perm:[3,2,1,0] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_fmac_f32_dpp %4, %12, %18 quad_perm:[3,2,1,0] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_fmac_f32_dpp %5, %13, %18 quad_perm:[3,2,1,0] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_fmac_f32_dpp %6, %14, %18 quad_perm:[3,2,1,0] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_fmac_f32_dpp %7, %15, %18 quad_perm:[3,2,1,0] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      WQ_X8("row_ror:8", "%19")
+      "s_nop 1"
+      : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7]),
+        "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3]), "=&v"(t[4]), "=&v"(t[5]), "=&v"(t[6]), "=&v"(t[7])
+      : "v"(b1), "v"(b2), "v"(b4), "v"(b8));
+#undef WQ_X8
+}
+
 __device__ __forceinline__ void fwht128_row16_signed(float (&v)[8], int jj) {
 #pragma unroll
   for (int h = 1; h < 8; h <<= 1) {
@@ -246,14 +294,10 @@ __device__ __forceinline__ void fwht128_row16_signed(float (&v)[8], int jj) {
       }
     }
   }
-  xstage_fma<kQuadXor1>(v, (jj & 1) ? -1.0f : 1.0f);
-  xstage_fma<kQuadXor2>(v, (jj & 2) ? -1.0f : 1.0f);
-  {
-    const float beta = (jj & 4) ? -1.0f : 1.0f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = fmaf(dpp_xor4(v[e]), beta, v[e]);
-  }
-  xstage_fma<kRowRor8>(v, (jj & 8) ? -1.0f : 1.0f);
+#if defined(__HIP_DEVICE_COMPILE__)
+  fwht_xstages_dpp(v, (jj & 1) ? -1.0f : 1.0f, (jj & 2) ? -1.0f : 1.0f, (jj & 4) ? -1.0f : 1.0f,
+                   (jj & 8) ? -1.0f : 1.0f);
+#endif
 }
 
 __device__ __forceinline__ float fwht_lane_sign(int jj) {
