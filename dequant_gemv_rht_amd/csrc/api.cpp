@@ -300,18 +300,21 @@ wq_status launch_tile(int count, const wq_weight *w, const uint16_t *const *x, c
   bool ring = false;
   bool stream = plan_stream(count, ws, m, rotate, wg, rpw, &slds, &ring);
   if (!stream && count == 1 && w[0].bits == 0 && m == 1) {
-    // mixed 6/8 at batch 1: the ring, each workgroup inside one 64-row block
-    const int64_t nblk = w[0].n / WQ_MIXED_ROWS;
-    int64_t wpb = device_cus() / nblk;
-    wpb = wpb < 1 ? 1 : (wpb > WQ_MIXED_ROWS / 2 ? WQ_MIXED_ROWS / 2 : wpb);
-    const int r = (int)((WQ_MIXED_ROWS + wpb - 1) / wpb);
-    const int need = wq::gemv_stream_lds_bytes(0, 1, w[0].k, r, true);
-    if (need <= kMaxLds && nblk * wpb <= INT32_MAX) {
+    // mixed 6/8 at batch 1: the rings, each workgroup inside one 64-row
+    // block.  One workgroup per CU spread over the blocks by their code
+    // words, where every block then gets one (an 8-bit block has 4/3 the
+    // words of a 6-bit one: at most 3/4 as many blocks as CUs), and at
+    // least 2 rows each; else one workgroup per block.
+    const int64_t nblk = w[0].n / WQ_MIXED_ROWS, ncu = device_cus();
+    const bool spread = 4 * nblk <= 3 * ncu;
+    const int64_t wgs = spread ? (ncu < 32 * nblk ? ncu : 32 * nblk) : nblk;
+    const int need = wq::gemv_stream_lds_bytes(0, 1, w[0].k, WQ_MIXED_ROWS, true);
+    if (need <= kMaxLds && wgs <= INT32_MAX) {
       stream = ring = true;
       slds = need;
-      rpw[0] = r;
-      wg[0] = (int)(nblk * wpb);
-      a.mixed_wpb = (int32_t)wpb;
+      rpw[0] = WQ_MIXED_ROWS;
+      wg[0] = (int)wgs;
+      a.mixed_wpb = spread ? 0 : 1;
     }
   }
   int64_t tiles = 0;

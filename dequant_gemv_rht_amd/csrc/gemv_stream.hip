@@ -15,8 +15,9 @@
 //   * gemv_ring_kernel: batch 1.  Rotates its linear's activations once into
 //     LDS, streams the weights through an LDS ring by direct buffer-to-LDS
 //     loads (section "Batch 1" below).
-//   * gemv_ring_mixed_kernel: batch 1 over the mixed 6/8-bit layout, one
-//     64-row block of uniform width per workgroup.
+//   * gemv_ring_mixed_kernel: batch 1 over the mixed 6/8-bit layout: each
+//     workgroup inside one 64-row block of uniform width, on that width's
+//     ring, the blocks getting workgroups in proportion to their bytes.
 //   * gemv_stream_kernel: batch 1 when the ring does not fit in LDS: codes
 //     prefetched into registers.
 //   * xprep_kernel + gemv_quad_kernel: batch tiles of 2, 4, 8 or 16 rows
@@ -608,6 +609,11 @@ __device__ __forceinline__ void stream_rows(const LinDesc &L, const uint32_t *co
 // lanes 0..31; int6: three), read from g's task.  Lane j of DPP row g finds
 // row r of its slice at byte 256 BITS r + 64 BITS g + 4 BITS j of the
 // region.
+// Workgroup size of every ring: 8 waves.  (16-wave rings for int6 and int8
+// measured slower: 7.57 against 6.81 us for an int6 9728 -> 2560 linear;
+// an 8-bit 16-wave ring does not fit beside a long K's activations.)
+constexpr int kRingThreads = 512;
+
 template <int BITS>
 struct Ring {
   static constexpr bool flat = BITS == 3 || BITS == 6;
@@ -617,12 +623,12 @@ struct Ring {
   static constexpr int ni = (codes + 1023) / 1024;                  // loads per step (flat)
   static constexpr int slot = codes + 2 * 64 * 4;                   // + scales, zeros
   // steps in flight (deeper rings measured slower: int4 depth 4, 5, 6 took
-  // 13.7, 14.2, 14.9 us against 12.2 us for the seven-projection block)
+  // 13.7, 14.2, 14.9 us against 12.2 us for the seven-projection block; int6
+  // and int8 depth 3 8.56 and 9.66 us against 6.81 and 8.00 us for a
+  // 9728 -> 2560 linear)
   static constexpr int depth = BITS == 3 ? 4 : BITS == 4 ? 3 : 2;
   static constexpr int q = (flat ? ni : 2 * nc) + 2;               // vector loads per wave per step
-  // workgroup size: 8 waves for the narrow codes (their steps are short and
-  // a smaller workgroup starts sooner), 16 for int6 and int8
-  static constexpr int threads = (BITS == 3 || BITS == 4) ? 512 : 1024;
+  static constexpr int threads = kRingThreads;
   static constexpr int waves = threads / 64;
 };
 
@@ -634,7 +640,7 @@ typedef __attribute__((address_space(3))) void *lds_ptr_t;
 // a raw buffer load does not include the scalar offset.
 template <int BITS, int C = 0>
 __device__ __forceinline__ void ring_row_loads(rsrc_t rc, uint32_t row, uint32_t off) {
-  using RS = Ring<BITS>;
+  using RS = Ring<BITS>;   // nc does not depend on the workgroup size
 #if defined(__HIP_DEVICE_COMPILE__)   // 16-byte LDS loads exist only in the gfx950 pass
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (lds_ptr_t)(row + 1024 * C), 16, off + 16 * C, 0, 0, kNT);
 #endif
@@ -856,18 +862,50 @@ __device__ __forceinline__ void consume(u32x4 a, uint32_t b) { asm volatile("" :
 // not for its vector loads (the ring's loads stay in flight across it).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// Activation items per DPP row whose loads precede the weight stream (the
+// rest are loaded while rotating).  int4: 3, so that a K = 9728 linear's 76
+// blocks on 32 DPP rows are all requested ahead of the ring (measured 6.76
+// -> 6.36 us for down_proj).
+template <int BITS>
+constexpr int kActAhead = BITS == 3 ? 2 : 3;
+
+// The activation loads a ring workgroup issues before anything else: loads
+// complete in order, so activations requested after the weight stream would
+// wait for it.  Item it = rg + RG q is rotation block it; lane j of DPP row
+// rg holds its elements 8j .. 8j + 7 and the sign word that covers them.
+// Without signs the sign range is empty and the loads read zero.
+template <int XC>
+struct ActAhead {
+  u32x4 xr[XC];
+  uint32_t sw[XC];
+};
+
+template <int XC>
+__device__ __forceinline__ void act_ahead_loads(const LinDesc &L, ActAhead<XC> &a) {
+  constexpr int RG = kRingThreads / 16;
+  const int t = threadIdx.x, rg = t >> 4, j = t & 15;
+  const int items = L.k / kGroup;
+  const rsrc_t rx = make_rsrc(L.x, (uint32_t)L.k * 2);
+  const rsrc_t rsg = make_rsrc(L.signs, L.signs ? (uint32_t)(L.k / 8) : 0u);
+#pragma unroll
+  for (int q = 0; q < XC; ++q) {
+    const int it = rg + RG * q;
+    const bool ok = it < items;
+    a.xr[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, ok ? (uint32_t)(256 * it + 16 * j) : kOOB, 0, 0));
+    a.sw[q] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsg, ok ? (uint32_t)(16 * it + 4 * (j >> 2)) : kOOB, 0, 0);
+  }
+}
+
 template <int BITS, bool FULL>
 // r0: the workgroup's first row; codes0: that row's code words (the rows
-// that follow are consecutive at BITS * k / 32 words each).
+// that follow are consecutive at BITS * k / 32 words each); ahead: the
+// activation loads act_ahead_loads issued.
 __device__ __forceinline__ void stream_ring(const LinDesc &L, const uint32_t *codes0, int r0, int rows,
-                                            uint32_t *smem) {
+                                            uint32_t *smem, const ActAhead<kActAhead<BITS>> &ahead) {
   using RS = Ring<BITS>;
   constexpr int R = RS::depth, Q = RS::q;
   constexpr int TH = RS::threads, RG = TH / 16;   // threads, DPP rows
-  // activation items per DPP row whose loads precede the weight stream
-  // (int4: 3, so that a K = 9728 linear's 76 blocks on 32 DPP rows are all
-  // requested ahead of the ring; measured 6.76 -> 6.36 us for down_proj)
-  constexpr int XC = BITS == 4 ? 3 : 2;
+  constexpr int XC = kActAhead<BITS>;
   const int t = threadIdx.x, rg = t >> 4, j = t & 15, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int K = L.k, KS = (K + kSeg - 1) / kSeg, G = K / kGroup, S = K / kSlice;
@@ -879,23 +917,9 @@ __device__ __forceinline__ void stream_ring(const LinDesc &L, const uint32_t *co
   float *part = reinterpret_cast<float *>(lds + lay.part);
   const int steps = (T + RG - 1) / RG;   // steps of this workgroup (uniform)
   const int nb = K / kGroup, items = nb;
-
-  // 1. activations and signs first: loads complete in order, so activations
-  //    requested after the weight stream would wait for it.  Item it = rg +
-  //    64 q is rotation block it; lane j holds its elements 8j .. 8j + 7.
-  //    Without signs the sign range is empty and the loads read zero.
   const rsrc_t rx = make_rsrc(L.x, (uint32_t)K * 2);
   const rsrc_t rsg = make_rsrc(L.signs, L.signs ? (uint32_t)(K / 8) : 0u);
   const bool rotate = L.signs != nullptr;
-  u32x4 xr[XC];
-  uint32_t sw[XC];
-#pragma unroll
-  for (int q = 0; q < XC; ++q) {
-    const int it = rg + RG * q;
-    const bool ok = it < items;
-    xr[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, ok ? (uint32_t)(256 * it + 16 * j) : kOOB, 0, 0));
-    sw[q] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsg, ok ? (uint32_t)(16 * it + 4 * (j >> 2)) : kOOB, 0, 0);
-  }
 
   // 2. the weight stream's cursor.  Task tau = rg + 64 i is (row pair
   //    tau / KS, segment tau % KS); quotients by KS of numbers up to 64 are
@@ -959,8 +983,8 @@ __device__ __forceinline__ void stream_ring(const LinDesc &L, const uint32_t *co
   // 16-wave int6 ring.)
 #pragma unroll
   for (int q = 0; q < XC; ++q) {
-    consume(xr[q], sw[q]);
-    rotate_item<BITS, 1>(rotate, xr[q], sw[q], nb, items, rg + RG * q, j, xp, S);
+    consume(ahead.xr[q], ahead.sw[q]);
+    rotate_item<BITS, 1>(rotate, ahead.xr[q], ahead.sw[q], nb, items, rg + RG * q, j, xp, S);
   }
   for (int it0 = RG * XC; it0 < items; it0 += RG) {
     const int it = it0 + rg;
@@ -1537,13 +1561,16 @@ __global__ __launch_bounds__(kXprepThreads) void xprep_kernel(XprepBatch a) {
 }
 
 template <int BITS, bool FULL>
-__global__ __launch_bounds__(Ring<BITS>::threads) void gemv_ring_kernel(GemvArgs a) {
+__global__ __launch_bounds__(kRingThreads) void gemv_ring_kernel(GemvArgs a) {
   extern __shared__ uint32_t smem[];
   const int w = blockIdx.x;
   const LinDesc L = fetch_desc(a, w);
   const int r0 = (w - L.tile_begin) * L.rows_per_wg;
   if (r0 >= L.n) return;
-  stream_ring<BITS, FULL>(L, L.codes + (size_t)r0 * (L.k / kSlice) * BITS, r0, min(L.rows_per_wg, L.n - r0), smem);
+  ActAhead<kActAhead<BITS>> ahead;
+  act_ahead_loads(L, ahead);
+  stream_ring<BITS, FULL>(L, L.codes + (size_t)r0 * (L.k / kSlice) * BITS, r0, min(L.rows_per_wg, L.n - r0), smem,
+                          ahead);
 }
 
 
@@ -1567,27 +1594,77 @@ __global__ __launch_bounds__(kStreamThreads) void gemv_stream_kernel(GemvArgs a)
   stream_rows<BITS, MT, Depth<BITS, MT>::d>(L, L.codes + (size_t)r0 * (L.k / kSlice) * BITS, a.m, r0, rows, smem);
 }
 
-// The mixed 6/8-bit layout at batch 1: workgroup w streams rows of one
-// 64-row block (mixed_wpb workgroups per block), so the code width is
-// uniform across it.  6-bit blocks take the LDS ring; 8-bit blocks the
-// register-prefetch stream (an 8-bit ring for a long K needs more LDS than
-// a compute unit has).
+// The mixed 6/8-bit layout at batch 1: every workgroup streams rows of one
+// 64-row block, so the code width is uniform across it, on the LDS ring of
+// that width.  With mixed_wpb == 0 the grid's G workgroups are spread over
+// the blocks in proportion to their code words: workgroup w belongs to the
+// block b with F(off[b]) <= w < F(off[b + 1]), F(o) = floor(G o / off[nblk]),
+// so an 8-bit block gets 4/3 the workgroups of a 6-bit one and every
+// workgroup streams about the same bytes; the block's rows are split evenly
+// among its workgroups.  (The host takes this only when every block gets
+// at least one workgroup: G >= 4/3 blocks.)  With mixed_wpb == 1 each
+// workgroup takes one whole block.  The activation loads go out first, so
+// the search for the block overlaps them.
+static_assert(kActAhead<6> == kActAhead<8>, "both widths take the same activation loads");
+
 template <bool FULL>
-__global__ __launch_bounds__(kStreamThreads) void gemv_ring_mixed_kernel(GemvArgs a) {
-  static_assert(Ring<6>::threads == kStreamThreads, "the 6-bit ring runs in this kernel's workgroup");
+__global__ __launch_bounds__(kRingThreads) void gemv_ring_mixed_kernel(GemvArgs a) {
   extern __shared__ uint32_t smem[];
   const int w = blockIdx.x;
   const LinDesc L = fetch_desc(a, w);
-  const int blk = w / a.mixed_wpb, sub = w - blk * a.mixed_wpb;
-  const int r0 = kMixedRows * blk + sub * L.rows_per_wg;
-  const int rows = min(min(L.rows_per_wg, kMixedRows * (blk + 1) - r0), L.n - r0);
+  ActAhead<kActAhead<6>> ahead;
+  act_ahead_loads(L, ahead);
+  const int nblk = L.n / kMixedRows, g = w - L.tile_begin;
+  int blk, r0, rows, bits;
+  uint64_t off;
+  if (a.mixed_wpb == 1) {
+    blk = g;
+    r0 = 0;
+    rows = kMixedRows;
+    bits = L.block_bits[blk];
+    off = L.block_off[blk];
+  } else {
+    // each wave finds its block by itself: 64 blocks per pass, one lane
+    // each, which also reads its block's width and first word
+    const int lane = threadIdx.x & 63;
+    const double G = (double)a.tiles, tot = (double)L.block_off[nblk];
+    int lo = 0, hi = 0, bl = 0;
+    uint64_t o0 = 0;
+    blk = -1;
+    for (int c = 0; c < nblk; c += 64) {
+      const int b = c + lane;
+      lo = hi = INT32_MAX;
+      if (b < nblk) {
+        o0 = L.block_off[b];
+        bl = L.block_bits[b];
+        lo = (int)floor((double)o0 * G / tot);
+        hi = (int)floor((double)L.block_off[b + 1] * G / tot);
+      }
+      const uint64_t hit = __ballot(lo <= g && g < hi);
+      if (hit) {
+        const int l = __builtin_ctzll(hit);
+        blk = c + l;
+        lo = __shfl(lo, l);
+        hi = __shfl(hi, l);
+        bl = __shfl(bl, l);
+        o0 = ((uint64_t)(uint32_t)__shfl((int)(o0 >> 32), l) << 32) | (uint32_t)__shfl((int)(uint32_t)o0, l);
+        break;
+      }
+    }
+    if (blk < 0) return;
+    const int wb = hi - lo, sub = g - lo;
+    r0 = kMixedRows * sub / wb;
+    rows = kMixedRows * (sub + 1) / wb - r0;
+    bits = bl;
+    off = o0;
+  }
   if (rows <= 0) return;
-  const int bits = L.block_bits[blk];
-  const uint32_t *codes0 = L.codes + L.block_off[blk] + (size_t)(r0 - kMixedRows * blk) * (L.k / kSlice) * bits;
+  const uint32_t *codes0 = L.codes + off + (size_t)r0 * (L.k / kSlice) * bits;
+  r0 += kMixedRows * blk;
   if (bits == 8)
-    stream_rows<8, 1, Depth<8, 1>::d>(L, codes0, 1, r0, rows, smem);
+    stream_ring<8, FULL>(L, codes0, r0, rows, smem, ahead);
   else
-    stream_ring<6, FULL>(L, codes0, r0, rows, smem);
+    stream_ring<6, FULL>(L, codes0, r0, rows, smem, ahead);
 }
 
 // Segments of code loads a lane keeps in flight (4 rows x BITS words each);
@@ -1629,9 +1706,9 @@ hipError_t launch_bits(int mt, const GemvArgs &a, hipStream_t s) {
     bool full = true;
     for (int i = 0; i < a.count; ++i) full = full && a.lin[i].k % kSeg == 0;
     if (full)
-      hipLaunchKernelGGL((gemv_ring_kernel<BITS, true>), dim3(a.tiles), dim3(Ring<BITS>::threads), a.lds_bytes, s, a);
+      hipLaunchKernelGGL((gemv_ring_kernel<BITS, true>), dim3(a.tiles), dim3(kRingThreads), a.lds_bytes, s, a);
     else
-      hipLaunchKernelGGL((gemv_ring_kernel<BITS, false>), dim3(a.tiles), dim3(Ring<BITS>::threads), a.lds_bytes, s, a);
+      hipLaunchKernelGGL((gemv_ring_kernel<BITS, false>), dim3(a.tiles), dim3(kRingThreads), a.lds_bytes, s, a);
     return hipGetLastError();
   }
   switch (mt) {
@@ -1658,10 +1735,9 @@ int gemv_stream_lds_bytes(int bits, int mt, int64_t k, int rows_per_wg, bool rin
   if (!ring) return stream_lds(mt, (int)S, (int)KS, (int)G, (int)np).total * 4;
   if (mt != 1) return 1 << 30;
   switch (bits) {
-    case 0: {   // mixed 6/8: room for the 6-bit ring and the 8-bit stream
-      const int l6 = ring_lds((int)S, (int)KS, (int)np, Ring<6>::slot, Ring<6>::depth, Ring<6>::waves).total;
-      const int l8 = stream_lds(1, (int)S, (int)KS, (int)G, (int)np).total * 4;
-      return l6 > l8 ? l6 : l8;
+    case 0: {   // mixed 6/8: room for either ring (the 8-bit one is the larger)
+      using R8 = Ring<8>;
+      return ring_lds((int)S, (int)KS, (int)np, R8::slot, R8::depth, R8::waves).total;
     }
     case 3: return ring_lds((int)S, (int)KS, (int)np, Ring<3>::slot, Ring<3>::depth, Ring<3>::waves).total;
     case 4: return ring_lds((int)S, (int)KS, (int)np, Ring<4>::slot, Ring<4>::depth, Ring<4>::waves).total;
@@ -1705,11 +1781,11 @@ hipError_t launch_xprep(int bits, int count, const uint16_t *const *x, const int
 
 hipError_t launch_gemv_stream(int bits, int mt, const GemvArgs &a, hipStream_t s) {
   if (bits == 0) {
-    if (!a.ring || mt != 1 || a.count != 1 || a.mixed_wpb <= 0) return hipErrorInvalidValue;
+    if (!a.ring || mt != 1 || a.count != 1 || a.mixed_wpb < 0 || a.mixed_wpb > 1) return hipErrorInvalidValue;
     if (a.lin[0].k % kSeg == 0)
-      hipLaunchKernelGGL((gemv_ring_mixed_kernel<true>), dim3(a.tiles), dim3(kStreamThreads), a.lds_bytes, s, a);
+      hipLaunchKernelGGL((gemv_ring_mixed_kernel<true>), dim3(a.tiles), dim3(kRingThreads), a.lds_bytes, s, a);
     else
-      hipLaunchKernelGGL((gemv_ring_mixed_kernel<false>), dim3(a.tiles), dim3(kStreamThreads), a.lds_bytes, s, a);
+      hipLaunchKernelGGL((gemv_ring_mixed_kernel<false>), dim3(a.tiles), dim3(kRingThreads), a.lds_bytes, s, a);
     return hipGetLastError();
   }
   if (a.ring || mt < 2) {

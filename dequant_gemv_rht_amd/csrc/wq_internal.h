@@ -60,7 +60,8 @@ struct GemvArgs {
   int32_t tiles;                // total workgroups
   int32_t lds_bytes;            // dynamic LDS per workgroup
   int32_t ring;                 // stream kernel, batch 1: weights staged through an LDS ring
-  int32_t mixed_wpb;            // batch-1 ring over the mixed 6/8-bit layout: workgroups per 64-row block
+  int32_t mixed_wpb;            // batch-1 ring over the mixed 6/8-bit layout: 1 = one workgroup per
+                                // 64-row block, 0 = workgroups spread over the blocks by code words
 };
 
 // The calling thread's message for wq_last_error (api.cpp): set_error

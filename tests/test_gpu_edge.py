@@ -71,9 +71,10 @@ MIXED_SEL = np.array([6, 8, 8, 6, 6], np.uint8)
 TRAINED_PATHS = (
     [(f"ring b{b}", b, 200, 1024, 1) for b in (3, 4, 6, 8)]
     + [(f"ring partial segment b{b}", b, 130, 1152, 1) for b in (3, 4, 6, 8)]
-    # K too long for the ring's LDS at one batch row: the register stream
-    + [("stream b3", 3, 64, 49152, 1), ("stream b4", 4, 64, 49152, 1), ("stream b6", 6, 64, 24576, 1),
-       ("stream b8", 8, 64, 9728, 1)]
+    # K too long for the ring's LDS at one batch row (its activations take
+    # 2.5 bytes per element beside 57 to 74 KB of ring): the register stream
+    + [("stream b3", 3, 64, 49152, 1), ("stream b4", 4, 64, 49152, 1), ("stream b6", 6, 64, 49152, 1),
+       ("stream b8", 8, 64, 36864, 1)]
     + [(f"tile 8 b{b}", b, 136, 1152, 6) for b in (3, 4, 6, 8)]
     + [(f"tile 16 b{b}", b, 136, 1152, 16) for b in (3, 4, 6, 8)]
     + [("mid 24 b4", 4, 96, 2560, 24), ("mid 40 b6", 6, 72, 1152, 40)]
@@ -92,8 +93,8 @@ def test_trained_scales_and_zeros(label, bits, n, k, m):
 @pytest.mark.parametrize("m", [1, 4, 20, 64])
 @pytest.mark.parametrize("k", [1024, 1152])
 def test_trained_scales_and_zeros_mixed(m, k):
-    # batch 1: 6-bit blocks on the ring, 8-bit blocks on the register stream
-    # (K = 1152: a partial last segment); above: the tiled mixed kernel
+    # batch 1: each block on the ring of its width (K = 1152: a partial last
+    # segment); above: the tiled mixed kernel
     say(f"trained s,z: mixed m={m} k={k}")
     _case(320, k, m, 0, trained=True, sel=MIXED_SEL, seed=600 + m + k, label=f"mixed m={m} k={k}")
 
@@ -136,7 +137,7 @@ def test_activation_magnitude_gemm(mag):
 @pytest.mark.parametrize("bits", [4, 8])
 def test_activation_magnitude_stream(bits, mag):
     # batch 1 with K too long for the ring
-    k = 49152 if bits == 4 else 9728
+    k = 49152 if bits == 4 else 36864
     say(f"activation magnitude stream bits={bits} k={k} {mag}")
     _case(64, k, 1, bits, seed=860 + bits, label=f"stream bits={bits} {mag}", **mag)
 
@@ -170,3 +171,24 @@ def test_grouped_mixed_width_batch(m):
     for (n, k, _), y, ref in zip(shapes, dq.wq_linear_batch(qs, xs), refs):
         rel, mx = check_close(y.float().cpu().numpy(), ref, f"grouped mixed n={n} k={k} m={m}")
         say(f"  n={n} k={k}: rel-L2 {rel:.2e} max/rms {mx:.2e}")
+
+
+# Batch 1 over the mixed layout: the workgroups are spread over the 64-row
+# blocks in proportion to their code words while every block still gets one
+# (up to 3/4 as many blocks as compute units), else one workgroup per block.
+# One block (32 workgroups of 2 rows), all-8-bit blocks, a random mix of 150
+# blocks, and 200 blocks (one workgroup each).
+MIXED_LAYOUTS = [("one block", np.array([8], np.uint8), 1024),
+                 ("all 8", np.full(4, 8, np.uint8), 2560),
+                 ("150 random", None, 1024),
+                 ("200 random, one workgroup per block", None, 1024)]
+
+
+@pytest.mark.parametrize("label,sel,k", MIXED_LAYOUTS, ids=[c[0] for c in MIXED_LAYOUTS])
+def test_mixed_batch1_block_spread(label, sel, k):
+    rng = np.random.default_rng(970 + k)
+    if sel is None:
+        nblk = 150 if label.startswith("150") else 200
+        sel = np.where(rng.random(nblk) < 0.3, 8, 6).astype(np.uint8)
+    say(f"mixed batch 1: {label} ({len(sel)} blocks, {int((sel == 8).sum())} of 8 bits) k={k}")
+    _case(64 * len(sel), k, 1, 0, sel=sel, seed=980 + len(sel), label=label)
