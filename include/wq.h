@@ -77,7 +77,11 @@ typedef enum wq_status {
   WQ_E_HIP = -5           /* the HIP runtime reported an error */
 } wq_status;
 
-typedef enum wq_dtype { WQ_F16 = 1, WQ_F32 = 2 } wq_dtype;
+/* Output element types.  A plain 32-bit integer rather than an enum type,
+ * so that any value a caller passes is a defined value for the library to
+ * check (and refuse with WQ_E_ARG); the same size as an enum in the C ABI. */
+typedef int32_t wq_dtype;
+enum { WQ_F16 = 1, WQ_F32 = 2 };
 
 /* wq_linear flag: rotate the activations (per 128-block, with the weight's
  * signs) inside the product.  Without it, x is used as given. */
