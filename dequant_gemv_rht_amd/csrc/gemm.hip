@@ -35,7 +35,18 @@
 // into the low half and the high nibble into bits 4..7 of the high half, each
 // over 1024.0's bit pattern (1024 + q, 1024 + 16 q); int8: v_perm_b32 places
 // two bytes next to 0x64 bytes; int3/int6: bit fields spread over the two
-// halves -- then q exactly with one packed fma, q - z and times s in fp16.
+// halves -- then q exactly with one packed fma and q - z in fp16 (exact
+// for an integer zero point, which round-to-nearest quantisation always
+// gives).
+//
+// Scales.  The products of a group of 128 are (q - z) x in fp32; the group's
+// scale s multiplies their sum, not the weight, so the weight is never
+// rounded to fp16 with its scale.  Instead of a second accumulator per group
+// the accumulator is kept in units of the current group's scale: at the
+// first step of a group it is multiplied by s_prev / s (one multiply per
+// accumulator per group), and the epilogue multiplies it by the last scale.
+// A group whose scale is 0 contributes nothing: its operand is masked to 0
+// and the units stay those of the previous group.
 //
 // MFMA operand layout (checked on the device): lane l holds A[l % 32][8 (l /
 // 32) .. +8] and B[8 (l / 32) .. +8][l % 32]; accumulator register v of lane
@@ -172,12 +183,14 @@ __device__ __forceinline__ uint32_t code_pair(const uint32_t (&w)[BITS], PairCon
   }
 }
 
-// The lane's B operand of 16-k block kk: codes 8 kk .. 8 kk + 7 of its slice,
-// dequantised: q = h c + d exactly (c, d per half remove the 1024 offset and
-// the int4 factor 16), then (q - z) s.
+// The lane's B operand of 16-k block kk: codes 8 kk .. 8 kk + 7 of its slice
+// as q - z: q = h c + d exactly (c, d per half remove the 1024 offset and
+// the int4 factor 16), then q - z, exact for an integer zero point and
+// rounded once otherwise.  The scale is not applied here: the accumulator
+// carries it (see the step below).  For a group whose scale is 0, c, d and
+// z come in as 0 and the operand is 0.
 template <int BITS, int KK>
-__device__ __forceinline__ half8 b_operand(const uint32_t (&w)[BITS], PairConsts k, half2v c, half2v d, half2v z,
-                                           half2v s) {
+__device__ __forceinline__ half8 b_operand(const uint32_t (&w)[BITS], PairConsts k, half2v c, half2v d, half2v z) {
   uint32_t p[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -189,7 +202,7 @@ __device__ __forceinline__ half8 b_operand(const uint32_t (&w)[BITS], PairConsts
       default: h = code_pair<BITS, 4 * KK + 3>(w, k); break;
     }
     const half2v q = __builtin_elementwise_fma(as_h2(h), c, d);
-    p[i] = as_u32((q - z) * s);
+    p[i] = as_u32(q - z);
   }
   return __builtin_bit_cast(half8, u32x4{p[0], p[1], p[2], p[3]});
 }
@@ -416,6 +429,11 @@ __global__ __launch_bounds__(kGemmThreads, (Tile<MB, NB>::PerCU)) void gemm_kern
   // step past the range only skips the products), so every iteration of the
   // loop has the same loads in flight and the compiler's own waits for the
   // weight registers stay as loose as this step's explicit one.
+  // unit[j]: the scale the accumulators of the lane's row j are counted in
+  float unit[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) unit[j] = 1.0f;
+
   auto step = [&](auto sconst, int kt, bool active) {
     constexpr int st = decltype(sconst)::value;
     constexpr int nx = (st + kAhead) % kStages;
@@ -433,17 +451,27 @@ __global__ __launch_bounds__(kGemmThreads, (Tile<MB, NB>::PerCU)) void gemm_kern
       read_step_narrow<st * kAStage, MB>(sz_rd0 + gofs, a_rd, szv[0], aall);
     else
       read_sz<NB>(sz_rd0 + gofs, sz_rd1 + gofs, szv);
+    // the first step of a group (or of the workgroup's K range): the
+    // accumulators change units from the previous group's scale to this one's
+    const bool gstart = (kt & 1) == 0 || kt == kt0;
     half8 bop[NB][4];
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
-      const half2v s = as_h2((szv[j] & 0xFFFFu) * 0x10001u);
-      const half2v z = as_h2((szv[j] >> 16) * 0x10001u);
-      const half2v c = {(_Float16)1.0f, kHi};
-      const half2v d = {(_Float16)-1024.0f, (_Float16)(BITS == 4 ? -64.0f : -1024.0f)};
-      bop[j][0] = b_operand<BITS, 0>(cw[st][j], pk, c, d, z, s);
-      bop[j][1] = b_operand<BITS, 1>(cw[st][j], pk, c, d, z, s);
-      bop[j][2] = b_operand<BITS, 2>(cw[st][j], pk, c, d, z, s);
-      bop[j][3] = b_operand<BITS, 3>(cw[st][j], pk, c, d, z, s);
+      const float sf = half_bits_to_float(szv[j] & 0xFFFFu);
+      const bool live = sf != 0.0f;
+      if (gstart) {
+        const float r = live ? unit[j] / sf : 1.0f;
+        unit[j] = live ? sf : unit[j];
+#pragma unroll
+        for (int i = 0; i < MB; ++i) acc[i][j] *= r;
+      }
+      const half2v z = live ? as_h2((szv[j] >> 16) * 0x10001u) : half2v{};
+      const half2v c = live ? half2v{(_Float16)1.0f, kHi} : half2v{};
+      const half2v d = live ? half2v{(_Float16)-1024.0f, (_Float16)(BITS == 4 ? -64.0f : -1024.0f)} : half2v{};
+      bop[j][0] = b_operand<BITS, 0>(cw[st][j], pk, c, d, z);
+      bop[j][1] = b_operand<BITS, 1>(cw[st][j], pk, c, d, z);
+      bop[j][2] = b_operand<BITS, 2>(cw[st][j], pk, c, d, z);
+      bop[j][3] = b_operand<BITS, 3>(cw[st][j], pk, c, d, z);
     }
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
@@ -518,7 +546,7 @@ __global__ __launch_bounds__(kGemmThreads, (Tile<MB, NB>::PerCU)) void gemm_kern
       for (int v = 0; v < 16; ++v) {
         const int row = m0 + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
         if (row < L.m && col < L.n) {
-          const float r = acc[i][j][v];
+          const float r = acc[i][j][v] * unit[j];
           if (L.ksplit > 1) {
             L.part[((size_t)ks * L.m + row) * L.n + col] = r;
           } else if (L.out_f32) {

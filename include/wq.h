@@ -179,9 +179,11 @@ size_t wq_linear_workspace(const wq_weight *w, int64_t m);
  * partial sum and products accumulate in fp32 (source: "24B0978 - Week 01
  * - Track 2", paragraph on group-wise affine integer quantisation).
  * m <= 16 runs the dequantising GEMV; m >= 17 runs the matrix-core GEMM
- * (the weight is dequantised to fp16 in registers before the contraction;
- * tiles of 32 batch rows up to m = 32, of 64 up to 64, of 128 above).  The
- * rotated activations are rounded to fp16 before the product.  Above one
+ * (the codes become q - z in fp16 registers, exact for an integer zero
+ * point and rounded once otherwise, and each group's scale multiplies the
+ * fp32 accumulator; tiles of 32 batch rows up to m = 32, of 64 up to 64, of
+ * 128 above).  The rotated activations are rounded to fp16 before the
+ * product.  Above one
  * batch row the GEMV first rotates and arranges all m activation rows into
  * the workspace in one pass, then streams the weights once per tile of batch
  * rows: 16 while 13 or more rows are left, else 8 while 5 or more are, else

@@ -12,11 +12,8 @@
   same kernels must take them.
 * Activations far from N(0, 1): RMS 1e-2, 1e-3 and 1e-4, and large values
   (RMS 256 with 1% of the channels x64), for every width at 1, 4 and 16
-  rows, the mixed layout and the matrix-core path; and batch rows of very
-  different magnitudes in one call.  The matrix-core path rounds the
-  dequantised weight to fp16 as well (its operands are fp16), and on the
-  outlier-heavy large case that second rounding takes its max-abs just over
-  the bound: that case is an expected failure, stated where it is declared.
+  rows, the mixed layout and the matrix-core path (its 32-, 64- and
+  128-row tiles); and batch rows of very different magnitudes in one call.
 * Grouped calls over several mixed-width linears.
 
 The oracle gets the same fp16 activations, codes, scales and zeros; outputs
@@ -118,19 +115,25 @@ def test_activation_magnitude_mixed(m, mag):
     _case(320, 1024, m, 0, sel=MIXED_SEL, seed=800 + m, label=f"mixed m={m} {mag}", **mag)
 
 
-GEMM_HEAVY_TAIL = pytest.param(
-    LARGE, id="large",
-    marks=pytest.mark.xfail(strict=True, reason=(
-        "the matrix cores take fp16 operands, so this path rounds the dequantised weight (q - z) s to fp16 "
-        "on top of the rotated activations; with 1% of the channels x64 the two roundings alone reach "
-        "max-abs 4.28e-3 x RMS on these inputs (fp64 emulation), over the 4e-3 bound (rel-L2 5.3e-4 passes)")))
-
-
-@pytest.mark.parametrize("mag", MAGNITUDES[:3] + [dict(rms=256.0), GEMM_HEAVY_TAIL],
+@pytest.mark.parametrize("mag", MAGNITUDES[:3] + [dict(rms=256.0), LARGE],
                          ids=MAG_IDS[:3] + ["large-no-outliers", "large"])
 def test_activation_magnitude_gemm(mag):
     say(f"activation magnitude gemm m=64 {mag}")
     _case(130, 640, 64, 4, seed=850, label=f"gemm m=64 {mag}", **mag)
+
+
+@pytest.mark.parametrize("m", [24, 128])
+@pytest.mark.parametrize("bits", [4, 8])
+def test_heavy_tail_gemm_tiles(bits, m):
+    # the 32-row and 128-row matrix-core tiles on the outlier-heavy large
+    # activations: the weight enters the product as q - z (exact for RTN's
+    # integer zero points) and the group's scale multiplies the fp32
+    # accumulator, so only the rotated activations are rounded to fp16.
+    # fp32 outputs: on these inputs a true output can exceed fp16's range
+    # (71475 for bits=8, m=128), where an fp16 output is rightly inf.
+    say(f"heavy-tailed activations gemm bits={bits} m={m}")
+    _case(136, 1152, m, bits, seed=870 + bits + m, out_f32=True, label=f"gemm heavy tail bits={bits} m={m}",
+          **LARGE)
 
 
 @pytest.mark.parametrize("mag", MAGNITUDES, ids=MAG_IDS)
@@ -192,3 +195,32 @@ def test_mixed_batch1_block_spread(label, sel, k):
         sel = np.where(rng.random(nblk) < 0.3, 8, 6).astype(np.uint8)
     say(f"mixed batch 1: {label} ({len(sel)} blocks, {int((sel == 8).sum())} of 8 bits) k={k}")
     _case(64 * len(sel), k, 1, 0, sel=sel, seed=980 + len(sel), label=label)
+
+
+@pytest.mark.parametrize("m", [1, 4, 24, 128])
+@pytest.mark.parametrize("bits", [4, 8])
+def test_scale_extremes(bits, m):
+    # groups whose scale is 0 (also a row's first group, and runs of them),
+    # fp16 subnormal scales and scales 10^7 apart each count exactly as
+    # s (q - z) x: on the GEMV (m = 1, 4) and on the matrix cores (m = 24,
+    # 128), whose accumulator is kept in units of the current group's scale
+    say(f"scale extremes bits={bits} m={m}")
+    n, k = 136, 1280
+    rng = np.random.default_rng(990 + bits + m)
+    w = W.weight(k, n, rng)
+    x = W.activations(m, k, rng)
+    signs = W.sign_bits(k, rng)
+    q, s, z = OR.prepare(w, signs, bits)
+    choices = np.array([0.0, 2.0 ** -24, 2.0 ** -14, 1e-3, 1.0, 300.0], np.float16)
+    s = choices[rng.integers(0, len(choices), size=s.shape)]
+    s[0, :] = 0                       # a row with no live group
+    s[1, 0] = 0                       # a row whose first group is dead
+    s[2, 1:4] = 0                     # a run of dead groups
+    s[3, :] = np.float16(2.0 ** -24)  # only subnormal scales
+    ref = OL.linear(q, s, z, x, signs)
+    packed, _ = dq.wq_pack(dev(q), bits)
+    qw = dq.QWeight(bits, n, k, packed, dev(s), dev(z), dev_u32(signs))
+    y = dq.wq_linear(qw, dev(x), torch.float32).cpu().numpy()
+    assert np.all(y[:, 0] == 0)
+    rel, mx = check_close(y, ref, f"scale extremes bits={bits} m={m}")
+    say(f"  rel-L2 {rel:.2e} max/rms {mx:.2e}")
