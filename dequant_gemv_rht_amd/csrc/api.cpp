@@ -376,6 +376,15 @@ wq_status check_io(const wq_weight &w, const uint16_t *x, int64_t m, int64_t ldx
   if (ldx % 8) return fail(WQ_E_ALIGN, "%s: ldx must be a multiple of 8 (16-byte rows)", who);
   if (ldy < w.n) return fail(WQ_E_ARG, "%s: ldy=%lld < n=%lld", who, (long long)ldy, (long long)w.n);
   if (ydt != WQ_F16 && ydt != WQ_F32) return fail(WQ_E_ARG, "%s: y_dtype must be WQ_F16 or WQ_F32", who);
+  // every kernel addresses a linear's activations, codes, scales and zeros
+  // with 32-bit buffer offsets: refuse here, before anything is launched,
+  // what they could not reach
+  if ((uint64_t)m * (uint64_t)ldx * 2 >= ((uint64_t)1 << 31))
+    return fail(WQ_E_UNSUPPORTED, "%s: m * ldx * 2 = %llu bytes of activations (at most 2^31 - 1)", who,
+                (unsigned long long)((uint64_t)m * (uint64_t)ldx * 2));
+  if (w.k >= ((int64_t)1 << 27)) return fail(WQ_E_UNSUPPORTED, "%s: k=%lld (below 2^27)", who, (long long)w.k);
+  if ((uint64_t)w.n * (uint64_t)w.k * (uint64_t)(w.bits ? w.bits : 8) / 8 >= ((uint64_t)1 << 32))
+    return fail(WQ_E_UNSUPPORTED, "%s: n x k codes above 4 GiB", who);
   return WQ_OK;
 }
 

@@ -200,6 +200,13 @@ size_t wq_linear_workspace(const wq_weight *w, int64_t m);
  *              path the rotated activations and the fp32 partial sums when
  *              it splits a long K over several workgroups.  Its contents
  *              need no initialisation and are not preserved.
+ * Errors (all before anything is launched): WQ_E_ARG (NULL pointer, m <= 0,
+ * ldx < k, ldy < n, bad y_dtype or flags, bad weight descriptor),
+ * WQ_E_ALIGN (a pointer not 16-byte aligned, ldx not a multiple of 8),
+ * WQ_E_UNSUPPORTED (bits, group or rht_block not supported; m * ldx * 2
+ * of 2^31 bytes or more, k of 2^27 or more, or n x k codes above 4 GiB:
+ * the kernels address them with 32-bit offsets), WQ_E_WORKSPACE (workspace
+ * smaller than wq_linear_workspace); WQ_E_HIP if a launch fails.
  */
 wq_status wq_linear(const wq_weight *w, const uint16_t *x, int64_t m, int64_t ldx,
                     void *y, wq_dtype y_dtype, int64_t ldy, uint32_t flags,

@@ -270,3 +270,28 @@ def test_grouped_workspace_matches_single_linear(lib, bits):
         single = lib.wq_linear_workspace(ctypes.byref(w), m)
         group = lib.wq_linear_batch_workspace(1, ctypes.byref(w), m)
         assert single == group, (bits, m, single, group)
+
+
+def test_sizes_beyond_32_bit_offsets_are_refused_before_launch(lib):
+    # the kernels address activations, codes, scales and zeros with 32-bit
+    # buffer offsets: larger requests are refused on the host, on the
+    # batch-tile, batch-1 and matrix-core paths alike (nothing is launched:
+    # no GPU here)
+    for m, ldx, k in ((1, 1 << 30, 256), (4, 1 << 28, 256), (64, 1 << 24, 256), (512, 1 << 21, 256)):
+        w = _weight(k=k, rht_signs=16, rht_block=128)
+        st = lib.wq_linear(ctypes.byref(w), 16, m, ldx, 16, dq.WQ_F16, 64, dq.WQ_FUSE_RHT, 16, 1 << 50, None)
+        assert st == dq.WQ_E_UNSUPPORTED, (m, ldx, lib.wq_last_error())
+        assert "activations" in lib.wq_last_error().decode()
+    w = _weight(k=1 << 27)
+    st = lib.wq_linear(ctypes.byref(w), 16, 1, 1 << 27, 16, dq.WQ_F16, 64, 0, 16, 1 << 50, None)
+    assert st == dq.WQ_E_UNSUPPORTED and "k=" in lib.wq_last_error().decode()
+    w = _weight(bits=8, n=1 << 20, k=1 << 12)
+    st = lib.wq_linear(ctypes.byref(w), 16, 64, 1 << 12, 16, dq.WQ_F16, 1 << 20, 0, 16, 1 << 50, None)
+    assert st == dq.WQ_E_UNSUPPORTED and "4 GiB" in lib.wq_last_error().decode()
+    arr = (dq.WqWeight * 2)(_weight(), _weight(k=1 << 27))
+    xs = (ctypes.c_void_p * 2)(16, 16)
+    lds = (ctypes.c_int64 * 2)(256, 1 << 27)
+    ys = (ctypes.c_void_p * 2)(16, 16)
+    dts = (ctypes.c_int32 * 2)(dq.WQ_F16, dq.WQ_F16)
+    ldy = (ctypes.c_int64 * 2)(64, 64)
+    assert lib.wq_linear_batch(2, arr, xs, lds, 1, ys, dts, ldy, 0, 16, 1 << 50, None) == dq.WQ_E_UNSUPPORTED
