@@ -24,6 +24,7 @@ import os
 from dataclasses import dataclass
 from typing import Optional, Sequence
 
+import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -45,7 +46,8 @@ class WqWeight(ctypes.Structure):
                 ("n", ctypes.c_int64), ("k", ctypes.c_int64),
                 ("codes", _vp), ("scales", _vp), ("zeros", _vp),
                 ("block_bits", _vp), ("block_off", _vp),
-                ("rht_signs", _vp), ("rht_block", ctypes.c_int32)]
+                ("rht_signs", _vp), ("rht_block", ctypes.c_int32),
+                ("block_bits_host", _vp)]
 
 
 SIGNATURES = {
@@ -129,11 +131,20 @@ class QWeight:
     signs: Optional[torch.Tensor] = None       # int32 view of uint32 [k/32]
     block_bits: Optional[torch.Tensor] = None  # uint8 [n/64]
     block_off: Optional[torch.Tensor] = None   # int64 view of uint64 [n/64 + 1]
+    # mixed width: also hand the library a host copy of block_bits (made
+    # once, here), so the batch-1 kernel need not read the block table first
+    host_widths: bool = True
+
+    def __post_init__(self):
+        self._bits_host = None
+        if self.bits == 0 and self.block_bits is not None and self.host_widths:
+            self._bits_host = np.ascontiguousarray(self.block_bits.cpu().numpy(), dtype=np.uint8)
 
     def c_struct(self) -> WqWeight:
+        bh = self._bits_host.ctypes.data if self._bits_host is not None else None
         return WqWeight(self.bits, 128, self.n, self.k, _ptr(self.codes), _ptr(self.scales),
                         _ptr(self.zeros), _ptr(self.block_bits), _ptr(self.block_off),
-                        _ptr(self.signs), 128 if self.signs is not None else 0)
+                        _ptr(self.signs), 128 if self.signs is not None else 0, bh)
 
 
 def wq_packed_words(bits: int, n: int, k: int, block_bits_host=None) -> int:

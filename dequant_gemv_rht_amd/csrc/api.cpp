@@ -74,6 +74,11 @@ wq_status check_weight(const wq_weight *w, const char *who) {
                                           (long long)w->n);
     if (!w->block_bits || !w->block_off)
       return fail(WQ_E_ARG, "%s: mixed width needs block_bits and block_off", who);
+    if (w->block_bits_host)
+      for (int64_t b = 0; b < w->n / WQ_MIXED_ROWS; ++b)
+        if (w->block_bits_host[b] != 6 && w->block_bits_host[b] != 8)
+          return fail(WQ_E_ARG, "%s: block_bits_host[%lld]=%d (6 or 8)", who, (long long)b,
+                      (int)w->block_bits_host[b]);
   }
   if (w->rht_signs) {
     if (w->rht_block != WQ_RHT_BLOCK)
@@ -282,6 +287,39 @@ wq_status run_gemv(int count, const wq_weight *w, const uint16_t *const *x, cons
   return WQ_OK;
 }
 
+// Every workgroup of a mixed 6/8 layout at batch 1, placed from the host
+// copy of the widths as the kernel's own search would: runs of same-width
+// blocks get the workgroups w with F(off[bs]) <= w < F(off[be]),
+// F(o) = floor(G o / total words), and split their row pairs evenly.
+// rec[w] = first code word | (first row | 8-bit << 31) << 32; rec[G] = n
+// rows.  False where a workgroup would get more than the 64 rows the
+// launch sizes the LDS for (not with one workgroup or more per block).
+bool mixed_table(const wq_weight &w, int G, uint64_t *rec) {
+  const int64_t nblk = w.n / WQ_MIXED_ROWS;
+  const uint8_t *bits = w.block_bits_host;
+  uint64_t tot = 0;
+  for (int64_t b = 0; b < nblk; ++b) tot += 2 * (uint64_t)w.k * bits[b];
+  uint64_t off = 0;
+  for (int64_t bs = 0, be; bs < nblk; bs = be) {
+    uint64_t words = 0;
+    for (be = bs; be < nblk && bits[be] == bits[bs]; ++be) words += 2 * (uint64_t)w.k * bits[be];
+    const int64_t lo = (int64_t)((unsigned __int128)off * (unsigned)G / tot);
+    const int64_t hi = (int64_t)((unsigned __int128)(off + words) * (unsigned)G / tot);
+    const int64_t pairs = (int64_t)(WQ_MIXED_ROWS / 2) * (be - bs), wr = hi - lo;
+    const uint64_t row_words = (uint64_t)w.k * bits[bs] / 32;
+    if (wr < 1) return false;
+    for (int64_t sub = 0; sub < wr; ++sub) {
+      const int64_t q0 = pairs * sub / wr, q1 = pairs * (sub + 1) / wr;
+      if (2 * (q1 - q0) > WQ_MIXED_ROWS) return false;
+      const uint64_t row = (uint64_t)(WQ_MIXED_ROWS * bs + 2 * q0), word = off + 2 * (uint64_t)q0 * row_words;
+      rec[lo + sub] = word | ((row | (bits[bs] == 8 ? (uint64_t)1 << 31 : 0)) << 32);
+    }
+    off += words;
+  }
+  rec[G] = (uint64_t)w.n << 32;
+  return true;
+}
+
 // One launch over `count` linears for a batch tile of m <= 16 rows.  xq:
 // the tile's arranged activations per linear, or NULL where the kernel
 // rotates for itself.
@@ -299,12 +337,14 @@ wq_status launch_tile(int count, const wq_weight *w, const uint16_t *const *x, c
   int wg[WQ_MAX_BATCH], rpw[WQ_MAX_BATCH], slds = 0;
   bool ring = false;
   bool stream = plan_stream(count, ws, m, rotate, wg, rpw, &slds, &ring);
+  bool table = false;   // mixed at batch 1, workgroups placed here from the host widths
   if (!stream && count == 1 && w[0].bits == 0 && m == 1) {
-    // mixed 6/8 at batch 1: the rings, each workgroup inside one 64-row
-    // block.  One workgroup per CU spread over the blocks by their code
-    // words, where every block then gets one (an 8-bit block has 4/3 the
-    // words of a 6-bit one: at most 3/4 as many blocks as CUs), and at
-    // least 2 rows each; else one workgroup per block.
+    // mixed 6/8 at batch 1: the rings, each workgroup on rows of one width
+    // (within a run of same-width blocks).  One workgroup per CU spread over
+    // the runs by their code words, where every block then gets one (an
+    // 8-bit block has 4/3 the words of a 6-bit one: at most 3/4 as many
+    // blocks as CUs), and at least 2 rows each, at most 64; else one
+    // workgroup per block.
     const int64_t nblk = w[0].n / WQ_MIXED_ROWS, ncu = device_cus();
     const bool spread = 4 * nblk <= 3 * ncu;
     const int64_t wgs = spread ? (ncu < 32 * nblk ? ncu : 32 * nblk) : nblk;
@@ -315,6 +355,7 @@ wq_status launch_tile(int count, const wq_weight *w, const uint16_t *const *x, c
       rpw[0] = WQ_MIXED_ROWS;
       wg[0] = (int)wgs;
       a.mixed_wpb = spread ? 0 : 1;
+      table = spread && w[0].block_bits_host && wgs <= wq::kMixedTableWgs;
     }
   }
   int64_t tiles = 0;
@@ -358,6 +399,15 @@ wq_status launch_tile(int count, const wq_weight *w, const uint16_t *const *x, c
   }
   if (tiles > INT32_MAX) return fail(WQ_E_UNSUPPORTED, "wq_linear: too many workgroups");
   a.tiles = (int32_t)tiles;
+  if (table) {
+    wq::MixedArgs ma;
+    memset(&ma, 0, sizeof ma);
+    ma.lin = a.lin[0];
+    ma.tiles = a.tiles;
+    ma.lds_bytes = slds;
+    if (mixed_table(w[0], a.tiles, ma.wg))
+      return hip_status(wq::launch_gemv_mixed_table(ma, s), "wq_linear");
+  }
   if (stream) {
     a.lds_bytes = slds;
     a.ring = ring ? 1 : 0;

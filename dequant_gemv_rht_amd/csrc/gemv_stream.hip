@@ -1595,73 +1595,161 @@ __global__ __launch_bounds__(kStreamThreads) void gemv_stream_kernel(GemvArgs a)
 }
 
 // The mixed 6/8-bit layout at batch 1: every workgroup streams rows of one
-// 64-row block, so the code width is uniform across it, on the LDS ring of
-// that width.  With mixed_wpb == 0 the grid's G workgroups are spread over
-// the blocks in proportion to their code words: workgroup w belongs to the
-// block b with F(off[b]) <= w < F(off[b + 1]), F(o) = floor(G o / off[nblk]),
-// so an 8-bit block gets 4/3 the workgroups of a 6-bit one and every
-// workgroup streams about the same bytes; the block's rows are split evenly
-// among its workgroups.  (The host takes this only when every block gets
-// at least one workgroup: G >= 4/3 blocks.)  With mixed_wpb == 1 each
-// workgroup takes one whole block.  The activation loads go out first, so
-// the search for the block overlaps them.
+// width, on the LDS ring of that width.  Blocks of one width that follow
+// each other form a run, whose rows lie one after another at one row
+// stride: a run is one uniform-width matrix.  With mixed_wpb == 0 the
+// grid's G workgroups are spread over the runs in proportion to their code
+// words: run [bs, be) gets the workgroups w with F(off[bs]) <= w <
+// F(off[be]), F(o) = floor(G o / off[nblk]), and its row pairs are split
+// evenly among them, so every workgroup streams about the same bytes in
+// about as many ring steps as the uniform kernel takes for that width.
+// (Splitting each 64-row block on its own instead left 10- and 11-row
+// workgroups beside each other; 11 rows are 6 row pairs, a ring step more
+// than 5: the all-6-bit layout took 8.85 us against 6.70 us for the same
+// matrix on the uniform kernel.)  The host takes this only when every
+// block gets at least one workgroup (G >= 4/3 blocks), so every run does.
+// With mixed_wpb == 1 each workgroup takes one whole block.  Without the
+// caller's host copy of the widths the kernel finds its run in the block
+// table; with it, the host places the workgroups
+// (gemv_ring_mixed_table_kernel).
 static_assert(kActAhead<6> == kActAhead<8>, "both widths take the same activation loads");
+
+// One pass of the run search over blocks c .. c + 63, one lane per block:
+// its width, its predecessor's width and its first word.
+struct MixedPass {
+  int bits, prev;
+  uint64_t off;
+};
+
+__device__ __forceinline__ MixedPass mixed_pass_loads(const LinDesc &L, int nblk, int c) {
+  const int b = c + (int)(threadIdx.x & 63);
+  MixedPass p{0, 0, 0};
+  if (b < nblk) {
+    p.bits = L.block_bits[b];
+    p.prev = b > 0 ? L.block_bits[b - 1] : 0;
+    p.off = L.block_off[b];
+  }
+  return p;
+}
+
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, int l) {
+  return ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(v >> 32), l) << 32) |
+         (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+}
 
 template <bool FULL>
 __global__ __launch_bounds__(kRingThreads) void gemv_ring_mixed_kernel(GemvArgs a) {
   extern __shared__ uint32_t smem[];
-  const int w = blockIdx.x;
-  const LinDesc L = fetch_desc(a, w);
+  const int g = blockIdx.x;   // one linear: its workgroups are the grid
+  const LinDesc L = a.lin[0];
+  asm volatile("" ::"s"(L.codes), "s"(L.scales), "s"(L.zeros), "s"(L.signs), "s"(L.x), "s"(L.y), "s"(L.n),
+               "s"(L.k), "s"(L.block_bits), "s"(L.block_off), "s"(a.tiles), "s"(a.mixed_wpb));
+  const int nblk = L.n / kMixedRows;
+  const bool spread = a.mixed_wpb == 0;
+  // The block table's loads (the search's first pass, or the block of a
+  // one-block workgroup) go out before the activations: vector loads
+  // return in order, and the two ways to the run meet before the ring
+  // starts, where the compiler waits for every vector load either issued.
+  // Every other value the search needs comes from the lanes holding it.
+  // (Even so the search holds the ring back: the all-6-bit down_proj takes
+  // 7.5 us here against 6.7 us for the same rows placed by the host in
+  // gemv_ring_mixed_table_kernel.)
+  MixedPass p0{0, 0, 0};
+  uint64_t tot = 0, off1 = 0;
+  int bits1 = 0;
+  if (!spread) {
+    bits1 = L.block_bits[g];
+    off1 = L.block_off[g];
+  } else {
+    p0 = mixed_pass_loads(L, nblk, 0);
+    tot = L.block_off[nblk];
+  }
+  asm volatile("" ::: "memory");
   ActAhead<kActAhead<6>> ahead;
   act_ahead_loads(L, ahead);
-  const int nblk = L.n / kMixedRows, g = w - L.tile_begin;
   int blk, r0, rows, bits;
   uint64_t off;
-  if (a.mixed_wpb == 1) {
+  if (!spread) {
     blk = g;
     r0 = 0;
     rows = kMixedRows;
-    bits = L.block_bits[blk];
-    off = L.block_off[blk];
+    bits = bits1;
+    off = off1;
   } else {
-    // each wave finds its block by itself: 64 blocks per pass, one lane
-    // each, which also reads its block's width and first word
+    // bs: the last run start with F(off[bs]) <= w; be: the first run start
+    // after it (nblk, at word tot, if none)
     const int lane = threadIdx.x & 63;
-    const double G = (double)a.tiles, tot = (double)L.block_off[nblk];
-    int lo = 0, hi = 0, bl = 0;
-    uint64_t o0 = 0;
-    blk = -1;
+    const double G = (double)a.tiles, T = (double)tot;
+    int bs = -1, be = nblk;
+    uint64_t off_e = tot;
+    off = 0;
+    bits = 0;
     for (int c = 0; c < nblk; c += 64) {
-      const int b = c + lane;
-      lo = hi = INT32_MAX;
-      if (b < nblk) {
-        o0 = L.block_off[b];
-        bl = L.block_bits[b];
-        lo = (int)floor((double)o0 * G / tot);
-        hi = (int)floor((double)L.block_off[b + 1] * G / tot);
+      const MixedPass p = c == 0 ? p0 : mixed_pass_loads(L, nblk, c);
+      const bool start = c + lane < nblk && (c + lane == 0 || p.bits != p.prev);
+      const int lo = (int)floor((double)p.off * G / T);
+      const uint64_t before = __ballot(start && lo <= g), after = __ballot(start && lo > g);
+      if (before) {
+        const int l = 63 - __builtin_clzll(before);
+        bs = c + l;
+        off = readlane64(p.off, l);
+        bits = __builtin_amdgcn_readlane(p.bits, l);
       }
-      const uint64_t hit = __ballot(lo <= g && g < hi);
-      if (hit) {
-        const int l = __builtin_ctzll(hit);
-        blk = c + l;
-        lo = __shfl(lo, l);
-        hi = __shfl(hi, l);
-        bl = __shfl(bl, l);
-        o0 = ((uint64_t)(uint32_t)__shfl((int)(o0 >> 32), l) << 32) | (uint32_t)__shfl((int)(uint32_t)o0, l);
+      if (after) {
+        const int l = __builtin_ctzll(after);
+        be = c + l;
+        off_e = readlane64(p.off, l);
         break;
       }
     }
-    if (blk < 0) return;
-    const int wb = hi - lo, sub = g - lo;
-    r0 = kMixedRows * sub / wb;
-    rows = kMixedRows * (sub + 1) / wb - r0;
-    bits = bl;
-    off = o0;
+    if (bs < 0) return;   // block 0 starts a run at F = 0 <= w: not reached
+    // the run's workgroups and this one's index; every block of the run
+    // brings at least one workgroup (wr >= be - bs), so a workgroup gets at
+    // most 64 rows, what the host sized the LDS for
+    const int lo = (int)floor((double)off * G / T), hi = (int)floor((double)off_e * G / T);
+    const int wr = hi - lo, sub = g - lo;
+    const int64_t pairs = (int64_t)(kMixedRows / 2) * (be - bs);
+    const int q0 = (int)(pairs * sub / wr), q1 = (int)(pairs * (sub + 1) / wr);
+    blk = bs;
+    r0 = 2 * q0;
+    rows = 2 * (q1 - q0);
   }
+  // the same on every lane: say so, so that the ring's cursor, loop counts
+  // and waits stay scalar as in the uniform kernel (as vector values they
+  // cost 0.3 us on the down_proj)
+  blk = __builtin_amdgcn_readfirstlane(blk);
+  r0 = __builtin_amdgcn_readfirstlane(r0);
+  rows = __builtin_amdgcn_readfirstlane(rows);
+  bits = __builtin_amdgcn_readfirstlane(bits);
+  off = readlane64(off, 0);
   if (rows <= 0) return;
   const uint32_t *codes0 = L.codes + off + (size_t)r0 * (L.k / kSlice) * bits;
   r0 += kMixedRows * blk;
   if (bits == 8)
+    stream_ring<8, FULL>(L, codes0, r0, rows, smem, ahead);
+  else
+    stream_ring<6, FULL>(L, codes0, r0, rows, smem, ahead);
+}
+
+// The same with every workgroup placed by the host (from the caller's host
+// copy of the widths): its record and the next one, read with the launch
+// arguments, give its first code word, rows and width, so the ring starts
+// right behind the activation loads, as in the uniform kernel.
+template <bool FULL>
+__global__ __launch_bounds__(kRingThreads) void gemv_ring_mixed_table_kernel(MixedArgs a) {
+  extern __shared__ uint32_t smem[];
+  const int g = blockIdx.x;
+  const LinDesc L = a.lin;
+  const uint64_t e0 = a.wg[g], e1 = a.wg[g + 1];
+  asm volatile("" ::"s"(L.codes), "s"(L.scales), "s"(L.zeros), "s"(L.signs), "s"(L.x), "s"(L.y), "s"(L.n),
+               "s"(L.k), "s"(e0), "s"(e1));
+  ActAhead<kActAhead<6>> ahead;
+  act_ahead_loads(L, ahead);
+  const int r0 = (int)((uint32_t)(e0 >> 32) & 0x7FFFFFFFu);
+  const int rows = (int)((uint32_t)(e1 >> 32) & 0x7FFFFFFFu) - r0;
+  if (rows <= 0) return;
+  const uint32_t *codes0 = L.codes + (uint32_t)e0;
+  if (e0 >> 63)
     stream_ring<8, FULL>(L, codes0, r0, rows, smem, ahead);
   else
     stream_ring<6, FULL>(L, codes0, r0, rows, smem, ahead);
@@ -1776,6 +1864,15 @@ hipError_t launch_xprep(int bits, int count, const uint16_t *const *x, const int
     case 8: hipLaunchKernelGGL(xprep_kernel<8>, grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemv_mixed_table(const MixedArgs &a, hipStream_t s) {
+  if (a.tiles < 1 || a.tiles > kMixedTableWgs) return hipErrorInvalidValue;
+  if (a.lin.k % kSeg == 0)
+    hipLaunchKernelGGL((gemv_ring_mixed_table_kernel<true>), dim3(a.tiles), dim3(kRingThreads), a.lds_bytes, s, a);
+  else
+    hipLaunchKernelGGL((gemv_ring_mixed_table_kernel<false>), dim3(a.tiles), dim3(kRingThreads), a.lds_bytes, s, a);
   return hipGetLastError();
 }
 

@@ -64,6 +64,22 @@ struct GemvArgs {
                                 // 64-row block, 0 = workgroups spread over the blocks by code words
 };
 
+// The mixed 6/8-bit layout at batch 1 when the caller also gave the block
+// widths on the host: the host places every workgroup (the same split as
+// the kernel's own search: runs of same-width blocks, workgroups by code
+// words, row pairs split evenly), and each workgroup reads its record and
+// the next one.  Record w: low word the code word of its first row, high
+// word that row | (1 << 31 if its rows are 8-bit); record G: n rows.
+constexpr int kMixedTableWgs = WQ_MIXED_HOST_WORKGROUPS;
+struct MixedArgs {
+  LinDesc lin;
+  int32_t tiles;                // workgroups G
+  int32_t lds_bytes;
+  uint64_t wg[kMixedTableWgs + 1];
+};
+static_assert(sizeof(MixedArgs) <= 4096, "mixed launch arguments within the 4 KB kernel-argument limit");
+hipError_t launch_gemv_mixed_table(const MixedArgs &a, hipStream_t s);
+
 // The calling thread's message for wq_last_error (api.cpp): set_error
 // formats it and returns st; clear_error empties it.
 wq_status set_error(wq_status st, const char *fmt, ...);

@@ -119,6 +119,11 @@ int main() {
       c.want = WQ_E_ALIGN; cases.push_back(c);
       c = base(); c.what = "mixed n"; c.w.bits = 0; c.w.n = 96; c.ldy = 96; c.want = WQ_E_ARG; cases.push_back(c);
       c = base(); c.what = "mixed tables"; c.w.bits = 0; c.want = WQ_E_ARG; cases.push_back(c);
+      // the optional host copy of the widths (n / 64 = 4 bytes, read on the host)
+      static const uint8_t bad_widths[4] = {6, 8, 6, 5};
+      c = base(); c.what = "mixed host widths"; c.w.bits = 0; c.w.block_bits = static_cast<const uint8_t *>(P16);
+      c.w.block_off = static_cast<const uint64_t *>(P16); c.w.block_bits_host = bad_widths; c.want = WQ_E_ARG;
+      cases.push_back(c);
       c = base(); c.what = "rht block"; c.w.rht_signs = static_cast<const uint32_t *>(P16); c.w.rht_block = 64;
       c.want = WQ_E_UNSUPPORTED; cases.push_back(c);
       for (int64_t m : {INT64_MIN, (int64_t)-1, (int64_t)0}) {

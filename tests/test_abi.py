@@ -92,6 +92,19 @@ def test_linear_rejects_bad_weights(lib, kw, status, text):
     assert text in lib.wq_last_error().decode()
 
 
+def test_linear_rejects_bad_host_widths(lib):
+    # the optional host copy of a mixed layout's widths is read on the host
+    # and refused (before anything is launched) unless every value is 6 or 8
+    good = (ctypes.c_uint8 * 2)(6, 8)
+    bad = (ctypes.c_uint8 * 2)(6, 7)
+    for bh, text in ((bad, "block_bits_host[1]=7"), (good, "y_dtype")):
+        # a good copy passes the weight checks and meets the next defect (the
+        # output type), so nothing is launched either way
+        w = _weight(bits=0, n=128, block_bits=16, block_off=16, block_bits_host=ctypes.addressof(bh))
+        st = lib.wq_linear(ctypes.byref(w), 16, 1, 256, 16, 7, 128, 0, 16, 1 << 20, None)
+        assert st == dq.WQ_E_ARG and text in lib.wq_last_error().decode()
+
+
 @pytest.mark.parametrize("args,status,text", [
     (dict(m=0), dq.WQ_E_ARG, "m=0"),
     (dict(x=None), dq.WQ_E_ARG, "non-NULL"),

@@ -38,7 +38,7 @@ LARGE = dict(rms=256.0, outlier_frac=0.01, outlier_scale=64.0)
 
 
 def _case(n, k, m, bits, *, rms=1.0, outlier_frac=0.0, outlier_scale=1.0, trained=False, rht=True,
-          out_f32=False, seed=0, sel=None, label=""):
+          out_f32=False, seed=0, sel=None, host_widths=True, label=""):
     """One linear through wq_linear against the oracle.  The GPU weight is
     the oracle's codes packed by wq_pack, with the oracle's (or trained)
     scales and zeros."""
@@ -55,7 +55,8 @@ def _case(n, k, m, bits, *, rms=1.0, outlier_frac=0.0, outlier_scale=1.0, traine
     ref = OL.linear(q, s, z, x, signs)
     sel_d = dev(sel) if sel is not None else None
     packed, off = dq.wq_pack(dev(q), bits, sel_d)
-    qw = dq.QWeight(bits, n, k, packed, dev(s), dev(z), dev_u32(signs) if rht else None, sel_d, off)
+    qw = dq.QWeight(bits, n, k, packed, dev(s), dev(z), dev_u32(signs) if rht else None, sel_d, off,
+                    host_widths=host_widths)
     y = dq.wq_linear(qw, dev(x), torch.float32 if out_f32 else torch.float16, fuse_rht=rht)
     rel, mx = check_close(y.float().cpu().numpy(), ref, label)
     say(f"  {label}: rel-L2 {rel:.2e} max/rms {mx:.2e}")
@@ -176,25 +177,50 @@ def test_grouped_mixed_width_batch(m):
         say(f"  n={n} k={k}: rel-L2 {rel:.2e} max/rms {mx:.2e}")
 
 
-# Batch 1 over the mixed layout: the workgroups are spread over the 64-row
-# blocks in proportion to their code words while every block still gets one
-# (up to 3/4 as many blocks as compute units), else one workgroup per block.
-# One block (32 workgroups of 2 rows), all-8-bit blocks, a random mix of 150
-# blocks, and 200 blocks (one workgroup each).
+# Batch 1 over the mixed layout: blocks of one width that follow each other
+# form a run (one uniform-width matrix); the workgroups are spread over the
+# runs in proportion to their code words while every block still gets one
+# (up to 3/4 as many blocks as compute units), and a run's row pairs are
+# split evenly among its workgroups; else one workgroup per block.  One block
+# (32 workgroups of 2 rows), all-8-bit blocks, all-6-bit blocks at the
+# down_proj shape (one run over 2560 rows), alternating widths (runs of one
+# block), runs that straddle the 64-block passes of the search, a random mix
+# of 150 blocks, and 200 blocks (one workgroup each).
+_STRADDLE = np.array([6] * 60 + [8] * 10 + [6] * 50 + [8] * 7 + [6] * 3, np.uint8)   # 130 blocks
 MIXED_LAYOUTS = [("one block", np.array([8], np.uint8), 1024),
                  ("all 8", np.full(4, 8, np.uint8), 2560),
+                 ("all 6, one run", np.full(40, 6, np.uint8), 9728),
+                 ("alternating", np.array([6, 8] * 20, np.uint8), 2560),
+                 ("runs across search passes", _STRADDLE, 1024),
                  ("150 random", None, 1024),
                  ("200 random, one workgroup per block", None, 1024)]
 
 
+# host_widths: the caller also passes the widths in host memory (the kernel
+# places its workgroups from its launch arguments), or not (it reads the
+# block table on the device); both must give the oracle's values
+@pytest.mark.parametrize("host_widths", [True, False], ids=["host widths", "device table"])
 @pytest.mark.parametrize("label,sel,k", MIXED_LAYOUTS, ids=[c[0] for c in MIXED_LAYOUTS])
-def test_mixed_batch1_block_spread(label, sel, k):
+def test_mixed_batch1_block_spread(label, sel, k, host_widths):
     rng = np.random.default_rng(970 + k)
     if sel is None:
         nblk = 150 if label.startswith("150") else 200
         sel = np.where(rng.random(nblk) < 0.3, 8, 6).astype(np.uint8)
-    say(f"mixed batch 1: {label} ({len(sel)} blocks, {int((sel == 8).sum())} of 8 bits) k={k}")
-    _case(64 * len(sel), k, 1, 0, sel=sel, seed=980 + len(sel), label=label)
+    say(f"mixed batch 1: {label} ({len(sel)} blocks, {int((sel == 8).sum())} of 8 bits) k={k} "
+        f"host widths {host_widths}")
+    _case(64 * len(sel), k, 1, 0, sel=sel, seed=980 + len(sel), host_widths=host_widths, label=label)
+
+
+@pytest.mark.parametrize("host_widths", [True, False], ids=["host widths", "device table"])
+def test_mixed_batch1_runs_trained(host_widths):
+    # trained scales and zeros on the run-split path at the down_proj shape,
+    # with the workload's seeded selectors (runs of 6-bit blocks between
+    # single 8-bit ones)
+    sel = W.block_selector(2560, np.random.default_rng(975))
+    say(f"mixed batch 1 runs, trained s,z: {int((sel == 8).sum())} of {len(sel)} blocks 8-bit, "
+        f"host widths {host_widths}")
+    _case(2560, 9728, 1, 0, sel=sel, trained=True, seed=976, host_widths=host_widths, label="mixed runs trained")
+
 
 
 @pytest.mark.parametrize("m", [1, 4, 24, 128])
