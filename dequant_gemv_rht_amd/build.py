@@ -38,6 +38,10 @@ def _compile(src: str, asm: bool) -> str:
     cmd = [HIPCC] + COMMON + ["-c", src, "-o", obj]
     if src.endswith(".hip"):
         cmd[1:1] = ["-x", "hip"]
+        if os.path.basename(src) == "gemv_stream.hip":
+            # the GEMV kernels' first seven arguments (the linears' first
+            # workgroups) arrive preloaded in scalar registers
+            cmd += ["-mllvm", "-amdgpu-kernarg-preload-count=7"]
         if asm:
             cmd += ["-save-temps=obj"]
     r = subprocess.run(cmd, capture_output=True, text=True, cwd=OUT)

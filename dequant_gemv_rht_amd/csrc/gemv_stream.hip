@@ -1561,10 +1561,10 @@ __global__ __launch_bounds__(kXprepThreads) void xprep_kernel(XprepBatch a) {
 }
 
 template <int BITS, bool FULL>
-__global__ __launch_bounds__(kRingThreads) void gemv_ring_kernel(GemvArgs a) {
+__global__ __launch_bounds__(kRingThreads) void gemv_ring_kernel(int t1, int t2, int t3, int t4, int t5, int t6, int t7, GemvArgs a) {
   extern __shared__ uint32_t smem[];
   const int w = blockIdx.x;
-  const LinDesc L = fetch_desc(a, w);
+  const LinDesc L = fetch_desc(a, w, FirstTiles{t1, t2, t3, t4, t5, t6, t7});
   const int r0 = (w - L.tile_begin) * L.rows_per_wg;
   if (r0 >= L.n) return;
   ActAhead<kActAhead<BITS>> ahead;
@@ -1584,10 +1584,10 @@ struct Depth {
 };
 
 template <int BITS, int MT>
-__global__ __launch_bounds__(kStreamThreads) void gemv_stream_kernel(GemvArgs a) {
+__global__ __launch_bounds__(kStreamThreads) void gemv_stream_kernel(int t1, int t2, int t3, int t4, int t5, int t6, int t7, GemvArgs a) {
   extern __shared__ uint32_t smem[];
   const int w = blockIdx.x;
-  const LinDesc L = fetch_desc(a, w);
+  const LinDesc L = fetch_desc(a, w, FirstTiles{t1, t2, t3, t4, t5, t6, t7});
   const int r0 = (w - L.tile_begin) * L.rows_per_wg;
   if (r0 >= L.n) return;
   const int rows = min(L.rows_per_wg, L.n - r0);
@@ -1764,10 +1764,10 @@ struct QDepth {
 };
 
 template <int BITS, int MT, bool CHUNKED>
-__global__ __launch_bounds__(kQuadThreads) void gemv_quad_kernel(GemvArgs a) {
+__global__ __launch_bounds__(kQuadThreads) void gemv_quad_kernel(int t1, int t2, int t3, int t4, int t5, int t6, int t7, GemvArgs a) {
   extern __shared__ uint32_t smem[];
   const int w = blockIdx.x;
-  const LinDesc L = fetch_desc(a, w);
+  const LinDesc L = fetch_desc(a, w, FirstTiles{t1, t2, t3, t4, t5, t6, t7});
   asm volatile("" ::"s"(L.q_chunks), "s"(L.q_kc), "s"(L.q_p), "s"(L.q_spu), "s"(L.q_pinv), "s"(L.q_sc),
                "s"(L.q_xinv), "s"(L.q_part), "s"(L.q_szl));
   const int r0 = (w - L.tile_begin) * L.rows_per_wg;
@@ -1781,9 +1781,9 @@ hipError_t launch_quad(const GemvArgs &a, hipStream_t s) {
   bool chunked = false;
   for (int i = 0; i < a.count; ++i) chunked = chunked || a.lin[i].q_chunks > 1;
   if (chunked)
-    hipLaunchKernelGGL((gemv_quad_kernel<BITS, MT, true>), dim3(a.tiles), dim3(kQuadThreads), a.lds_bytes, s, a);
+    hipLaunchKernelGGL((gemv_quad_kernel<BITS, MT, true>), dim3(a.tiles), dim3(kQuadThreads), a.lds_bytes, s, a.first_tile[1], a.first_tile[2], a.first_tile[3], a.first_tile[4], a.first_tile[5], a.first_tile[6], a.first_tile[7], a);
   else
-    hipLaunchKernelGGL((gemv_quad_kernel<BITS, MT, false>), dim3(a.tiles), dim3(kQuadThreads), a.lds_bytes, s, a);
+    hipLaunchKernelGGL((gemv_quad_kernel<BITS, MT, false>), dim3(a.tiles), dim3(kQuadThreads), a.lds_bytes, s, a.first_tile[1], a.first_tile[2], a.first_tile[3], a.first_tile[4], a.first_tile[5], a.first_tile[6], a.first_tile[7], a);
   return hipGetLastError();
 }
 
@@ -1794,14 +1794,14 @@ hipError_t launch_bits(int mt, const GemvArgs &a, hipStream_t s) {
     bool full = true;
     for (int i = 0; i < a.count; ++i) full = full && a.lin[i].k % kSeg == 0;
     if (full)
-      hipLaunchKernelGGL((gemv_ring_kernel<BITS, true>), dim3(a.tiles), dim3(kRingThreads), a.lds_bytes, s, a);
+      hipLaunchKernelGGL((gemv_ring_kernel<BITS, true>), dim3(a.tiles), dim3(kRingThreads), a.lds_bytes, s, a.first_tile[1], a.first_tile[2], a.first_tile[3], a.first_tile[4], a.first_tile[5], a.first_tile[6], a.first_tile[7], a);
     else
-      hipLaunchKernelGGL((gemv_ring_kernel<BITS, false>), dim3(a.tiles), dim3(kRingThreads), a.lds_bytes, s, a);
+      hipLaunchKernelGGL((gemv_ring_kernel<BITS, false>), dim3(a.tiles), dim3(kRingThreads), a.lds_bytes, s, a.first_tile[1], a.first_tile[2], a.first_tile[3], a.first_tile[4], a.first_tile[5], a.first_tile[6], a.first_tile[7], a);
     return hipGetLastError();
   }
   switch (mt) {
     case 1:
-      hipLaunchKernelGGL((gemv_stream_kernel<BITS, 1>), dim3(a.tiles), dim3(kStreamThreads), a.lds_bytes, s, a);
+      hipLaunchKernelGGL((gemv_stream_kernel<BITS, 1>), dim3(a.tiles), dim3(kStreamThreads), a.lds_bytes, s, a.first_tile[1], a.first_tile[2], a.first_tile[3], a.first_tile[4], a.first_tile[5], a.first_tile[6], a.first_tile[7], a);
       break;
     case 2: return launch_quad<BITS, 2>(a, s);
     case 4: return launch_quad<BITS, 4>(a, s);

@@ -334,15 +334,33 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
 // fields are all read in one round of scalar loads: read where first used,
 // each would wait for its own round trip to the argument block, and the
 // first weight load waits for the pointers.
-__device__ __forceinline__ LinDesc fetch_desc(const GemvArgs &a, int w) {
+// The first workgroups of linears 1 .. 7 (first_tile[1 .. 7]), passed as
+// the kernel's first seven arguments: the build preloads them into scalar
+// registers, so the descriptor's address is known without a round trip to
+// the kernel arguments (0.1 us per launch of the seven-projection block).
+struct FirstTiles {
+  int t1, t2, t3, t4, t5, t6, t7;
+};
+
+__device__ __forceinline__ LinDesc fetch_desc(const GemvArgs &a, int w, FirstTiles f) {
   int l = 0;
-#pragma unroll
-  for (int i = 1; i < kMaxBatch; ++i)
-    if (w >= a.first_tile[i]) l = i;
+  if (w >= f.t1) l = 1;
+  if (w >= f.t2) l = 2;
+  if (w >= f.t3) l = 3;
+  if (w >= f.t4) l = 4;
+  if (w >= f.t5) l = 5;
+  if (w >= f.t6) l = 6;
+  if (w >= f.t7) l = 7;
   const LinDesc L = a.lin[l];
   asm volatile("" ::"s"(L.codes), "s"(L.scales), "s"(L.zeros), "s"(L.signs), "s"(L.x), "s"(L.y), "s"(L.ldx),
                "s"(L.ldy), "s"(L.n), "s"(L.k), "s"(L.rows_per_wg), "s"(L.tile_begin), "s"(L.out_f32));
   return L;
+}
+
+// The same with the first workgroups read from the launch arguments.
+__device__ __forceinline__ LinDesc fetch_desc(const GemvArgs &a, int w) {
+  return fetch_desc(a, w, FirstTiles{a.first_tile[1], a.first_tile[2], a.first_tile[3], a.first_tile[4],
+                                     a.first_tile[5], a.first_tile[6], a.first_tile[7]});
 }
 
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
