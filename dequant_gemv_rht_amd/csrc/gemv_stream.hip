@@ -48,6 +48,8 @@
 // the two sums, the factor 2^-E, 4 spare): with that stride the 16 lanes of
 // a DPP row reading their slices with ds_read_b128 hit 16 distinct 4-bank
 // groups.
+#include <algorithm>
+
 #include "wq_internal.h"
 
 #include <climits>
@@ -621,13 +623,18 @@ struct Ring {
   static constexpr int row = 64 * 4 * BITS;                         // bytes per row per wave per step
   static constexpr int codes = 2 * row;                             // code bytes per wave per step
   static constexpr int ni = (codes + 1023) / 1024;                  // loads per step (flat)
-  static constexpr int slot = codes + 2 * 64 * 4;                   // + scales, zeros
+  // 8-bit rows: the workgroup's scales and zeros are staged in LDS once
+  // (the 151936 x 2560 head 70.9 -> 69.0 us); the other widths fetch each
+  // step's with its codes (staging measured even for int3 and int4 and
+  // 1% slower for int6)
+  static constexpr bool stage = BITS == 8;
+  static constexpr int slot = codes + (stage ? 0 : 2 * 64 * 4);      // + scales, zeros
   // steps in flight (deeper rings measured slower: int4 depth 4, 5, 6 took
   // 13.7, 14.2, 14.9 us against 12.2 us for the seven-projection block; int6
   // and int8 depth 3 8.56 and 9.66 us against 6.81 and 8.00 us for a
   // 9728 -> 2560 linear)
   static constexpr int depth = BITS == 3 ? 4 : BITS == 4 ? 3 : 2;
-  static constexpr int q = (flat ? ni : 2 * nc) + 2;               // vector loads per wave per step
+  static constexpr int q = (flat ? ni : 2 * nc) + (stage ? 0 : 2);  // vector loads per wave per step
   static constexpr int threads = kRingThreads;
   static constexpr int waves = threads / 64;
 };
@@ -661,7 +668,7 @@ struct RingCursor {
   uint32_t dco, wco, dso, wso;
   int ls;
   uint32_t lco;   // byte offset of this lane's code words, row 0 of the task
-  uint32_t lso;   // byte offset of the scale/zero this lane fetches (lanes 0..7 of a task)
+  uint32_t lso;   // byte offset of the scale/zero this lane fetches (lanes 0..7 of a task; not staged)
   // flat layouts: per load k, the segment and byte offset of this lane's item
   int fls[RS::flat ? RS::ni : 1];
   uint32_t flco[RS::flat ? RS::ni : 1];
@@ -692,32 +699,52 @@ struct RingCursor {
       ring_row_loads<BITS>(rc, slot, lco);
       ring_row_loads<BITS>(rc1, slot + RS::row, lco);
     }
+    if constexpr (!RS::stage) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    // one fp16 per lane, zero-extended to 4 bytes at slot + 4 L: a 2-byte
-    // load never reaches past the end of its range (a load that does
-    // returns zero as a whole)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsc, (lds_ptr_t)(slot + RS::codes), 2, lso, 0, 0, kNT);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rz, (lds_ptr_t)(slot + RS::codes + 256), 2, lso, 0, 0, kNT);
+      // one fp16 per lane, zero-extended to 4 bytes at slot + 4 L: a 2-byte
+      // load never reaches past the end of its range (a load that does
+      // returns zero as a whole)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsc, (lds_ptr_t)(slot + RS::codes), 2, lso, 0, 0, kNT);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rz, (lds_ptr_t)(slot + RS::codes + 256), 2, lso, 0, 0, kNT);
 #endif
+    }
     ls += ds;
     const bool wrap = ls >= KS;
     ls = wrap ? ls - KS : ls;
     if constexpr (!RS::flat) lco += wrap ? wco : dco;
-    lso += wrap ? wso : dso;
+    if constexpr (!RS::stage) lso += wrap ? wso : dso;
   }
 };
 
+// Scales and zeros of an 8-bit ring workgroup's rows are staged in LDS once, each
+// array as the bytes of its rows from the 16-byte boundary at or below the
+// first row through one more row than the workgroup has (read, masked, by
+// a missing odd row and by the groups past K of a partial last segment)
+// and 16 bytes more.  Each wave issues kRingSzLoads direct 16-byte loads
+// per array (64 items of 16 bytes each), whether needed or not, so that
+// every wave issues the same loads; a wave's chunks past the rows land in a
+// 1 KB dummy area.
+constexpr int kRingSzLoads = 3;
+
+// 16-byte items one staged array takes (at most the loads' reach)
+__host__ __device__ inline int ring_sz_items(int np, int G) { return (15 + (2 * np + 1) * G * 2 + 16 + 15) / 16; }
+
 // LDS layout of a ring workgroup, in bytes.
 struct RingLds {
-  int xs, part, ring, total;
+  int xs, part, ring, sc, zr, dummy, total;
 };
 
-__host__ __device__ inline RingLds ring_lds(int S, int KS, int np, int slot, int depth, int waves) {
+__host__ __device__ inline RingLds ring_lds(int S, int KS, int np, int G, int slot, int depth, int waves,
+                                            bool stage) {
   RingLds l;
   l.xs = S * kSliceStride * 4;                      // activations: [S][20] u32, sums in words 16, 17
   l.part = l.xs;                                    // partials: [2np][KS] f32
   l.ring = (l.part + 2 * np * KS * 4 + 15) & ~15;
-  l.total = l.ring + depth * waves * slot;
+  const int szb = stage ? (ring_sz_items(np, G) + 63) / 64 * 1024 : 0;   // whole 64-item chunks
+  l.sc = l.ring + depth * waves * slot;             // staged scales
+  l.zr = l.sc + szb;                                // staged zeros
+  l.dummy = l.zr + szb;                             // chunks past the rows
+  l.total = l.dummy + (stage ? 1024 : 0);
   return l;
 }
 
@@ -745,9 +772,8 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 
 // A task's LDS operands, read in one asm statement that also waits for
 // them: the activation slice (4 x 16 bytes) and its sums and factor (bytes
-// 64..79 of the slice), the scales and
-// zeros of the lane's group (rows 0, 1), and the lane's code words of both
-// rows from the ring slot.  Keeping these reads out of the compiler's view
+// 64..79 of the slice), the staged scales and zeros of the lane's group
+// (rows 0, 1), and the lane's code words of both rows from the ring slot.  Keeping these reads out of the compiler's view
 // keeps it from tying them to the ring's direct loads with waits of its own.
 struct TaskOps {
   u32x4 x[4];
@@ -757,24 +783,37 @@ struct TaskOps {
   uint32_t s0, s1, z0, z1;
 };
 
+// sa, sb, za, zb: the scales of rows 0 and 1 and their zeros; staged, at
+// any distances; else in the ring slot at fixed ones (sa only).
 template <int BITS>
-__device__ __forceinline__ void read_task(uint32_t xa, uint32_t sza, uint32_t ca16, uint32_t ca4, TaskOps &o,
-                                          uint32_t (&w)[2][BITS]) {
-#define WQ_OPS_READS                    \
+__device__ __forceinline__ void read_task(uint32_t xa, uint32_t sa, uint32_t sb, uint32_t za, uint32_t zb,
+                                          uint32_t ca16, uint32_t ca4, TaskOps &o, uint32_t (&w)[2][BITS]) {
+  static_assert(Ring<BITS>::stage == (BITS == 8), "the 8-bit reads take the staged addresses");
+#define WQ_OPS_XREADS                   \
   "ds_read_b128 %[x0], %[xa]\n\t"       \
   "ds_read_b128 %[x1], %[xa] offset:16\n\t" \
   "ds_read_b128 %[x2], %[xa] offset:32\n\t" \
   "ds_read_b128 %[x3], %[xa] offset:48\n\t" \
   "ds_read_b64 %[xq], %[xa] offset:64\n\t" \
-  "ds_read_b32 %[xf], %[xa] offset:72\n\t" \
-  "ds_read_u16 %[s0], %[sza]\n\t"       \
-  "ds_read_u16 %[s1], %[sza] offset:16\n\t" \
-  "ds_read_u16 %[z0], %[sza] offset:256\n\t" \
-  "ds_read_u16 %[z1], %[sza] offset:272\n\t"
+  "ds_read_b32 %[xf], %[xa] offset:72\n\t"
+// ring slot: row r's scale at sa + 16 r, its zero 256 bytes on
+#define WQ_OPS_READS                    \
+  WQ_OPS_XREADS                         \
+  "ds_read_u16 %[s0], %[sa]\n\t"       \
+  "ds_read_u16 %[s1], %[sa] offset:16\n\t" \
+  "ds_read_u16 %[z0], %[sa] offset:256\n\t" \
+  "ds_read_u16 %[z1], %[sa] offset:272\n\t"
+// staged: four addresses
+#define WQ_OPS_READS_STAGED             \
+  WQ_OPS_XREADS                         \
+  "ds_read_u16 %[s0], %[sa]\n\t"        \
+  "ds_read_u16 %[s1], %[sb]\n\t"        \
+  "ds_read_u16 %[z0], %[za]\n\t"        \
+  "ds_read_u16 %[z1], %[zb]\n\t"
 #define WQ_OPS_OUT                                                                                      \
   [x0] "=&v"(o.x[0]), [x1] "=&v"(o.x[1]), [x2] "=&v"(o.x[2]), [x3] "=&v"(o.x[3]), [xq] "=&v"(o.xq), [xf] "=&v"(o.xf), \
       [s0] "=&v"(o.s0), [s1] "=&v"(o.s1), [z0] "=&v"(o.z0), [z1] "=&v"(o.z1)
-#define WQ_OPS_IN [xa] "v"(xa), [sza] "v"(sza), [ca16] "v"(ca16), [ca4] "v"(ca4)
+#define WQ_OPS_IN [xa] "v"(xa), [sa] "v"(sa), [ca16] "v"(ca16), [ca4] "v"(ca4)
   if constexpr (BITS == 4) {
     // row r: 16 bytes at r * 1024 + 16 L
     u32x4 c0, c1;
@@ -790,14 +829,14 @@ __device__ __forceinline__ void read_task(uint32_t xa, uint32_t sza, uint32_t ca
   } else if constexpr (BITS == 8) {
     // row r: words 0..3 at r * 2048 + 16 L, words 4..7 at r * 2048 + 1024 + 16 L
     u32x4 c0, c1, c2, c3;
-    asm volatile(WQ_OPS_READS
+    asm volatile(WQ_OPS_READS_STAGED
                  "ds_read_b128 %[c0], %[ca16]\n\t"
                  "ds_read_b128 %[c1], %[ca16] offset:1024\n\t"
                  "ds_read_b128 %[c2], %[ca16] offset:2048\n\t"
                  "ds_read_b128 %[c3], %[ca16] offset:3072\n\t"
                  "s_waitcnt lgkmcnt(0)"
                  : WQ_OPS_OUT, [c0] "=&v"(c0), [c1] "=&v"(c1), [c2] "=&v"(c2), [c3] "=&v"(c3)
-                 : WQ_OPS_IN
+                 : WQ_OPS_IN, [sb] "v"(sb), [za] "v"(za), [zb] "v"(zb)
                  : "memory");
     w[0][0] = c0.x; w[0][1] = c0.y; w[0][2] = c0.z; w[0][3] = c0.w;
     w[0][4] = c1.x; w[0][5] = c1.y; w[0][6] = c1.z; w[0][7] = c1.w;
@@ -844,7 +883,9 @@ __device__ __forceinline__ void read_task(uint32_t xa, uint32_t sza, uint32_t ca
       w[1][2 * e] = (uint32_t)c[3 + e]; w[1][2 * e + 1] = (uint32_t)(c[3 + e] >> 32);
     }
   }
+#undef WQ_OPS_XREADS
 #undef WQ_OPS_READS
+#undef WQ_OPS_READS_STAGED
 #undef WQ_OPS_OUT
 #undef WQ_OPS_IN
 }
@@ -911,7 +952,7 @@ __device__ __forceinline__ void stream_ring(const LinDesc &L, const uint32_t *co
   const int K = L.k, KS = (K + kSeg - 1) / kSeg, G = K / kGroup, S = K / kSlice;
   const int wpr = S * BITS;
   const int NP = (rows + 1) >> 1, T = NP * KS;
-  const RingLds lay = ring_lds(S, KS, NP, RS::slot, R, RS::waves);
+  const RingLds lay = ring_lds(S, KS, NP, G, RS::slot, R, RS::waves, RS::stage);
   uint8_t *lds = reinterpret_cast<uint8_t *>(smem);
   uint32_t *xp = smem;
   float *part = reinterpret_cast<float *>(lds + lay.part);
@@ -935,16 +976,22 @@ __device__ __forceinline__ void stream_ring(const LinDesc &L, const uint32_t *co
     const uint32_t seg_step = 16 * BITS * 4;
     cur.rc = make_rsrc(codes0, (uint32_t)rows * row_bytes);
     cur.rc1 = make_rsrc(codes0 + wpr, (uint32_t)(rows - 1) * row_bytes);
-    const uint32_t szb = (uint32_t)rows * G * 2;
-    cur.rsc = make_rsrc(L.scales + (size_t)r0 * G, szb);
-    cur.rz = make_rsrc(L.zeros + (size_t)r0 * G, szb);
+    if constexpr (!RS::stage) {
+      const uint32_t szb = (uint32_t)rows * G * 2;
+      cur.rsc = make_rsrc(L.scales + (size_t)r0 * G, szb);
+      cur.rz = make_rsrc(L.zeros + (size_t)r0 * G, szb);
+      cur.dso = (uint32_t)(2 * (2 * dp * G + 4 * ds));
+      cur.wso = cur.dso + (uint32_t)(2 * (2 * G - 4 * KS));
+      // lanes j < 8 fetch the scale/zero of row 2p + (j >> 2), group 4s + (j & 3);
+      // the other lanes start past any resource (bit 31 set) and stay there as the offset advances
+      cur.lso = (__umul24((uint32_t)(2 * cp0 + (j >> 2)), (uint32_t)(2 * G)) + (uint32_t)(8 * cs0 + 2 * (j & 3))) |
+                (j < 8 ? 0u : kOOB);
+    }
     cur.slot0 = lds_addr(lds + lay.ring) + (uint32_t)(wave * RS::slot);
     cur.KS = KS;
     cur.ds = ds;
     cur.dco = (uint32_t)dp * pair_bytes + (uint32_t)ds * seg_step;
     cur.wco = cur.dco + pair_bytes - (uint32_t)KS * seg_step;
-    cur.dso = (uint32_t)(2 * (2 * dp * G + 4 * ds));
-    cur.wso = cur.dso + (uint32_t)(2 * (2 * G - 4 * KS));
     cur.ls = cs0;
     cur.lco = __umul24((uint32_t)cp0, pair_bytes) + (uint32_t)cs0 * seg_step + (uint32_t)j * (BITS * 4);
     if constexpr (RS::flat) {
@@ -961,10 +1008,31 @@ __device__ __forceinline__ void stream_ring(const LinDesc &L, const uint32_t *co
       }
       cur.flast = lane < 2 * per_row - 64 * (RS::ni - 1);
     }
-    // lanes j < 8 fetch the scale/zero of row 2p + (j >> 2), group 4s + (j & 3);
-    // the other lanes start past any resource (bit 31 set) and stay there as the offset advances
-    cur.lso = (__umul24((uint32_t)(2 * cp0 + (j >> 2)), (uint32_t)(2 * G)) + (uint32_t)(8 * cs0 + 2 * (j & 3))) |
-              (j < 8 ? 0u : kOOB);
+  }
+  // the scales and zeros of the workgroup's rows, staged once (before the
+  // weight stream, so that waiting for them never waits for it)
+  const uint32_t sz0 = (uint32_t)r0 * (uint32_t)G * 2, sz_al = sz0 & ~15u;   // first byte, its 16-byte boundary
+  if constexpr (RS::stage) {
+    const int n16 = ring_sz_items(NP, G);
+    // the arrays' range rounded up to 16 bytes: a 16-byte load that reaches
+    // past its range returns zero as a whole, which would drop the last
+    // row's last scales; the array starts 16-byte aligned, so the rounded
+    // end stays in its last page (the bytes past the array only reach
+    // masked lanes and rows that are not stored)
+    const uint32_t szn = ((uint32_t)L.n * (uint32_t)G * 2 + 15u) & ~15u;
+    const rsrc_t rs = make_rsrc(L.scales, szn), rz = make_rsrc(L.zeros, szn);
+#pragma unroll
+    for (int q = 0; q < kRingSzLoads; ++q) {
+      const int c = q * RS::waves + wave, it = 64 * c + lane;   // chunk, item
+      const bool used = 64 * c < n16;
+      const uint32_t dst_s = lds_addr(lds + (used ? lay.sc + 1024 * c : lay.dummy));
+      const uint32_t dst_z = lds_addr(lds + (used ? lay.zr + 1024 * c : lay.dummy));
+      const uint32_t src = it < n16 ? sz_al + 16u * (uint32_t)it : kOOB;
+#if defined(__HIP_DEVICE_COMPILE__)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)dst_s, 16, src, 0, 0, kNT);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rz, (lds_ptr_t)dst_z, 16, src, 0, 0, kNT);
+#endif
+    }
   }
   cur.template issue<0>();
   if constexpr (R > 1) cur.template issue<1>();
@@ -994,6 +1062,7 @@ __device__ __forceinline__ void stream_ring(const LinDesc &L, const uint32_t *co
     consume(raw, w1);
     rotate_item<BITS, 1>(rotate, raw, w1, nb, items, it0 + rg, j, xp, S);
   }
+  if constexpr (RS::stage) wait_vmcnt<R * Q>();   // this wave's staged scales and zeros are in LDS
   lds_barrier();
 
   // 3. consume the ring
@@ -1009,7 +1078,14 @@ __device__ __forceinline__ void stream_ring(const LinDesc &L, const uint32_t *co
   const uint32_t dxa = (uint32_t)ds * kSegBytes, wxa = (uint32_t)KS * kSegBytes;
   const uint32_t dpa = (uint32_t)((2 * dp * KS + ds) * 4), wpa = dpa + (uint32_t)(KS * 4);
   int cs = cs0;   // only needed to mask slices of a partial last segment
-  const uint32_t sza_l = cur.slot0 + RS::codes + (lane & 48) * 4 + (j >> 2) * 4;
+  // the staged scale of row 2 cp, group 4 cs + j / 4; the row below it and
+  // the zeros at fixed distances; advancing like the activation slice
+  // (unstaged: the lane's group in the ring slot, 4 bytes each at
+  // task * 64 + 4 * (4 row + group), fetched by lanes 0..7 of its task)
+  uint32_t sa = RS::stage ? lds_addr(lds + lay.sc) + (sz0 - sz_al) + (uint32_t)((2 * cp0 * G + 4 * cs0 + (j >> 2)) * 2)
+                          : cur.slot0 + RS::codes + (lane & 48) * 4 + (j >> 2) * 4;
+  const uint32_t srow = 2 * (uint32_t)G, zdist = (uint32_t)(lay.zr - lay.sc);
+  const uint32_t dsa = (uint32_t)(2 * (2 * dp * G + 4 * ds)), wsa = dsa + (uint32_t)(2 * (2 * G - 4 * KS));
   const uint32_t ca16_l = cur.slot0 + lane * 16;
   const uint32_t ca4_l = cur.slot0 + (uint32_t)((lane >> 4) * (64 * BITS) + j * (4 * BITS));   // flat layouts
   constexpr uint32_t kStage = (TH / 64) * RS::slot;   // bytes between ring stages
@@ -1023,9 +1099,12 @@ __device__ __forceinline__ void stream_ring(const LinDesc &L, const uint32_t *co
         const bool sv = FULL || cs * 16 + j < S;
         TaskOps o;
         uint32_t cw[2][BITS];
-        // scales/zeros of this lane's group (rows 0, 1) were fetched by lanes
-        // 0..7 of its task: 4 bytes each at task * 64 + 4 * (4 row + group)
-        read_task<BITS>(sv ? xa : lds_addr(xp), sza_l + d * kStage, ca16_l + d * kStage, ca4_l + d * kStage, o, cw);
+        if constexpr (RS::stage)
+          read_task<BITS>(sv ? xa : lds_addr(xp), sa, sa + srow, sa + zdist, sa + zdist + srow, ca16_l + d * kStage,
+                          ca4_l + d * kStage, o, cw);
+        else
+          read_task<BITS>(sv ? xa : lds_addr(xp), sa + d * kStage, 0, 0, 0, ca16_l + d * kStage, ca4_l + d * kStage,
+                          o, cw);
         uint32_t xv[16];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -1044,7 +1123,10 @@ __device__ __forceinline__ void stream_ring(const LinDesc &L, const uint32_t *co
           float dd = fmaf(-zc[r], xsum, -xoff);
 #pragma unroll
           for (int q = 0; q < 16; ++q) dd = dot2(pr[q], xv[q], dd);
-          a[r] = fmaf(sv ? sc[r] : 0.f, dd, 0.0f);   // one v_fma_mix with the fp16 scale
+          // one v_fma_mix with the fp16 scale; slices past K (partial last
+          // segment) are dropped by a select, as their staged scale and
+          // zero may be any bits
+          a[r] = FULL ? fmaf(sc[r], dd, 0.0f) : sv ? fmaf(sc[r], dd, 0.0f) : 0.0f;
         }
         // both rows summed over the 16 lanes at once: after the first
         // exchange, even lanes carry row 0 and odd lanes row 1
@@ -1060,6 +1142,7 @@ __device__ __forceinline__ void stream_ring(const LinDesc &L, const uint32_t *co
         const bool wrap = xa >= xa_end;
         xa = wrap ? xa - wxa : xa;
         pa += wrap ? wpa : dpa;
+        if constexpr (RS::stage) sa += wrap ? wsa : dsa;
         if constexpr (!FULL) cs = wrap ? cs + ds - KS : cs + ds;
       }
       wait_lgkm0();   // this slot's bytes are in registers before it is refilled
@@ -1822,15 +1905,20 @@ int gemv_stream_lds_bytes(int bits, int mt, int64_t k, int rows_per_wg, bool rin
   if (!ring && mt >= 2) return quad_lds(mt, (int)S, (int)KS, (int)G, (rows_per_wg + 3) / 4).total * 4;
   if (!ring) return stream_lds(mt, (int)S, (int)KS, (int)G, (int)np).total * 4;
   if (mt != 1) return 1 << 30;
+  // the staged scales and zeros (8-bit rows) must lie within the loads' reach
+  if ((bits == 8 || bits == 0) && (int64_t)ring_sz_items((int)np, (int)G) > (int64_t)64 * kRingSzLoads * (kRingThreads / 64))
+    return 1 << 30;
+  const int s = (int)S, ks = (int)KS, n = (int)np, g = (int)G;
+  auto need = [&](auto ring) {
+    using RS = decltype(ring);
+    return ring_lds(s, ks, n, g, RS::slot, RS::depth, RS::waves, RS::stage).total;
+  };
   switch (bits) {
-    case 0: {   // mixed 6/8: room for either ring (the 8-bit one is the larger)
-      using R8 = Ring<8>;
-      return ring_lds((int)S, (int)KS, (int)np, R8::slot, R8::depth, R8::waves).total;
-    }
-    case 3: return ring_lds((int)S, (int)KS, (int)np, Ring<3>::slot, Ring<3>::depth, Ring<3>::waves).total;
-    case 4: return ring_lds((int)S, (int)KS, (int)np, Ring<4>::slot, Ring<4>::depth, Ring<4>::waves).total;
-    case 6: return ring_lds((int)S, (int)KS, (int)np, Ring<6>::slot, Ring<6>::depth, Ring<6>::waves).total;
-    case 8: return ring_lds((int)S, (int)KS, (int)np, Ring<8>::slot, Ring<8>::depth, Ring<8>::waves).total;
+    case 0: return std::max(need(Ring<6>{}), need(Ring<8>{}));   // mixed 6/8: room for either ring
+    case 3: return need(Ring<3>{});
+    case 4: return need(Ring<4>{});
+    case 6: return need(Ring<6>{});
+    case 8: return need(Ring<8>{});
   }
   return 1 << 30;
 }
