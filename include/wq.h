@@ -45,7 +45,11 @@
  *      int3: 32 codes per 3 uint32, int6: 16 codes per 3 uint32; the three
  *            words form the 96-bit little-endian integer w0|w1<<32|w2<<64
  *            and code j of the run sits in bits [b*j, b*j+b).
- *  - scales, zeros: fp16 [N][K/128], row-major.
+ *  - scales, zeros: fp16 [N][K/128], row-major.  (The batch-1 kernel for
+ *    8-bit codes reads these arrays in 16-byte pieces, up to the 16-byte
+ *    boundary after their last element: up to 15 bytes past their end,
+ *    never past that boundary, so never into another page.  Those bytes do
+ *    not affect any result.)
  *  - mixed width: rows are cut into blocks of 64; block i is coded at
  *    block_bits[i] bits (6 or 8) with the layout above; blocks follow each
  *    other with no padding; block i starts at word block_off[i], and
