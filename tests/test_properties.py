@@ -10,7 +10,8 @@
   group of one; a group's workspace is the sum of its members' (batch
   tiles) or holds every member's rotated activations (matrix cores); and a
   call with any one defect is refused with that defect's status before any
-  HIP call (no GPU is touched here).
+  HIP call (no GPU is touched here); a mixed layout's host copy of its
+  widths is checked value by value on the host.
 """
 
 import ctypes
@@ -178,3 +179,25 @@ def test_abi_any_single_defect_is_refused(lib, bits, k, n, m, defect):
                         16, 1 << 40, None)
     assert st_ == status, (defect, lib.wq_last_error())
     assert lib.wq_last_error().decode()
+
+
+@SETTINGS
+@given(k=k_st, widths=st.lists(st.integers(0, 255), min_size=1, max_size=12), data=st.data())
+def test_abi_host_widths_checked_on_the_host(lib, k, widths, data):
+    # a mixed layout's optional host copy of its widths: any value other than
+    # 6 and 8 is refused (WQ_E_ARG, naming the first bad block) before any HIP
+    # call; valid widths pass the weight checks and the call meets its next
+    # defect, the output type (so nothing is launched either way)
+    if data.draw(st.booleans()):
+        widths = [data.draw(st.sampled_from([6, 8])) for _ in widths]
+    arr = (ctypes.c_uint8 * len(widths))(*widths)
+    w = _weight(bits=0, n=64 * len(widths), k=k, block_bits=16, block_off=16,
+                block_bits_host=ctypes.addressof(arr))
+    st_ = lib.wq_linear(ctypes.byref(w), 16, 1, k, 16, 9, 64 * len(widths), 0, 16, 1 << 40, None)
+    msg = lib.wq_last_error().decode()
+    bad = [i for i, v in enumerate(widths) if v not in (6, 8)]
+    assert st_ == dq.WQ_E_ARG
+    if bad:
+        assert f"block_bits_host[{bad[0]}]={widths[bad[0]]}" in msg, msg
+    else:
+        assert "y_dtype" in msg, msg
