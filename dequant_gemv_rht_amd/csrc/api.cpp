@@ -523,11 +523,19 @@ wq_status run_gemm(int count, const wq_weight *w, const uint16_t *const *x, cons
     ldo[i] = ldy[i];
     yo[i] = y[i];
   }
+  // int4 up to 64 rows (the narrow tiles): when every linear's activations
+  // pass through the rotation, it stores each 8-element group in the order
+  // the kernel unpacks a code word in, cheaper than natural order (24 / 63
+  // rows of the int4 block: 37.9 -> 37.3 / 46.8 -> 45.5 us).  The 128 x 256
+  // tile keeps natural order: there the compiler interleaves the cheaper
+  // unpack worse with the matrix products (M = 512: 141.7 -> 147.8 us).
+  bool pair_order = wq::gemm_pair_order(w[0].bits) && m <= 64;
+  for (int i = 0; i < count; ++i) pair_order = pair_order && rotate && w[i].rht_signs;
   if (nr) {
-    const wq_status st = hip_status(wq::launch_rht_batch(nr, rx, ry, rs, m, rk, rlx, rly, s), who);
+    const wq_status st = hip_status(wq::launch_rht_batch(nr, rx, ry, rs, m, rk, rlx, rly, pair_order, s), who);
     if (st != WQ_OK) return st;
   }
-  return hip_status(wq::launch_gemm_batch(count, w, xr, ldr, m, yo, f32, ldo, g.ksplit, part, s), who);
+  return hip_status(wq::launch_gemm_batch(count, w, xr, ldr, m, yo, f32, ldo, g.ksplit, part, pair_order, s), who);
 }
 
 // One validated linear: the matrix-core path, the GEMV over all m rows

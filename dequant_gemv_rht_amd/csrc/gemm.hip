@@ -37,7 +37,9 @@
 // two bytes next to 0x64 bytes; int3/int6: bit fields spread over the two
 // halves -- then q exactly with one packed fma and q - z in fp16 (exact
 // for an integer zero point, which round-to-nearest quantisation always
-// gives).
+// gives).  int4 up to 64 batch rows takes activations that the rotation
+// stored in pair order instead (b_operand4p): cheaper unpack, and one fma
+// per pair where the wave's zero points are integers.
 //
 // Scales.  The products of a group of 128 are (q - z) x in fp32; the group's
 // scale s multiplies their sum, not the weight, so the weight is never
@@ -207,6 +209,47 @@ __device__ __forceinline__ half8 b_operand(const uint32_t (&w)[BITS], PairConsts
   return __builtin_bit_cast(half8, u32x4{p[0], p[1], p[2], p[3]});
 }
 
+// int4 with the activations in pair order (each 8-element group stored as
+// 0, 4, 1, 5, 2, 6, 3, 7 by the rotation pre-pass): code word KK of the
+// slice, nibbles 0..7, gives the pairs (0, 4) and (2, 6) as (1024 + q) from
+// the word and the word shifted by 8 under mask 0x000F000F, and (1, 5),
+// (3, 7) as (1024 + 16 q) under mask 0x00F000F0: one shift and four
+// v_and_or_b32 for the eight codes (against a v_perm_b32 and a v_and_or_b32
+// per pair in natural order).  Then q - z:
+//  * FAST (every zero point of the step an integer in [-1024, 1023], as
+//    round-to-nearest always gives): one fma per pair, h c + (d - z) with
+//    (c, d) = (1, -1024) or (1/16, -64); the product and the addend are
+//    exact in fp16, so the fma's one rounding of the exact q - z (an
+//    integer below 2048) is exact;
+//  * else h c + d (exactly q), then q - z, rounded once.
+// c, d and z come in as 0 for a group whose scale is 0 (operand 0).
+struct PairConsts4 {
+  uint32_t lo, hi, bias;
+};
+
+__device__ __forceinline__ PairConsts4 pair_consts4() {
+  PairConsts4 c;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(c.lo) : "i"(0x000F000Fu));
+  asm volatile("v_mov_b32 %0, %1" : "=v"(c.hi) : "i"(0x00F000F0u));
+  asm volatile("v_mov_b32 %0, %1" : "=v"(c.bias) : "i"(kMagic));
+  return c;
+}
+
+template <int KK, bool FAST>
+__device__ __forceinline__ half8 b_operand4p(const uint32_t (&w)[4], PairConsts4 k, half2v c1, half2v d1,
+                                             half2v c16, half2v d16, half2v z) {
+  const uint32_t x = w[KK], x8 = x >> 8;
+  half2v q[4] = {__builtin_elementwise_fma(as_h2((x & k.lo) | k.bias), c1, d1),
+                 __builtin_elementwise_fma(as_h2((x & k.hi) | k.bias), c16, d16),
+                 __builtin_elementwise_fma(as_h2((x8 & k.lo) | k.bias), c1, d1),
+                 __builtin_elementwise_fma(as_h2((x8 & k.hi) | k.bias), c16, d16)};
+  if constexpr (!FAST) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) q[i] = q[i] - z;
+  }
+  return __builtin_bit_cast(half8, u32x4{as_u32(q[0]), as_u32(q[1]), as_u32(q[2]), as_u32(q[3])});
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
@@ -329,8 +372,10 @@ __device__ __forceinline__ int logical_tile(int b, int nb) {
   return (xcd < rem ? xcd * (q + 1) : rem * (q + 1) + (xcd - rem) * q) + slot;
 }
 
-template <int BITS, int MB, int NB>
+// PAIR: int4 with the activations in pair order (b_operand4p)
+template <int BITS, int MB, int NB, bool PAIR>
 __global__ __launch_bounds__(kGemmThreads, (Tile<MB, NB>::PerCU)) void gemm_kernel(GemmBatch a) {
+  static_assert(!PAIR || BITS == 4, "pair order is an int4 layout");
   using TL = Tile<MB, NB>;
   constexpr int kTM = TL::TM, kTN = TL::TN, kAStage = TL::AStage;
   constexpr int kStages = TL::Stages, kAhead = kStages - 1;   // kAhead: steps loaded ahead of the one computed
@@ -424,6 +469,7 @@ __global__ __launch_bounds__(kGemmThreads, (Tile<MB, NB>::PerCU)) void gemm_kern
   for (int kk = 0; kk < 4; ++kk) a_rd[kk] = lds_addr(As) + (uint32_t)(ar * 128 + (a_slot(4 * bh + kk, ar) << 4));
   constexpr _Float16 kHi = BITS == 4 ? (_Float16)0.0625f : (_Float16)1.0f;
   const PairConsts pk = pair_consts<BITS>();
+  const PairConsts4 pk4 = pair_consts4();
 
   // One step: the waits, the barrier and the loads are unconditional (a
   // step past the range only skips the products), so every iteration of the
@@ -434,8 +480,12 @@ __global__ __launch_bounds__(kGemmThreads, (Tile<MB, NB>::PerCU)) void gemm_kern
 #pragma unroll
   for (int j = 0; j < NB; ++j) unit[j] = 1.0f;
 
-  auto step = [&](auto sconst, int kt, bool active) {
+  // FAST (pair order only): every zero point of the wave's rows over its K
+  // range takes the one-fma path; chosen once per wave, before the loop, so
+  // that the step stays one straight block the compiler can interleave
+  auto step = [&](auto sconst, int kt, bool active, auto fconst) {
     constexpr int st = decltype(sconst)::value;
+    constexpr bool fast = decltype(fconst)::value;
     constexpr int nx = (st + kAhead) % kStages;
     // this step's activations (this wave's rows) and weights: the younger
     // loads are those of the kAhead - 1 steps issued after it
@@ -466,12 +516,32 @@ __global__ __launch_bounds__(kGemmThreads, (Tile<MB, NB>::PerCU)) void gemm_kern
         for (int i = 0; i < MB; ++i) acc[i][j] *= r;
       }
       const half2v z = live ? as_h2((szv[j] >> 16) * 0x10001u) : half2v{};
-      const half2v c = live ? half2v{(_Float16)1.0f, kHi} : half2v{};
-      const half2v d = live ? half2v{(_Float16)-1024.0f, (_Float16)(BITS == 4 ? -64.0f : -1024.0f)} : half2v{};
-      bop[j][0] = b_operand<BITS, 0>(cw[st][j], pk, c, d, z);
-      bop[j][1] = b_operand<BITS, 1>(cw[st][j], pk, c, d, z);
-      bop[j][2] = b_operand<BITS, 2>(cw[st][j], pk, c, d, z);
-      bop[j][3] = b_operand<BITS, 3>(cw[st][j], pk, c, d, z);
+      if constexpr (PAIR) {
+        const half2v c1 = live ? half2v{(_Float16)1.0f, (_Float16)1.0f} : half2v{};
+        const half2v c16 = live ? half2v{(_Float16)0.0625f, (_Float16)0.0625f} : half2v{};
+        half2v d1 = live ? half2v{(_Float16)-1024.0f, (_Float16)-1024.0f} : half2v{};
+        half2v d16 = live ? half2v{(_Float16)-64.0f, (_Float16)-64.0f} : half2v{};
+        if constexpr (fast) {
+          d1 = d1 - z;
+          d16 = d16 - z;
+          bop[j][0] = b_operand4p<0, true>(cw[st][j], pk4, c1, d1, c16, d16, z);
+          bop[j][1] = b_operand4p<1, true>(cw[st][j], pk4, c1, d1, c16, d16, z);
+          bop[j][2] = b_operand4p<2, true>(cw[st][j], pk4, c1, d1, c16, d16, z);
+          bop[j][3] = b_operand4p<3, true>(cw[st][j], pk4, c1, d1, c16, d16, z);
+        } else {
+          bop[j][0] = b_operand4p<0, false>(cw[st][j], pk4, c1, d1, c16, d16, z);
+          bop[j][1] = b_operand4p<1, false>(cw[st][j], pk4, c1, d1, c16, d16, z);
+          bop[j][2] = b_operand4p<2, false>(cw[st][j], pk4, c1, d1, c16, d16, z);
+          bop[j][3] = b_operand4p<3, false>(cw[st][j], pk4, c1, d1, c16, d16, z);
+        }
+      } else {
+        const half2v c = live ? half2v{(_Float16)1.0f, kHi} : half2v{};
+        const half2v d = live ? half2v{(_Float16)-1024.0f, (_Float16)(BITS == 4 ? -64.0f : -1024.0f)} : half2v{};
+        bop[j][0] = b_operand<BITS, 0>(cw[st][j], pk, c, d, z);
+        bop[j][1] = b_operand<BITS, 1>(cw[st][j], pk, c, d, z);
+        bop[j][2] = b_operand<BITS, 2>(cw[st][j], pk, c, d, z);
+        bop[j][3] = b_operand<BITS, 3>(cw[st][j], pk, c, d, z);
+      }
     }
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
@@ -524,15 +594,33 @@ __global__ __launch_bounds__(kGemmThreads, (Tile<MB, NB>::PerCU)) void gemm_kern
     if (g < ng && lane < WR) szw[lane * kMaxGroups + g] = (szs[g] & 0xFFFFu) | (szz[g] << 16);
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   static_assert(kStages >= 3 && kStages <= 8, "the loop below unrolls up to 8 stages");
-  for (int i0 = 0; i0 < T; i0 += kStages) {
-    step(std::integral_constant<int, 0>{}, kt0 + i0, true);
-    step(std::integral_constant<int, 1>{}, kt0 + i0 + 1, i0 + 1 < T);
-    step(std::integral_constant<int, 2>{}, kt0 + i0 + 2, i0 + 2 < T);
-    if constexpr (kStages > 3) step(std::integral_constant<int, 3>{}, kt0 + i0 + 3, i0 + 3 < T);
-    if constexpr (kStages > 4) step(std::integral_constant<int, 4>{}, kt0 + i0 + 4, i0 + 4 < T);
-    if constexpr (kStages > 5) step(std::integral_constant<int, 5>{}, kt0 + i0 + 5, i0 + 5 < T);
-    if constexpr (kStages > 6) step(std::integral_constant<int, 6>{}, kt0 + i0 + 6, i0 + 6 < T);
-    if constexpr (kStages > 7) step(std::integral_constant<int, 7>{}, kt0 + i0 + 7, i0 + 7 < T);
+  auto loop = [&](auto fconst) {
+    for (int i0 = 0; i0 < T; i0 += kStages) {
+      step(std::integral_constant<int, 0>{}, kt0 + i0, true, fconst);
+      step(std::integral_constant<int, 1>{}, kt0 + i0 + 1, i0 + 1 < T, fconst);
+      step(std::integral_constant<int, 2>{}, kt0 + i0 + 2, i0 + 2 < T, fconst);
+      if constexpr (kStages > 3) step(std::integral_constant<int, 3>{}, kt0 + i0 + 3, i0 + 3 < T, fconst);
+      if constexpr (kStages > 4) step(std::integral_constant<int, 4>{}, kt0 + i0 + 4, i0 + 4 < T, fconst);
+      if constexpr (kStages > 5) step(std::integral_constant<int, 5>{}, kt0 + i0 + 5, i0 + 5 < T, fconst);
+      if constexpr (kStages > 6) step(std::integral_constant<int, 6>{}, kt0 + i0 + 6, i0 + 6 < T, fconst);
+      if constexpr (kStages > 7) step(std::integral_constant<int, 7>{}, kt0 + i0 + 7, i0 + 7 < T, fconst);
+    }
+  };
+  if constexpr (PAIR) {
+    // the wave's zero points (lane = row, its groups of the K range; rows
+    // past N read 0): all integers in [-1024, 1023]?
+    bool ok = true;
+#pragma unroll
+    for (int g = 0; g < kMaxGroups; ++g) {
+      const float zf = half_bits_to_float(szz[g] & 0xFFFFu);
+      ok = ok && (g >= ng || lane >= WR || (zf == __builtin_floorf(zf) && zf >= -1024.0f && zf <= 1023.0f));
+    }
+    if (__ballot(!ok) == 0)
+      loop(std::true_type{});
+    else
+      loop(std::false_type{});
+  } else {
+    loop(std::false_type{});
   }
   wait_vmcnt<0>();   // the trailing out-of-range loads still write LDS
 
@@ -615,6 +703,7 @@ __global__ __launch_bounds__(256) void gemm_finalize_kernel(GemmBatch a) {
 }  // namespace
 
 bool gemm_available(int bits) { return bits == 3 || bits == 4 || bits == 6 || bits == 8; }
+bool gemm_pair_order(int bits) { return bits == 4; }
 
 namespace {
 
@@ -663,14 +752,16 @@ void gemm_plan(int count, const wq_weight *w, int64_t m, int *ksplit) {
 }
 
 namespace {
-template <int BITS>
+template <int BITS, bool PAIR>
 hipError_t launch_shape(Shape sh, dim3 grid, dim3 block, const GemmBatch &a, hipStream_t s) {
   if (sh.mb == 1)
-    hipLaunchKernelGGL((gemm_kernel<BITS, 1, 1>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((gemm_kernel<BITS, 1, 1, PAIR>), grid, block, 0, s, a);
   else if (sh.mb == 2)
-    hipLaunchKernelGGL((gemm_kernel<BITS, 2, 1>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((gemm_kernel<BITS, 2, 1, PAIR>), grid, block, 0, s, a);
+  else if constexpr (!PAIR)
+    hipLaunchKernelGGL((gemm_kernel<BITS, 4, 2, false>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL((gemm_kernel<BITS, 4, 2>), grid, block, 0, s, a);
+    return hipErrorInvalidValue;   // pair order is taken by the narrow tiles only
   return hipGetLastError();
 }
 }  // namespace
@@ -681,8 +772,9 @@ size_t gemm_partial_bytes(const wq_weight &w, int64_t m, int ksplit) {
 
 hipError_t launch_gemm_batch(int count, const wq_weight *w, const uint16_t *const *xr, const int64_t *ldx,
                              int64_t m, void *const *y, const int *out_f32, const int64_t *ldy,
-                             const int *ksplit, float *const *part, hipStream_t s) {
+                             const int *ksplit, float *const *part, bool pair_order, hipStream_t s) {
   if (count <= 0 || count > kMaxBatch) return hipErrorInvalidValue;
+  if (pair_order && (!gemm_pair_order(w[0].bits) || shape_for(m).mb > 2)) return hipErrorInvalidValue;
   GemmBatch a;
   memset(&a, 0, sizeof a);
   for (int i = 0; i < kMaxBatch; ++i) a.first_tile[i] = INT32_MAX;
@@ -724,10 +816,12 @@ hipError_t launch_gemm_batch(int count, const wq_weight *w, const uint16_t *cons
   const dim3 grid((unsigned)tiles), block(kGemmThreads);
   hipError_t e = hipSuccess;
   switch (w[0].bits) {
-    case 3: e = launch_shape<3>(sh, grid, block, a, s); break;
-    case 4: e = launch_shape<4>(sh, grid, block, a, s); break;
-    case 6: e = launch_shape<6>(sh, grid, block, a, s); break;
-    case 8: e = launch_shape<8>(sh, grid, block, a, s); break;
+    case 3: e = launch_shape<3, false>(sh, grid, block, a, s); break;
+    case 4:
+      e = pair_order && sh.mb <= 2 ? launch_shape<4, true>(sh, grid, block, a, s) : launch_shape<4, false>(sh, grid, block, a, s);
+      break;
+    case 6: e = launch_shape<6, false>(sh, grid, block, a, s); break;
+    case 8: e = launch_shape<8, false>(sh, grid, block, a, s); break;
   }
   if (e != hipSuccess || fin_blocks == 0) return e;
   hipLaunchKernelGGL(gemm_finalize_kernel, dim3((unsigned)fin_blocks), dim3(256), 0, s, a);

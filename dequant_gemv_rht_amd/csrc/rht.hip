@@ -18,10 +18,11 @@ using namespace dev;
 
 namespace {
 
-// Block b of row `row`, lane jj's eight elements.
+// Block b of row `row`, lane jj's eight elements; with pair_order stored in
+// the order 0, 4, 1, 5, 2, 6, 3, 7.
 __device__ __forceinline__ void rotate_block(const uint16_t *__restrict__ x, uint16_t *y,
                                              const uint32_t *__restrict__ signs, int64_t row, int64_t b,
-                                             int jj, int64_t ldx, int64_t ldy) {
+                                             int jj, int64_t ldx, int64_t ldy, bool pair_order = false) {
   const int64_t kk = b * 128 + 8 * jj;
   const uint4 raw = *reinterpret_cast<const uint4 *>(x + row * ldx + kk);
   float v[8];
@@ -35,10 +36,17 @@ __device__ __forceinline__ void rotate_block(const uint16_t *__restrict__ x, uin
   fwht128_row16_signed(v, jj);
   const float sc = fwht_lane_sign(jj) * 0.08838834764831845f;
   uint4 out;
-  out.x = pack_half2(v[0] * sc, v[1] * sc);
-  out.y = pack_half2(v[2] * sc, v[3] * sc);
-  out.z = pack_half2(v[4] * sc, v[5] * sc);
-  out.w = pack_half2(v[6] * sc, v[7] * sc);
+  if (pair_order) {
+    out.x = pack_half2(v[0] * sc, v[4] * sc);
+    out.y = pack_half2(v[1] * sc, v[5] * sc);
+    out.z = pack_half2(v[2] * sc, v[6] * sc);
+    out.w = pack_half2(v[3] * sc, v[7] * sc);
+  } else {
+    out.x = pack_half2(v[0] * sc, v[1] * sc);
+    out.y = pack_half2(v[2] * sc, v[3] * sc);
+    out.z = pack_half2(v[4] * sc, v[5] * sc);
+    out.w = pack_half2(v[6] * sc, v[7] * sc);
+  }
   *reinterpret_cast<uint4 *>(y + row * ldy + kk) = out;
 }
 
@@ -64,6 +72,7 @@ struct RhtMat {
 struct RhtBatch {
   int32_t first_wg[kMaxBatch];   // mat[i].wg_begin, packed; INT32_MAX past count
   RhtMat mat[kMaxBatch];
+  int32_t pair_order;
 };
 
 __global__ __launch_bounds__(256) void rht_batch_kernel(RhtBatch a) {
@@ -76,7 +85,7 @@ __global__ __launch_bounds__(256) void rht_batch_kernel(RhtBatch a) {
   const int64_t nb = M.k / 128;
   const int64_t item = (int64_t)(w - M.wg_begin) * 16 + (threadIdx.x >> 4);
   if (item >= M.m * nb) return;
-  rotate_block(M.x, M.y, M.signs, item / nb, item % nb, threadIdx.x & 15, M.ldx, M.ldy);
+  rotate_block(M.x, M.y, M.signs, item / nb, item % nb, threadIdx.x & 15, M.ldx, M.ldy, a.pair_order != 0);
 }
 
 }  // namespace
@@ -91,10 +100,12 @@ hipError_t launch_rht(const uint16_t *x, uint16_t *y, const uint32_t *signs, int
 }
 
 hipError_t launch_rht_batch(int count, const uint16_t *const *x, uint16_t *const *y, const uint32_t *const *signs,
-                            int64_t m, const int64_t *k, const int64_t *ldx, const int64_t *ldy, hipStream_t s) {
+                            int64_t m, const int64_t *k, const int64_t *ldx, const int64_t *ldy, bool pair_order,
+                            hipStream_t s) {
   if (count <= 0 || count > kMaxBatch) return hipErrorInvalidValue;
   RhtBatch a;
   memset(&a, 0, sizeof a);
+  a.pair_order = pair_order ? 1 : 0;
   for (int i = 0; i < kMaxBatch; ++i) a.first_wg[i] = INT32_MAX;
   int64_t wgs = 0;
   for (int i = 0; i < count; ++i) {

@@ -107,13 +107,17 @@ int gemv_lds_bytes(int mt, int chunk, int rows, int64_t k);
 // Other launchers.
 hipError_t launch_rht(const uint16_t *x, uint16_t *y, const uint32_t *signs, int64_t m,
                       int64_t k, int64_t ldx, int64_t ldy, hipStream_t s);
-// the same rotation for up to kMaxBatch matrices of m rows in one launch
 // One plain read of `bytes` (a multiple of 16) at `src`, nothing stored
 // (the read ceiling of include/wq_measure.h).
 hipError_t launch_stream_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t s);
 
+// the same rotation for up to kMaxBatch matrices of m rows in one launch;
+// with `pair_order` each 8 consecutive outputs are stored in the order
+// 0, 4, 1, 5, 2, 6, 3, 7 (the order the int4 matrix-core kernel unpacks a
+// code word in; gemm_pair_order)
 hipError_t launch_rht_batch(int count, const uint16_t *const *x, uint16_t *const *y, const uint32_t *const *signs,
-                            int64_t m, const int64_t *k, const int64_t *ldx, const int64_t *ldy, hipStream_t s);
+                            int64_t m, const int64_t *k, const int64_t *ldx, const int64_t *ldy, bool pair_order,
+                            hipStream_t s);
 hipError_t launch_quantize(int bits, int64_t n, int64_t k, const float *w,
                            const uint32_t *signs, const uint8_t *block_bits, uint8_t *codes,
                            uint16_t *scales, uint16_t *zeros, hipStream_t s);
@@ -134,11 +138,16 @@ hipError_t launch_embed(const wq_weight &w, const int32_t *ids, int64_t count, v
 // fp32 partials go to part[i] ([ksplit][m][n], gemm_partial_bytes) and are
 // added by a second kernel.
 bool gemm_available(int bits);
+// whether the kernel for `bits` can take activations whose 8-element groups
+// are in rht_batch's pair order (int4: a cheaper unpack)
+bool gemm_pair_order(int bits);
 void gemm_plan(int count, const wq_weight *w, int64_t m, int *ksplit);
 size_t gemm_partial_bytes(const wq_weight &w, int64_t m, int ksplit);
+// pair_order: every xr[i] is in rht_batch's pair order (only where
+// gemm_pair_order(bits))
 hipError_t launch_gemm_batch(int count, const wq_weight *w, const uint16_t *const *xr, const int64_t *ldx,
                              int64_t m, void *const *y, const int *out_f32, const int64_t *ldy,
-                             const int *ksplit, float *const *part, hipStream_t s);
+                             const int *ksplit, float *const *part, bool pair_order, hipStream_t s);
 
 }  // namespace wq
 
