@@ -250,3 +250,49 @@ def test_scale_extremes(bits, m):
     assert np.all(y[:, 0] == 0)
     rel, mx = check_close(y, ref, f"scale extremes bits={bits} m={m}")
     say(f"  rel-L2 {rel:.2e} max/rms {mx:.2e}")
+
+
+# int4 on the matrix cores up to 64 rows takes its activations in pair order
+# from the rotation pre-pass when every linear of the call is rotated, and
+# picks per wave between one fma per code pair (every zero point of the
+# wave's rows an integer) and the general path.  Cases: zero points moved
+# off the integers for a few rows only (waves of both kinds in one launch),
+# no rotation (natural order), and a grouped call that does not rotate.
+@pytest.mark.parametrize("m", [24, 63])
+def test_gemm_pair_order_paths(m):
+    rng = np.random.default_rng(1600 + m)
+    n, k = 256, 2560
+    w = W.weight(k, n, rng)
+    x = W.activations(m, k, rng)
+    signs = W.sign_bits(k, rng)
+    q, s, z = OR.prepare(w, signs, 4)
+    z = z.copy()
+    z[40:47] = (z[40:47].astype(np.float32) + np.float32(0.375)).astype(np.float16)   # 7 rows, one wave's tile
+    ref = OL.linear(q, s, z, x, signs)
+    packed, _ = dq.wq_pack(dev(q), 4)
+    qw = dq.QWeight(4, n, k, packed, dev(s), dev(z), dev_u32(signs))
+    say(f"pair order m={m}: fractional zero points in rows 40..46")
+    rel, mx = check_close(dq.wq_linear(qw, dev(x)).float().cpu().numpy(), ref, f"pair order mixed zeros m={m}")
+    say(f"  rel-L2 {rel:.2e} max/rms {mx:.2e}")
+
+    say(f"pair order m={m}: no rotation")
+    _case(130, 2560, m, 4, rht=False, seed=1610 + m, label=f"int4 unrotated m={m}")
+
+    # a call that does not rotate, over linears that carry signs (the caller
+    # rotated the activations): natural order for every linear
+    say(f"pair order m={m}: grouped call, rotation off")
+    shapes = [(256, 2560), (96, 1024)]
+    qs, xs, refs = [], [], []
+    for i, (nn, kk) in enumerate(shapes):
+        r = np.random.default_rng(1620 + m + i)
+        wi = W.weight(kk, nn, r)
+        xi = W.activations(m, kk, r)
+        si = W.sign_bits(kk, r)
+        qi, sc, zi = OR.prepare(wi, si, 4)
+        refs.append(OL.linear(qi, sc, zi, xi, None))
+        pk, _ = dq.wq_pack(dev(qi), 4)
+        qs.append(dq.QWeight(4, nn, kk, pk, dev(sc), dev(zi), dev_u32(si)))
+        xs.append(dev(xi))
+    for (nn, kk), y, ref in zip(shapes, dq.wq_linear_batch(qs, xs, fuse_rht=False), refs):
+        rel, mx = check_close(y.float().cpu().numpy(), ref, f"grouped n={nn} k={kk} unrotated m={m}")
+        say(f"  n={nn} k={kk}: rel-L2 {rel:.2e} max/rms {mx:.2e}")

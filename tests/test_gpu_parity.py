@@ -397,13 +397,16 @@ def test_batch_shared_input_rotated_once(m):
         check_close(a.float().cpu().numpy(), ref, f"shared input m={m}")
 
 
-def test_deterministic_with_uninitialised_workspace():
+@pytest.mark.parametrize("m,k", [(16, 9728), (40, 4096)])
+def test_deterministic_with_uninitialised_workspace(m, k):
     # the workspace needs no initialisation: one filled with NaN bit
-    # patterns gives the same bits as a zeroed one, call after call
-    say("determinism")
-    w, x, signs = _inputs(512, 4096, 2, 5)
+    # patterns gives the same bits as a zeroed one, call after call (16
+    # rows at K 9728: the streaming kernel's K-split partial sums; 40 rows:
+    # the GEMM's rotated activations)
+    say(f"determinism m={m} k={k}")
+    w, x, signs = _inputs(512, k, m, 5)
     qw = _gpu_weight(w, signs, 4)
-    need = dq.wq_linear_workspace(qw, 2)
+    need = dq.wq_linear_workspace(qw, m)
     assert need > 0
     xd = dev(x)
     first = dq.wq_linear(qw, xd, workspace=dq.new_workspace(need))
