@@ -480,41 +480,19 @@ GemmLayout gemm_layout(int count, const wq_weight *w, int64_t m, bool rotate) {
 
 size_t gemm_path_workspace(const wq_weight &w, int64_t m) { return gemm_layout(1, &w, m, true).total; }
 
-// Batches of 5 to 16 rows with one uniform code width stream the weights
-// once through the matrix cores (mma_kernel), at any K (the int4 block of
-// seven projections: 8 rows 35.6 -> 29.9 us, 16 rows 59.4 -> 30.1 us against
-// the row-quad tiles; at 4 rows and below the row-quad tiles, from 17 rows
-// the GEMM's narrow tiles are faster).
-constexpr int64_t kMmaMinRows = 5, kMmaMaxRows = 16;
-bool use_mma(const wq_weight &w, int64_t m) {
-  return m >= kMmaMinRows && m <= kMmaMaxRows && wq::gemm_available(w.bits);
-}
-
-// Workspace of a narrow matrix-core launch: each split linear's fp32
-// partial sums (the kernel rotates in LDS, so no rotated copies).
-struct MmaLayout {
-  size_t part[WQ_MAX_BATCH], total;
-  wq::MmaPlan plan[WQ_MAX_BATCH];
-};
-
-MmaLayout mma_layout(int count, const wq_weight *w, int64_t m) {
-  MmaLayout g;
-  wq::mma_plan(count, w, m, device_cus(), g.plan);
-  size_t off = 0;
-  for (int i = 0; i < count; ++i) {
-    g.part[i] = off;
-    off += align256(wq::mma_partial_bytes(w[i], m, g.plan[i]));
-  }
-  g.total = off;
-  return g;
-}
-
-// The rotations of a matrix-core call, all in one launch into the
-// workspace at ws + rot[i] (linears that share an input share its
-// rotation): xr[i], ldr[i] receive each linear's activation operand.
-wq_status rotate_inputs(int count, const wq_weight *w, const uint16_t *const *x, const int64_t *ldx, int64_t m,
-                        bool rotate, char *ws, const size_t *rot, bool pair_order, const uint16_t **xr,
-                        int64_t *ldr, hipStream_t s, const char *who) {
+// Validated linears on the matrix cores: rotations into the workspace, then
+// one GEMM launch for all of them (plus one launch adding K-split partials).
+wq_status run_gemm(int count, const wq_weight *w, const uint16_t *const *x, const int64_t *ldx, int64_t m,
+                   void *const *y, const wq_dtype *ydt, const int64_t *ldy, bool rotate, void *workspace,
+                   hipStream_t s, const char *who) {
+  const GemmLayout g = gemm_layout(count, w, m, rotate);
+  char *ws = static_cast<char *>(workspace);
+  const uint16_t *xr[WQ_MAX_BATCH];
+  int64_t ldr[WQ_MAX_BATCH], ldo[WQ_MAX_BATCH];
+  int f32[WQ_MAX_BATCH];
+  float *part[WQ_MAX_BATCH];
+  void *yo[WQ_MAX_BATCH];
+  // the rotations of all linears in one launch
   int nr = 0;
   const uint16_t *rx[WQ_MAX_BATCH];
   uint16_t *ry[WQ_MAX_BATCH];
@@ -529,7 +507,7 @@ wq_status rotate_inputs(int count, const wq_weight *w, const uint16_t *const *x,
       xr[i] = xr[j];
       ldr[i] = ldr[j];
     } else if (rotate && w[i].rht_signs) {
-      uint16_t *xt = reinterpret_cast<uint16_t *>(ws + rot[i]);
+      uint16_t *xt = reinterpret_cast<uint16_t *>(ws + g.rot[i]);
       ldr[i] = rotated_ld(w[i]);
       rx[nr] = x[i];
       ry[nr] = xt;
@@ -540,24 +518,6 @@ wq_status rotate_inputs(int count, const wq_weight *w, const uint16_t *const *x,
       ++nr;
       xr[i] = xt;
     }
-  }
-  if (!nr) return WQ_OK;
-  return hip_status(wq::launch_rht_batch(nr, rx, ry, rs, m, rk, rlx, rly, pair_order, s), who);
-}
-
-// Validated linears on the matrix cores: rotations into the workspace, then
-// one GEMM launch for all of them (plus one launch adding K-split partials).
-wq_status run_gemm(int count, const wq_weight *w, const uint16_t *const *x, const int64_t *ldx, int64_t m,
-                   void *const *y, const wq_dtype *ydt, const int64_t *ldy, bool rotate, void *workspace,
-                   hipStream_t s, const char *who) {
-  const GemmLayout g = gemm_layout(count, w, m, rotate);
-  char *ws = static_cast<char *>(workspace);
-  const uint16_t *xr[WQ_MAX_BATCH];
-  int64_t ldr[WQ_MAX_BATCH], ldo[WQ_MAX_BATCH];
-  int f32[WQ_MAX_BATCH];
-  float *part[WQ_MAX_BATCH];
-  void *yo[WQ_MAX_BATCH];
-  for (int i = 0; i < count; ++i) {
     part[i] = g.ksplit[i] > 1 ? reinterpret_cast<float *>(ws + g.part[i]) : nullptr;
     f32[i] = ydt[i] == WQ_F32;
     ldo[i] = ldy[i];
@@ -571,40 +531,17 @@ wq_status run_gemm(int count, const wq_weight *w, const uint16_t *const *x, cons
   // unpack worse with the matrix products (M = 512: 141.7 -> 147.8 us).
   bool pair_order = wq::gemm_pair_order(w[0].bits) && m <= 64;
   for (int i = 0; i < count; ++i) pair_order = pair_order && rotate && w[i].rht_signs;
-  const wq_status st = rotate_inputs(count, w, x, ldx, m, rotate, ws, g.rot, pair_order, xr, ldr, s, who);
-  if (st != WQ_OK) return st;
-  return hip_status(wq::launch_gemm_batch(count, w, xr, ldr, m, yo, f32, ldo, g.ksplit, part, pair_order, s), who);
-}
-
-// Narrow batches (mma_kernel): one streaming launch over all the linears,
-// each workgroup rotating the activations it needs, then one launch adding
-// K-split partials.
-wq_status run_mma(int count, const wq_weight *w, const uint16_t *const *x, const int64_t *ldx, int64_t m,
-                  void *const *y, const wq_dtype *ydt, const int64_t *ldy, bool rotate, void *workspace,
-                  hipStream_t s, const char *who) {
-  const MmaLayout g = mma_layout(count, w, m);
-  char *ws = static_cast<char *>(workspace);
-  const uint32_t *sg[WQ_MAX_BATCH];
-  int64_t ldo[WQ_MAX_BATCH];
-  int f32[WQ_MAX_BATCH];
-  float *part[WQ_MAX_BATCH];
-  void *yo[WQ_MAX_BATCH];
-  for (int i = 0; i < count; ++i) {
-    sg[i] = rotate ? w[i].rht_signs : nullptr;
-    part[i] = g.plan[i].ksplit > 1 ? reinterpret_cast<float *>(ws + g.part[i]) : nullptr;
-    f32[i] = ydt[i] == WQ_F32;
-    ldo[i] = ldy[i];
-    yo[i] = y[i];
+  if (nr) {
+    const wq_status st = hip_status(wq::launch_rht_batch(nr, rx, ry, rs, m, rk, rlx, rly, pair_order, s), who);
+    if (st != WQ_OK) return st;
   }
-  return hip_status(wq::launch_mma_batch(count, w, x, ldx, rotate ? sg : nullptr, m, yo, f32, ldo, g.plan, part, s),
-                    who);
+  return hip_status(wq::launch_gemm_batch(count, w, xr, ldr, m, yo, f32, ldo, g.ksplit, part, pair_order, s), who);
 }
 
 // One validated linear: the matrix-core path, the GEMV over all m rows
 // (uniform width), or the GEMV in chunks of 16 batch rows (mixed width).
 wq_status linear_one(const wq_weight &w, const uint16_t *x, int64_t m, int64_t ldx, void *y, wq_dtype y_dtype,
                      int64_t ldy, bool rotate, void *workspace, hipStream_t s) {
-  if (use_mma(w, m)) return run_mma(1, &w, &x, &ldx, m, &y, &y_dtype, &ldy, rotate, workspace, s, "wq_linear");
   if (use_gemm(w, m)) return run_gemm(1, &w, &x, &ldx, m, &y, &y_dtype, &ldy, rotate, workspace, s, "wq_linear");
   if (uses_xprep(w, m)) return run_gemv(1, &w, &x, &ldx, m, &y, &y_dtype, &ldy, rotate, workspace, s);
   const size_t esz = y_dtype == WQ_F32 ? 4 : 2;
@@ -735,7 +672,6 @@ size_t wq_linear_workspace(const wq_weight *w, int64_t m) {
     fail(WQ_E_ARG, "wq_linear_workspace: m must be positive");
     return (size_t)-1;
   }
-  if (use_mma(*w, m)) return mma_layout(1, w, m).total;
   if (use_gemm(*w, m)) return gemm_path_workspace(*w, m);
   // the GEMV above one batch row: the arranged activations of all m rows
   return uses_xprep(*w, m) ? xprep_bytes(w->k, m) : 0;
@@ -768,16 +704,13 @@ size_t wq_linear_batch_workspace(int32_t count, const wq_weight *w, int64_t m) {
     fail(WQ_E_ARG, "wq_linear_batch_workspace: m must be positive");
     return (size_t)-1;
   }
-  // use_mma and use_gemm alone decide which path, and so which workspace, the call takes
-  bool mma = true, gemm = true;
+  bool gemm = true;   // use_gemm alone decides which path, and so which workspace, the call takes
   size_t all = 0;
   for (int i = 0; i < count; ++i) {
     if (check_weight(&w[i], "wq_linear_batch_workspace") != WQ_OK) return (size_t)-1;
-    mma = mma && use_mma(w[i], m) && w[i].bits == w[0].bits;
     gemm = gemm && use_gemm(w[i], m) && w[i].bits == w[0].bits;
     if (uses_xprep(w[i], m)) all += xprep_bytes(w[i].k, m);
   }
-  if (mma) return mma_layout(count, w, m).total;
   // above 16 rows with one uniform width: one matrix-core launch over all of them;
   // below: every linear's arranged activations side by side (none for the
   // mixed layout, whose GEMV needs no workspace)
@@ -810,9 +743,6 @@ wq_status wq_linear_batch(int32_t count, const wq_weight *w, const uint16_t *con
     return fail(WQ_E_WORKSPACE, "wq_linear_batch: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
   if (workspace && !aligned16(workspace))
     return fail(WQ_E_ALIGN, "wq_linear_batch: workspace must be 16-byte aligned");
-  if (use_mma(w[0], m))   // one width (checked above): all streamed through the matrix cores in one launch
-    return run_mma(count, w, x, ldx, m, y, y_dtype, ldy, rotate, workspace, (hipStream_t)stream,
-                   "wq_linear_batch");
   if (use_gemm(w[0], m))   // one width (checked above): all on the matrix cores in one launch
     return run_gemm(count, w, x, ldx, m, y, y_dtype, ldy, rotate, workspace, (hipStream_t)stream,
                     "wq_linear_batch");

@@ -57,10 +57,8 @@
 
 #include <algorithm>
 #include <climits>
-#include <cmath>
 #include <cstring>
 #include <type_traits>
-#include <utility>
 
 namespace wq {
 using namespace dev;
@@ -702,346 +700,6 @@ __global__ __launch_bounds__(256) void gemm_finalize_kernel(GemmBatch a) {
   }
 }
 
-
-// ---------------------------------------------------------------------------
-// Narrow batches (up to 16 rows): the weights streamed once, the products on
-// v_mfma_f32_16x16x32_f16.
-//
-// At a few batch rows the matrix path above reads each weight once per tile
-// of 32 rows, but its steps are short (64 k, a barrier each) and the weight
-// read runs at a third of HBM speed.  This kernel is built like the batch-1
-// stream instead: a workgroup of 16 waves owns `rows` output rows of one
-// linear over a range of K (one K split); the split's activations of all
-// batch rows and the rows' scales and zeros over it sit in LDS for the
-// workgroup's whole life, and every wave walks its own share of the
-// workgroup's units with no barrier: a unit is 16 rows x one group of 128
-// (the lane's 32-code slice of one row), four products of 16 x 16 x 32
-// whose fp32 sum is scaled once by the group's scale (model card "24B0978 -
-// Week 01 - Track 2, 20% target", section "How these techniques accelerate
-// inference on CUDA", group-wise affine paragraph: dequantise in registers,
-// one scale per group).  Each wave keeps kMmaDepth units of code loads in
-// flight in registers.
-//
-// Units are numbered tile-major (16-row tile t, group g: u = t G + g) and
-// wave v takes [U v / 16, U (v + 1) / 16).  The last tile of a workgroup
-// may hold fewer than 16 rows (rows past it read zero and are not stored).
-// A tile whose groups one wave covers alone is written out by it; a tile cut
-// between waves leaves one fp32 piece per wave (kept in registers until the
-// loop ends, then put in LDS over the activations), added after the
-// workgroup's barrier by the wave that holds the tile's last group, in wave
-// (K) order, so the result does not depend on timing.  A K split writes
-// fp32 partial outputs that gemm_finalize_kernel adds in split order.
-//
-// MFMA operand layout (16 x 16 x 32): lane l holds A[l % 16][8 (l / 16) ..
-// +8] and B[8 (l / 16) .. +8][l % 16]; accumulator register v of lane l is
-// D[4 (l / 16) + v][l % 16].  Lane l = 16 h + c takes row c of the tile and
-// codes 32 h .. 32 h + 31 of the group; product j uses codes 8 j .. 8 j + 7
-// of them, so its A fragment is batch row c, elements 32 h + 8 j .. +8 of
-// the group (in the unpack order: pair order for int4 when the rotation
-// stored it so).
-//
-// LDS.  Activations: 16-byte chunk q (elements 8 q .. 8 q + 7 of the K
-// split) of batch row m at (q MR + m) x 16 bytes, MR = the batch rows
-// rounded up to 4, 8 or 16: the 16 lanes of one h read 16 consecutive
-// chunks (rows c, or c mod MR below 16 rows; those rows' outputs are
-// dropped), conflict-free.  Rows past M are loaded as zeros.  Then the
-// scale and zero of local row r, group g as one word (s | z << 16) at r S +
-// g, S = the split's groups rounded up to odd (the 16 rows of a read fall
-// in 16 different banks).
-constexpr int kMmaWaves = 16, kMmaThreads = 64 * kMmaWaves;
-// code loads in flight per wave (units): 8 for 3- and 4-bit codes (one or
-// two 16-byte loads a unit), 4 for 6- and 8-bit codes (the registers)
-__host__ __device__ constexpr int mma_depth(int bits) { return bits <= 4 ? 8 : 4; }
-constexpr int kMmaLds = 160 * 1024;
-constexpr int kMmaABytes = 128 * 1024;       // the split's activations, at most
-constexpr int kMmaSzWords = 8192;            // scale/zero words of a workgroup, at most
-constexpr int kMmaAPerLane = kMmaABytes / 16 / kMmaThreads;   // 16-byte activation chunks per thread
-constexpr int kMmaSzPerLane = kMmaSzWords / kMmaThreads;      // scale/zero words per thread
-static_assert(kMmaABytes + 4 * kMmaSzWords <= kMmaLds, "activations and scales within LDS");
-// the pieces, after the loop: two per wave of MT KB
-__host__ __device__ constexpr int mma_piece_bytes(int mt) { return kMmaWaves * 2 * mt * 64 * 16; }
-
-struct MmaLin {
-  const uint32_t *codes;
-  const uint16_t *scales, *zeros;
-  const uint16_t *x;     // activations [m][ldx]
-  const uint32_t *signs; // rotation signs (rotated in the kernel), or NULL
-  void *y;
-  float *part;           // ksplit > 1: fp32 partial outputs [ksplit][m][n]
-  int64_t ldx, ldy;
-  int32_t n, k, out_f32;
-  int32_t rows;          // output rows per workgroup
-  int32_t kgroups;       // groups of 128 per K split
-  int32_t ksplit, rblocks, wg_begin;
-};
-
-struct MmaBatch {
-  int32_t first_wg[kMaxBatch];   // lin[i].wg_begin, packed; INT32_MAX past count
-  MmaLin lin[kMaxBatch];
-  int32_t count, wgs, m;
-};
-
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-template <typename F, size_t... I>
-__device__ __forceinline__ void unroll_stages(F &&f, std::index_sequence<I...>) {
-  (f(std::integral_constant<int, (int)I>{}), ...);
-}
-
-// MR: batch rows in LDS (4, 8 or 16); MT = m tiles of 16 per product (one)
-template <int BITS, int MR, bool PAIR>
-__global__ __launch_bounds__(kMmaThreads, 1) void mma_kernel(MmaBatch a) {
-  static_assert(!PAIR || BITS == 4, "pair order is an int4 layout");
-  static_assert(MR == 4 || MR == 8 || MR == 16, "batch rows in LDS");
-  constexpr int MT = 1;
-  constexpr int D = mma_depth(BITS);
-  extern __shared__ __attribute__((aligned(16))) uint8_t mma_smem[];
-  const int wg = blockIdx.x;
-  int l = 0;
-#pragma unroll
-  for (int i = 1; i < kMaxBatch; ++i)
-    if (wg >= a.first_wg[i]) l = i;
-  const MmaLin L = a.lin[l];
-  const int local = wg - L.wg_begin;
-  const int rb = local % L.rblocks, ks = local / L.rblocks;
-  const int row0 = rb * L.rows;
-  const int G = L.k / kGroup, g0 = ks * L.kgroups, Gw = min(L.kgroups, G - g0);
-  const int nrows = min(L.rows, L.n - row0), tiles = (nrows + 15) >> 4, U = tiles * Gw;
-  const int M = a.m;
-  const int wpr = (L.k / kSlice) * BITS;   // code words per weight row
-  const int t = threadIdx.x, lane = t & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int c = lane & 15, h = lane >> 4;
-
-  // Prologue: every thread loads its activation pieces and scale/zero
-  // pairs (blocks past the split, rows past M and pairs past the rows read
-  // zero), the code loads of its wave's first units go out, then the
-  // activations (rotated: the block Hadamard transform of the model card
-  // "24B0978 - Week 01 - Track 2, 20% target", paragraph on the random
-  // Hadamard transform, as in the batch-1 kernel), scales and zeros are
-  // written to LDS.  Activation item it = 16-lane row (t / 16) + 64 i of
-  // the workgroup: block it / MR of the split, batch row it % MR; lane jj =
-  // t % 16 holds its elements 8 jj .. 8 jj + 7, LDS chunk 16 b + jj.
-  const int nchunk = Gw * 16 * MR, szs = Gw | 1, nsz = nrows * Gw;
-  uint8_t *const as = mma_smem;
-  uint32_t *const szl = reinterpret_cast<uint32_t *>(mma_smem + (size_t)nchunk * 16);
-  const int jj = t & 15;
-  u32x4 av[kMmaAPerLane];
-  uint32_t sg[kMmaAPerLane];
-  uint32_t sp[kMmaSzPerLane], zp[kMmaSzPerLane];
-  {
-    const rsrc_t rx = make_rsrc(L.x, (uint32_t)((size_t)M * L.ldx * 2));
-    const rsrc_t rsg = make_rsrc(L.signs, L.signs ? (uint32_t)(L.k / 8) : 0u);
-    const uint32_t kb = (uint32_t)g0 * (kGroup * 2);
-#pragma unroll
-    for (int i = 0; i < kMmaAPerLane; ++i) {
-      const int it = (t >> 4) + 64 * i, b = it / MR, mm = it % MR;
-      const bool in = b < Gw;
-      const uint32_t vo = in && mm < M ? (uint32_t)((size_t)mm * L.ldx * 2) + kb + (uint32_t)(b * 256 + jj * 16) : kOOB;
-      av[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, vo, 0, 0));
-      // sign bits of elements k .. k + 7, k = 128 (g0 + b) + 8 jj: byte jj % 4 of word k / 32
-      sg[i] = __builtin_amdgcn_raw_buffer_load_b32(rsg, in ? (uint32_t)((g0 + b) * 16 + (jj >> 2) * 4) : kOOB, 0, 0);
-    }
-    // pair idx: local row idx / Gw, group idx % Gw (exact: idx < 2^13, Gw < 2^11)
-    const uint64_t inv = ((1u << 24) + (uint32_t)Gw - 1) / (uint32_t)Gw;
-    const rsrc_t rs = make_rsrc(L.scales + (size_t)row0 * G, (uint32_t)nrows * G * 2);
-    const rsrc_t rz = make_rsrc(L.zeros + (size_t)row0 * G, (uint32_t)nrows * G * 2);
-#pragma unroll
-    for (int i = 0; i < kMmaSzPerLane; ++i) {
-      const uint32_t idx = (uint32_t)(t + i * kMmaThreads), r = (uint32_t)((idx * inv) >> 24), g = idx - r * (uint32_t)Gw;
-      const uint32_t vo = idx < (uint32_t)nsz ? (r * (uint32_t)G + (uint32_t)g0 + g) * 2 : kOOB;
-      sp[i] = __builtin_amdgcn_raw_buffer_load_b16(rs, vo, 0, 0);
-      zp[i] = __builtin_amdgcn_raw_buffer_load_b16(rz, vo, 0, 0);
-    }
-  }
-
-  // this wave's units; a wave with none (U < 16) loads the last unit and computes nothing
-  const int u0 = (int)((int64_t)U * wave / kMmaWaves), u1 = (int)((int64_t)U * (wave + 1) / kMmaWaves);
-  const int nu = u1 - u0;
-  const int ulast = max(u1, 1 + min(u0, U - 1)) - 1;
-  int ul = min(u0, U - 1), tl = ul / Gw, gl = ul - tl * Gw;   // load cursor
-  const uint32_t wvo = (uint32_t)(c * wpr * 4 + h * BITS * 4);
-  // the load cursor's tile: its rows' codes (the resource is rebuilt when the tile changes)
-  rsrc_t rc;
-  auto set_tile = [&]() {
-    rc = make_rsrc(L.codes + (size_t)(row0 + 16 * tl) * wpr, (uint32_t)min(16, nrows - 16 * tl) * (uint32_t)wpr * 4);
-  };
-  set_tile();
-  uint32_t cw[D][BITS];
-  auto issue = [&](auto sconst) {
-    constexpr int st = decltype(sconst)::value;
-    load_slice<BITS>(rc, wvo, (uint32_t)(g0 + gl) * (4 * BITS * 4), cw[st]);
-    if (ul < ulast) {
-      ++ul;
-      if (++gl == Gw) {
-        gl = 0;
-        ++tl;
-        set_tile();
-      }
-    }
-  };
-  unroll_stages(issue, std::make_index_sequence<D>{});
-#pragma unroll
-  for (int i = 0; i < kMmaAPerLane; ++i) {
-    // (the wave's four 16-lane rows hold items 4 wave .. 4 wave + 3 + 64 i)
-    if (4 * wave + 64 * i >= Gw * MR) break;
-    const int it = (t >> 4) + 64 * i, b = it / MR, mm = it % MR;
-    u32x4 o = av[i];
-    if (L.signs) {   // whole waves alike: the DPP stages see whole 16-lane rows
-      float v[8];
-      const uint32_t w4[4] = {o.x, o.y, o.z, o.w};
-      const uint32_t sb = sg[i] >> (8 * (jj & 3));
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float f = half_bits_to_float((w4[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-        v[e] = ((sb >> e) & 1u) ? -f : f;
-      }
-      fwht128_row16_signed(v, jj);
-      const float sc = fwht_lane_sign(jj) * 0.08838834764831845f;   // 1 / sqrt(128)
-      if constexpr (PAIR)
-        o = u32x4{pack_half2(v[0] * sc, v[4] * sc), pack_half2(v[1] * sc, v[5] * sc),
-                  pack_half2(v[2] * sc, v[6] * sc), pack_half2(v[3] * sc, v[7] * sc)};
-      else
-        o = u32x4{pack_half2(v[0] * sc, v[1] * sc), pack_half2(v[2] * sc, v[3] * sc),
-                  pack_half2(v[4] * sc, v[5] * sc), pack_half2(v[6] * sc, v[7] * sc)};
-    }
-    if (b < Gw) *reinterpret_cast<u32x4 *>(as + (size_t)((16 * b + jj) * MR + mm) * 16) = o;
-  }
-  {
-    const uint64_t inv = ((1u << 24) + (uint32_t)Gw - 1) / (uint32_t)Gw;
-#pragma unroll
-    for (int i = 0; i < kMmaSzPerLane; ++i) {
-      const uint32_t idx = (uint32_t)(t + i * kMmaThreads), r = (uint32_t)((idx * inv) >> 24), g = idx - r * (uint32_t)Gw;
-      if (idx < (uint32_t)nsz) szl[r * (uint32_t)szs + g] = (sp[i] & 0xFFFFu) | (zp[i] << 16);
-    }
-  }
-  __syncthreads();
-
-  // lane's A chunk for product j of local group g, m tile i:
-  // (16 g + 4 h + j) MR + 16 i + (c or c mod MR)
-  const uint8_t *ab = as + (size_t)((4 * h * MR + (MR < 16 ? (c & (MR - 1)) : c)) * 16);
-  const PairConsts pk = pair_consts<BITS>();
-  const PairConsts4 pk4 = pair_consts4();
-  constexpr _Float16 kHi = BITS == 4 ? (_Float16)0.0625f : (_Float16)1.0f;
-
-  // outputs of tile tt from the lane's accumulators: D[4 h + v][c] of m tile i
-  auto store = [&](int tt, const f32x4 (&v)[MT]) {
-    if (16 * tt + c >= nrows) return;
-    const int col = row0 + 16 * tt + c;
-#pragma unroll
-    for (int i = 0; i < MT; ++i)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = 16 * i + 4 * h + e;
-        if (row >= M) continue;
-        if (L.ksplit > 1) {
-          L.part[((size_t)ks * M + row) * L.n + col] = v[i][e];
-        } else if (L.out_f32) {
-          reinterpret_cast<float *>(L.y)[(size_t)row * L.ldy + col] = v[i][e];
-        } else {
-          const _Float16 hv = (_Float16)v[i][e];
-          reinterpret_cast<uint16_t *>(L.y)[(size_t)row * L.ldy + col] = __builtin_bit_cast(uint16_t, hv);
-        }
-      }
-  };
-
-  f32x4 acc[MT], piece[2][MT];
-#pragma unroll
-  for (int i = 0; i < MT; ++i) acc[i] = piece[0][i] = piece[1][i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  const int tfirst = min(u0, U - 1) / Gw;
-  int tc = tfirst, gc = min(u0, U - 1) - tfirst * Gw, uc = u0;   // compute cursor
-  // One unit.  Code loads and products run unconditionally (units past the
-  // wave's range recompute its last unit and are dropped), so that no load
-  // sits in a branch: the compiler's waits for a stage's registers then
-  // count only the loads issued after them.
-  auto step = [&](auto sconst) {
-    constexpr int st = decltype(sconst)::value;
-    const bool active = uc < u1;
-    const uint32_t szv = szl[(16 * tc + c) * szs + gc];
-    half8 b[4];
-    const half2v z = as_h2((szv >> 16) * 0x10001u);
-    if constexpr (PAIR) {
-      const half2v c1 = {(_Float16)1.0f, (_Float16)1.0f}, d1 = {(_Float16)-1024.0f, (_Float16)-1024.0f};
-      const half2v c16 = {(_Float16)0.0625f, (_Float16)0.0625f}, d16 = {(_Float16)-64.0f, (_Float16)-64.0f};
-      b[0] = b_operand4p<0, false>(cw[st], pk4, c1, d1, c16, d16, z);
-      b[1] = b_operand4p<1, false>(cw[st], pk4, c1, d1, c16, d16, z);
-      b[2] = b_operand4p<2, false>(cw[st], pk4, c1, d1, c16, d16, z);
-      b[3] = b_operand4p<3, false>(cw[st], pk4, c1, d1, c16, d16, z);
-    } else {
-      const half2v cc = {(_Float16)1.0f, kHi};
-      const half2v dd = {(_Float16)-1024.0f, (_Float16)(BITS == 4 ? -64.0f : -1024.0f)};
-      b[0] = b_operand<BITS, 0>(cw[st], pk, cc, dd, z);
-      b[1] = b_operand<BITS, 1>(cw[st], pk, cc, dd, z);
-      b[2] = b_operand<BITS, 2>(cw[st], pk, cc, dd, z);
-      b[3] = b_operand<BITS, 3>(cw[st], pk, cc, dd, z);
-    }
-    const float s = half_bits_to_float(szv & 0xFFFFu);
-    // this stage's registers now take a later unit: only after every use
-    // of their current contents (a load moved above those uses would need
-    // other registers and a copy, and so a wait, at the loop's back edge)
-    asm volatile("" ::"v"(b[0]), "v"(b[1]), "v"(b[2]), "v"(b[3]) : "memory");
-    issue(sconst);
-    const uint8_t *ag = ab + (size_t)gc * (16 * MR * 16);
-#pragma unroll
-    for (int i = 0; i < MT; ++i) {
-      f32x4 p = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const half8 av8 = *reinterpret_cast<const half8 *>(ag + j * (MR * 16) + i * 256);
-#if defined(__HIP_DEVICE_COMPILE__)   // the 16x16x32 f16 MFMA exists only in the gfx950 pass
-        p = __builtin_amdgcn_mfma_f32_16x16x32_f16(av8, b[j], p, 0, 0, 0);
-#endif
-      }
-      acc[i] = p * s + acc[i];
-    }
-    // the end of a tile or of the wave's range: out whole, or kept as a piece
-    if (active && (gc + 1 == Gw || uc + 1 == u1)) {
-      if (gc + 1 == Gw && tc * Gw >= u0) {
-        store(tc, acc);
-      } else if (tc == tfirst) {
-#pragma unroll
-        for (int i = 0; i < MT; ++i) piece[0][i] = acc[i];
-      } else {
-#pragma unroll
-        for (int i = 0; i < MT; ++i) piece[1][i] = acc[i];
-      }
-#pragma unroll
-      for (int i = 0; i < MT; ++i) acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    }
-    ++uc;
-    if (++gc == Gw) {
-      gc = 0;
-      ++tc;
-    }
-  };
-  for (int i0 = 0; i0 < nu; i0 += D) unroll_stages(step, std::make_index_sequence<D>{});
-  // A tile cut between waves: every wave's pieces go to LDS (over the
-  // activations, now read by all), and the wave holding the tile's last
-  // group adds them in wave order (a wave's piece of its first tile is
-  // slot 0, of its last tile slot 1).
-  __syncthreads();
-  f32x4 *pl = reinterpret_cast<f32x4 *>(mma_smem);   // [wave][slot][mt][lane]
-#pragma unroll
-  for (int sl = 0; sl < 2; ++sl)
-#pragma unroll
-    for (int i = 0; i < MT; ++i) pl[((wave * 2 + sl) * MT + i) * 64 + lane] = piece[sl][i];
-  __syncthreads();
-  if (nu > 0 && u0 > tfirst * Gw && (tfirst + 1) * Gw <= u1) {
-    const int ustart = tfirst * Gw;
-    f32x4 sum[MT];
-#pragma unroll
-    for (int i = 0; i < MT; ++i) sum[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    for (int w = 0; w <= wave; ++w) {
-      const int a0 = (int)((int64_t)U * w / kMmaWaves), a1 = (int)((int64_t)U * (w + 1) / kMmaWaves);
-      if (a1 <= ustart || a0 == a1) continue;
-      const int slot = a0 >= ustart ? 0 : 1;
-#pragma unroll
-      for (int i = 0; i < MT; ++i) sum[i] += pl[((w * 2 + slot) * MT + i) * 64 + lane];
-    }
-    store(tfirst, sum);
-  }
-}
-
 }  // namespace
 
 bool gemm_available(int bits) { return bits == 3 || bits == 4 || bits == 6 || bits == 8; }
@@ -1167,158 +825,6 @@ hipError_t launch_gemm_batch(int count, const wq_weight *w, const uint16_t *cons
   }
   if (e != hipSuccess || fin_blocks == 0) return e;
   hipLaunchKernelGGL(gemm_finalize_kernel, dim3((unsigned)fin_blocks), dim3(256), 0, s, a);
-  return hipGetLastError();
-}
-
-}  // namespace wq
-
-namespace wq {
-
-// ---------------------------------------------------------------------------
-// Narrow batches on the matrix cores (mma_kernel): plan and launch
-// ---------------------------------------------------------------------------
-int mma_batch_rows(int64_t m) { return m <= 4 ? 4 : m <= 8 ? 8 : 16; }
-
-int mma_max_groups(int64_t m) { return kMmaABytes / (16 * 16 * mma_batch_rows(m)); }
-
-// K is cut into as few splits as the LDS allows (each split's activations
-// of all batch rows must fit: at most mma_max_groups groups), and each
-// split's rows are dealt to workgroups in equal runs (at most kMmaSzWords
-// scale/zero pairs each).  Each linear gets the fewest workgroups that keep
-// every one within T bytes of codes, scales and zeros; T is the smallest
-// for which the call needs no more than `wgs` workgroups (the CUs: one
-// workgroup each).
-namespace {
-MmaPlan mma_split(const wq_weight &w, int64_t m, double T, int64_t *wgs) {
-  const int64_t G = w.k / kGroup, N = w.n, gmax = mma_max_groups(m);
-  const int64_t s = (G + gmax - 1) / gmax, gs = (G + s - 1) / s, splits = (G + gs - 1) / gs;
-  const double per = 16.0 * w.bits + 4.0;   // bytes of one row and one group
-  int64_t per_split = (int64_t)std::ceil((double)N * (double)gs * per / T);
-  per_split = std::max<int64_t>(per_split, (N * (gs | 1) + kMmaSzWords - 1) / kMmaSzWords);
-  per_split = std::max<int64_t>(1, std::min<int64_t>(per_split, N));
-  const int64_t rows = (N + per_split - 1) / per_split;
-  *wgs = splits * ((N + rows - 1) / rows);
-  return MmaPlan{(int)splits, (int)gs, (int)rows};
-}
-}  // namespace
-
-void mma_plan(int count, const wq_weight *w, int64_t m, int wgs, MmaPlan *plan) {
-  auto total = [&](double T) {
-    int64_t sum = 0, c = 0;
-    for (int i = 0; i < count; ++i) {
-      mma_split(w[i], m, T, &c);
-      sum += c;
-    }
-    return sum;
-  };
-  double hi = 0;   // one workgroup per K split
-  for (int i = 0; i < count; ++i) {
-    const int64_t G = w[i].k / kGroup, gs = std::min<int64_t>(G, mma_max_groups(m));
-    hi = std::max(hi, (double)w[i].n * (double)gs * (16.0 * w[i].bits + 4.0));
-  }
-  if (total(hi) < (int64_t)wgs) {
-    double lo = 0;
-    for (int it = 0; it < 48; ++it) {
-      const double mid = 0.5 * (lo + hi);
-      if (total(mid) <= (int64_t)wgs) hi = mid; else lo = mid;
-    }
-  }
-  int64_t c = 0;
-  for (int i = 0; i < count; ++i) plan[i] = mma_split(w[i], m, hi, &c);
-}
-
-size_t mma_partial_bytes(const wq_weight &w, int64_t m, const MmaPlan &p) {
-  return p.ksplit > 1 ? (size_t)p.ksplit * (size_t)m * (size_t)w.n * sizeof(float) : 0;
-}
-
-namespace {
-template <int BITS, bool PAIR>
-hipError_t launch_mma_rows(int mr, int wgs, int lds, const MmaBatch &a, hipStream_t s) {
-  const dim3 grid((unsigned)wgs), block(kMmaThreads);
-  switch (mr) {
-    case 4: hipLaunchKernelGGL((mma_kernel<BITS, 4, PAIR>), grid, block, lds, s, a); break;
-    case 8: hipLaunchKernelGGL((mma_kernel<BITS, 8, PAIR>), grid, block, lds, s, a); break;
-    default: hipLaunchKernelGGL((mma_kernel<BITS, 16, PAIR>), grid, block, lds, s, a); break;
-  }
-  return hipGetLastError();
-}
-}  // namespace
-
-hipError_t launch_mma_batch(int count, const wq_weight *w, const uint16_t *const *xr, const int64_t *ldx,
-                            const uint32_t *const *signs, int64_t m, void *const *y, const int *out_f32,
-                            const int64_t *ldy, const MmaPlan *plan, float *const *part, hipStream_t s) {
-  if (count <= 0 || count > kMaxBatch || m < 1 || m > 16) return hipErrorInvalidValue;
-  // int4 rotated in the kernel: stored in the order the unpack produces (pair order)
-  bool pair_order = w[0].bits == 4 && signs;
-  for (int i = 0; i < count && pair_order; ++i) pair_order = signs[i] != nullptr;
-  for (int i = 0; i < count && signs; ++i)
-    if ((signs[i] != nullptr) != (signs[0] != nullptr)) return hipErrorInvalidValue;   // all or none
-  const int mr = mma_batch_rows(m), mt = mr > 16 ? 2 : 1;
-  MmaBatch a;
-  memset(&a, 0, sizeof a);
-  for (int i = 0; i < kMaxBatch; ++i) a.first_wg[i] = INT32_MAX;
-  a.count = count;
-  a.m = (int32_t)m;
-  GemmBatch f;   // the K splits' sums (gemm_finalize_kernel)
-  memset(&f, 0, sizeof f);
-  f.count = count;
-  int64_t wgs = 0, fin_blocks = 0;
-  int lds = 0;
-  for (int i = 0; i < count; ++i) {
-    const MmaPlan &p = plan[i];
-    if (!gemm_available(w[i].bits) || w[i].bits != w[0].bits || w[i].k % kGroup) return hipErrorInvalidValue;
-    if ((uint64_t)m * (uint64_t)ldx[i] * 2 > 0x7FFFFFFFull || (uint64_t)w[i].k * 16 * w[i].bits / 8 > 0x7FFFFFFFull)
-      return hipErrorInvalidValue;   // 32-bit buffer offsets and sizes
-    const int64_t G = w[i].k / kGroup;
-    if (p.rows < 1 || p.kgroups < 1 || p.kgroups > mma_max_groups(m) ||
-        p.ksplit != (G + p.kgroups - 1) / p.kgroups)
-      return hipErrorInvalidValue;
-    if (p.ksplit > 1 && !part[i]) return hipErrorInvalidValue;
-    MmaLin &L = a.lin[i];
-    L.codes = w[i].codes;
-    L.scales = w[i].scales;
-    L.zeros = w[i].zeros;
-    L.x = xr[i];
-    L.signs = signs ? signs[i] : nullptr;
-    L.y = y[i];
-    L.part = p.ksplit > 1 ? part[i] : nullptr;
-    L.ldx = ldx[i];
-    L.ldy = ldy[i];
-    L.n = (int32_t)w[i].n;
-    L.k = (int32_t)w[i].k;
-    L.out_f32 = out_f32[i];
-    L.rows = p.rows;
-    L.kgroups = p.kgroups;
-    L.ksplit = p.ksplit;
-    L.rblocks = (int32_t)((w[i].n + p.rows - 1) / p.rows);
-    L.wg_begin = (int32_t)wgs;
-    a.first_wg[i] = (int32_t)wgs;
-    wgs += (int64_t)L.rblocks * L.ksplit;
-    const int64_t rows_here = std::min<int64_t>(p.rows, w[i].n);
-    if (rows_here * (p.kgroups | 1) > kMmaSzWords) return hipErrorInvalidValue;
-    lds = std::max(lds, std::max(mma_piece_bytes(mt),
-                                 p.kgroups * 16 * mr * 16 + (int)rows_here * (p.kgroups | 1) * 4));
-    GemmLin &F = f.lin[i];
-    F.part = L.part;
-    F.y = L.y;
-    F.ldy = L.ldy;
-    F.m = (int32_t)m;
-    F.n = L.n;
-    F.out_f32 = L.out_f32;
-    F.ksplit = L.ksplit;
-    if (L.ksplit > 1) fin_blocks += (finalize_items(F) + 255) / 256;
-  }
-  if (wgs > INT32_MAX || lds > kMmaLds) return hipErrorInvalidValue;
-  a.wgs = (int32_t)wgs;
-  hipError_t e = hipSuccess;
-  switch (w[0].bits) {
-    case 3: e = launch_mma_rows<3, false>(mr, (int)wgs, lds, a, s); break;
-    case 4: e = pair_order ? launch_mma_rows<4, true>(mr, (int)wgs, lds, a, s) : launch_mma_rows<4, false>(mr, (int)wgs, lds, a, s); break;
-    case 6: e = launch_mma_rows<6, false>(mr, (int)wgs, lds, a, s); break;
-    case 8: e = launch_mma_rows<8, false>(mr, (int)wgs, lds, a, s); break;
-  }
-  if (e != hipSuccess || fin_blocks == 0) return e;
-  hipLaunchKernelGGL(gemm_finalize_kernel, dim3((unsigned)fin_blocks), dim3(256), 0, s, f);
   return hipGetLastError();
 }
 

@@ -137,22 +137,6 @@ hipError_t launch_embed(const wq_weight &w, const int32_t *ids, int64_t count, v
 // given), [m][ldx[i]].  ksplit[i] > 1 cuts K over that many workgroups whose
 // fp32 partials go to part[i] ([ksplit][m][n], gemm_partial_bytes) and are
 // added by a second kernel.
-// Narrow batches (1 to 16 rows) on the matrix cores, the weights streamed
-// once (gemm.hip, mma_kernel): per linear, K splits of `kgroups` groups
-// each and `rows` output rows per workgroup.
-struct MmaPlan {
-  int ksplit, kgroups, rows;
-};
-int mma_batch_rows(int64_t m);
-int mma_max_groups(int64_t m);
-void mma_plan(int count, const wq_weight *w, int64_t m, int wgs, MmaPlan *plan);
-size_t mma_partial_bytes(const wq_weight &w, int64_t m, const MmaPlan &p);
-// signs: per linear the rotation's sign vector (the kernel rotates the
-// activations itself), or signs == NULL: none rotated
-hipError_t launch_mma_batch(int count, const wq_weight *w, const uint16_t *const *x, const int64_t *ldx,
-                            const uint32_t *const *signs, int64_t m, void *const *y, const int *out_f32,
-                            const int64_t *ldy, const MmaPlan *plan, float *const *part, hipStream_t s);
-
 bool gemm_available(int bits);
 // whether the kernel for `bits` can take activations whose 8-element groups
 // are in rht_batch's pair order (int4: a cheaper unpack)

@@ -138,17 +138,9 @@ def test_workspace_sizes(lib):
     assert lib.wq_linear_workspace(ctypes.byref(_weight()), 1) == 0
     w = _weight(n=4096, k=2560, rht_signs=16, rht_block=128)
     assert lib.wq_linear_workspace(ctypes.byref(w), 1) == 0
-    # 2..4 rows: the arranged activations of all m rows
-    for m in (2, 3, 4):
+    # 2..16 rows: the arranged activations of all m rows
+    for m in (2, 3, 4, 16):
         assert lib.wq_linear_workspace(ctypes.byref(w), m) == _arranged(2560, m)
-    # 5..16 rows: the streaming matrix-core kernel rotates in LDS; only a K
-    # longer than its LDS holds (K 9728: 64 groups at 8 rows, 32 at 16)
-    # leaves fp32 partial sums, [splits][m][n]
-    for m in (5, 8, 16):
-        assert lib.wq_linear_workspace(ctypes.byref(w), m) == 0
-    w_long = _weight(n=4096, k=9728, rht_signs=16, rht_block=128)
-    assert lib.wq_linear_workspace(ctypes.byref(w_long), 8) == 2 * 8 * 4096 * 4
-    assert lib.wq_linear_workspace(ctypes.byref(w_long), 16) == 3 * 16 * 4096 * 4
     # without rotation the activations are still arranged (pair order, sums)
     w_plain = _weight(n=4096, k=2560)
     assert lib.wq_linear_workspace(ctypes.byref(w_plain), 4) == _arranged(2560, 4)
@@ -183,19 +175,15 @@ def test_other_entry_points_reject(lib):
 
 
 def test_batch_workspace_for_large_m(lib):
-    # m = 1: no workspace; 2 <= m <= 4: every linear's arranged activations
-    # side by side; 5 <= m <= 16: the streaming matrix-core launch, whose
-    # workspace holds the fp32 partial sums [splits][m][n] of a K longer
-    # than its LDS takes (9728: 2 splits at 5 rows, 3 at 16); m >= 17: one
-    # matrix-core launch over all the linears, whose workspace holds every
-    # linear's rotated activations (fp16 [m][k]) and the fp32 partial sums
-    # of split K
+    # m = 1: no workspace; 2 <= m <= 16: every linear's arranged activations
+    # side by side; m >= 17: one matrix-core launch over all the linears,
+    # whose workspace holds every linear's rotated activations (fp16 [m][k])
+    # and the fp32 partial sums of split K
     sg = dict(rht_signs=16, rht_block=128)
     arr = (dq.WqWeight * 2)(_weight(n=256, k=2560, **sg), _weight(n=128, k=9728, **sg))
     assert lib.wq_linear_batch_workspace(2, arr, 1) == 0
-    assert lib.wq_linear_batch_workspace(2, arr, 4) == _arranged(2560, 4) + _arranged(9728, 4)
-    assert lib.wq_linear_batch_workspace(2, arr, 16) == 3 * 16 * 128 * 4
-    assert lib.wq_linear_batch_workspace(2, arr, 5) == 2 * 5 * 128 * 4
+    assert lib.wq_linear_batch_workspace(2, arr, 16) == _arranged(2560, 16) + _arranged(9728, 16)
+    assert lib.wq_linear_batch_workspace(2, arr, 5) == _arranged(2560, 5) + _arranged(9728, 5)
     assert lib.wq_linear_batch_workspace(2, arr, 40) >= 40 * (2560 + 9728) * 2
     need = lib.wq_linear_batch_workspace(2, arr, 512)
     assert need >= 512 * (2560 + 9728) * 2

@@ -401,8 +401,8 @@ def test_batch_shared_input_rotated_once(m):
 def test_deterministic_with_uninitialised_workspace(m, k):
     # the workspace needs no initialisation: one filled with NaN bit
     # patterns gives the same bits as a zeroed one, call after call (16
-    # rows at K 9728: the streaming kernel's K-split partial sums; 40 rows:
-    # the GEMM's rotated activations)
+    # rows at K 9728: the arranged activations of the 16-row tile; 40 rows:
+    # the GEMM's rotated activations and K-split partial sums)
     say(f"determinism m={m} k={k}")
     w, x, signs = _inputs(512, k, m, 5)
     qw = _gpu_weight(w, signs, 4)

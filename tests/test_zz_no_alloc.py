@@ -17,9 +17,8 @@ from gpu_util import check_close, dev, dev_u32, say
 
 pytestmark = pytest.mark.gpu
 
-# The workspace holds: at 2 to 4 rows the arranged activations; at 16 rows
-# the partial sums of K = 9728, split over workgroups; above 16 rows the
-# rotated activations and the partial sums of split K
+# K = 9728 is split over workgroups at 64 rows and more (partial sums in the
+# workspace); below 64 rows the workspace holds the arranged activations
 SHAPES = [(256, 2560), (130, 9728), (64, 1024)]
 
 
@@ -42,8 +41,7 @@ def test_noalloc_matches_workspace_call(ms):
     for m in ms:
         say(f"noalloc grouped call m={m}")
         qs, xs, refs = _linears(m, 300 + m)
-        need = dq.wq_linear_batch_workspace(qs, m)
-        assert need <= dq.NOALLOC_SCRATCH_BYTES and (need > 0) == (m > 1)
+        assert 0 < dq.wq_linear_batch_workspace(qs, m) <= dq.NOALLOC_SCRATCH_BYTES or m == 1
         want = dq.wq_linear_batch(qs, xs)
         got = dq.wq_linear_batch_noalloc(qs, xs)
         torch.cuda.synchronize()
