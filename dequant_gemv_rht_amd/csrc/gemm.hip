@@ -188,10 +188,13 @@ __device__ __forceinline__ uint32_t code_pair(const uint32_t (&w)[BITS], PairCon
 // The lane's B operand of 16-k block kk: codes 8 kk .. 8 kk + 7 of its slice
 // as q - z: q = h c + d exactly (c, d per half remove the 1024 offset and
 // the int4 factor 16), then q - z, exact for an integer zero point and
-// rounded once otherwise.  The scale is not applied here: the accumulator
-// carries it (see the step below).  For a group whose scale is 0, c, d and
-// z come in as 0 and the operand is 0.
-template <int BITS, int KK>
+// rounded once otherwise.  FAST (every zero point of the wave's rows an
+// integer in [-1024, 1023]): the caller passes d - z as d and one fma gives
+// q - z (h c and d - z are exact in fp16, and so is the integer q - z, of
+// magnitude below 2048, that the fma rounds).  The scale is not applied
+// here: the accumulator carries it (see the step below).  For a group whose
+// scale is 0, c, d and z come in as 0 and the operand is 0.
+template <int BITS, int KK, bool FAST = false>
 __device__ __forceinline__ half8 b_operand(const uint32_t (&w)[BITS], PairConsts k, half2v c, half2v d, half2v z) {
   uint32_t p[4];
 #pragma unroll
@@ -204,7 +207,7 @@ __device__ __forceinline__ half8 b_operand(const uint32_t (&w)[BITS], PairConsts
       default: h = code_pair<BITS, 4 * KK + 3>(w, k); break;
     }
     const half2v q = __builtin_elementwise_fma(as_h2(h), c, d);
-    p[i] = as_u32(q - z);
+    p[i] = as_u32(FAST ? q : q - z);
   }
   return __builtin_bit_cast(half8, u32x4{p[0], p[1], p[2], p[3]});
 }
@@ -480,7 +483,7 @@ __global__ __launch_bounds__(kGemmThreads, (Tile<MB, NB>::PerCU)) void gemm_kern
 #pragma unroll
   for (int j = 0; j < NB; ++j) unit[j] = 1.0f;
 
-  // FAST (pair order only): every zero point of the wave's rows over its K
+  // FAST (narrow tiles): every zero point of the wave's rows over its K
   // range takes the one-fma path; chosen once per wave, before the loop, so
   // that the step stays one straight block the compiler can interleave
   auto step = [&](auto sconst, int kt, bool active, auto fconst) {
@@ -510,7 +513,9 @@ __global__ __launch_bounds__(kGemmThreads, (Tile<MB, NB>::PerCU)) void gemm_kern
       const float sf = half_bits_to_float(szv[j] & 0xFFFFu);
       const bool live = sf != 0.0f;
       if (gstart) {
-        const float r = live ? unit[j] / sf : 1.0f;
+        // the ratio need not be exact: its rounding (v_rcp_f32 is within
+        // 1 ulp) changes the accumulated sum by a few parts in 2^24
+        const float r = live ? unit[j] * __builtin_amdgcn_rcpf(sf) : 1.0f;
         unit[j] = live ? sf : unit[j];
 #pragma unroll
         for (int i = 0; i < MB; ++i) acc[i][j] *= r;
@@ -536,11 +541,12 @@ __global__ __launch_bounds__(kGemmThreads, (Tile<MB, NB>::PerCU)) void gemm_kern
         }
       } else {
         const half2v c = live ? half2v{(_Float16)1.0f, kHi} : half2v{};
-        const half2v d = live ? half2v{(_Float16)-1024.0f, (_Float16)(BITS == 4 ? -64.0f : -1024.0f)} : half2v{};
-        bop[j][0] = b_operand<BITS, 0>(cw[st][j], pk, c, d, z);
-        bop[j][1] = b_operand<BITS, 1>(cw[st][j], pk, c, d, z);
-        bop[j][2] = b_operand<BITS, 2>(cw[st][j], pk, c, d, z);
-        bop[j][3] = b_operand<BITS, 3>(cw[st][j], pk, c, d, z);
+        half2v d = live ? half2v{(_Float16)-1024.0f, (_Float16)(BITS == 4 ? -64.0f : -1024.0f)} : half2v{};
+        if constexpr (fast) d = d - z;
+        bop[j][0] = b_operand<BITS, 0, fast>(cw[st][j], pk, c, d, z);
+        bop[j][1] = b_operand<BITS, 1, fast>(cw[st][j], pk, c, d, z);
+        bop[j][2] = b_operand<BITS, 2, fast>(cw[st][j], pk, c, d, z);
+        bop[j][3] = b_operand<BITS, 3, fast>(cw[st][j], pk, c, d, z);
       }
     }
 #pragma unroll
@@ -606,9 +612,11 @@ __global__ __launch_bounds__(kGemmThreads, (Tile<MB, NB>::PerCU)) void gemm_kern
       if constexpr (kStages > 7) step(std::integral_constant<int, 7>{}, kt0 + i0 + 7, i0 + 7 < T, fconst);
     }
   };
-  if constexpr (PAIR) {
-    // the wave's zero points (lane = row, its groups of the K range; rows
-    // past N read 0): all integers in [-1024, 1023]?
+  // narrow tiles: the wave's zero points (lane = row, its groups of the K
+  // range; rows past N read 0) all integers in [-1024, 1023]?  The 128 x
+  // 256 tile keeps the general path: there the one-fma operand measured
+  // slower (the int4 block at M = 512: 160.8 -> 166.4 us; 204 -> 221 VGPRs)
+  if constexpr (MB <= 2) {
     bool ok = true;
 #pragma unroll
     for (int g = 0; g < kMaxGroups; ++g) {

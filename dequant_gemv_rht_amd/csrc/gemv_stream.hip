@@ -1556,23 +1556,27 @@ __device__ __forceinline__ void stream_quads(const LinDesc &L, int m_valid, int 
 
 // The pre-pass of the batch-tile kernels: every linear's activations, all m
 // rows, rotated (when the linear has signs) and arranged in the slice layout
-// [m][K/32][20 words].  One exponent per batch row, from the largest |x'| of
-// the whole row, so that the batch-tile kernel removes it from each output
-// once (its partials add slices of many blocks in registers).  One
-// 512-thread workgroup per (linear, batch row), dealt by a packed table of
-// first workgroups; DPP row rg takes blocks rg + 32 i, the first
-// kXprepHeld of them held in registers between the maximum and the stores,
-// any further ones (K above 12288) rotated twice: for the maximum, then to
-// store.
-constexpr int kXprepThreads = 512;
-constexpr int kXprepHeld = 3;
+// [m][K/32][20 words].  One exponent per batch row, so that the batch-tile
+// kernel removes it from each output once (its partials add slices of many
+// blocks in registers).  The exponent comes from a bound on the row's
+// rotated values that needs no rotation: a rotated value is a sum of 128
+// signed values over sqrt(128), so |x'| <= sqrt(128) max |x| (max |x| itself
+// without rotation); E puts that bound in [2^14, 2^15), which keeps every
+// stored value below 2^15 and the row's largest one at 2^7 or more.  So
+// each workgroup of one wave can take its own 512-wide chunk of a row (one
+// 128-block per DPP row) and still agree on E with the row's other chunks:
+// it reads the whole row for the maximum (lane L's loads cover elements
+// 512 i + 8 L .. + 7, and load i = its chunk holds its own elements), then
+// rotates and stores its four blocks.  Workgroups per (linear, batch row):
+// ceil(K / 512), dealt by a packed table of first workgroups.
+constexpr int kXprepThreads = 64;
 
 struct XprepMat {
   const uint16_t *x;
   uint32_t *out;
   const uint32_t *signs;
   int64_t ldx;
-  int32_t k, m, wg_begin;
+  int32_t k, m, chunks, wg_begin;
 };
 
 struct XprepBatch {
@@ -1580,67 +1584,50 @@ struct XprepBatch {
   XprepMat mat[kMaxBatch];
 };
 
+// Largest |value| of the eight fp16 values in v.
+__device__ __forceinline__ float absmax8h(u32x4 v) {
+  const uint32_t a = v.x & 0x7FFF7FFFu, b = v.y & 0x7FFF7FFFu, c = v.z & 0x7FFF7FFFu, d = v.w & 0x7FFF7FFFu;
+  // magnitudes of finite fp16 values order as their bit patterns
+  const uint32_t lo = max(max(a & 0xFFFFu, b & 0xFFFFu), max(c & 0xFFFFu, d & 0xFFFFu));
+  const uint32_t hi = max(max(a >> 16, b >> 16), max(c >> 16, d >> 16));
+  return half_bits_to_float(max(lo, hi));
+}
+
 template <int BITS>
 __global__ __launch_bounds__(kXprepThreads) void xprep_kernel(XprepBatch a) {
-  constexpr int RG = kXprepThreads / 16;
-  __shared__ __align__(16) float red[RG];
   const int w = blockIdx.x;
   int l = 0;
 #pragma unroll
   for (int i = 1; i < kMaxBatch; ++i)
     if (w >= a.first_wg[i]) l = i;
   const XprepMat M = a.mat[l];
-  const int m = w - M.wg_begin;
+  const int local = w - M.wg_begin, m = local / M.chunks, c = local - m * M.chunks;
   const int nb = M.k / kGroup, S = M.k / kSlice;
-  const int t = threadIdx.x, rg = t >> 4, jj = t & 15;
+  const int lane = threadIdx.x, jj = lane & 15, b = 4 * c + (lane >> 4);
   const bool rotate = M.signs != nullptr;
-  const uint16_t *xrow = M.x + (size_t)m * M.ldx;
-  uint32_t *orow = M.out + (size_t)m * S * kSliceStride;
-  // branches on the block index are uniform across the 16 lanes of a DPP row
-  auto load = [&](int b, float (&v)[8]) {
-    const int kk = 128 * b + 8 * jj;
-    const u32x4 raw = *reinterpret_cast<const u32x4 *>(xrow + kk);
-    const uint32_t sword = rotate ? M.signs[kk >> 5] : 0u;
-    load_rotated8(rotate, raw, sword, kk, jj, v);
-  };
-  float v[kXprepHeld][8];
+  const rsrc_t rx = make_rsrc(M.x + (size_t)m * M.ldx, (uint32_t)M.k * 2u);   // elements past K read zero
   float mx = 0.f;
-#pragma unroll
-  for (int i = 0; i < kXprepHeld; ++i) {
-    if (rg + RG * i < nb) {
-      load(rg + RG * i, v[i]);
-      mx = fmaxf(mx, absmax8(v[i]));
-    }
-  }
-  for (int b = rg + RG * kXprepHeld; b < nb; b += RG) {
-    float u[8];
-    load(b, u);
-    mx = fmaxf(mx, absmax8(u));
+  u32x4 mine = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll 4
+  for (int i = 0; i < M.chunks; ++i) {
+    const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (uint32_t)(1024 * i + 16 * lane), 0, 0));
+    mx = fmaxf(mx, absmax8h(v));
+    if (i == c) mine = v;
   }
   mx = row16_max(mx);
-  if (jj == 0) red[rg] = mx;
-  __syncthreads();
-  float g = 0.f;
-#pragma unroll
-  for (int q = 0; q < RG; q += 4) {
-    const float4 r4 = *reinterpret_cast<const float4 *>(&red[q]);
-    g = fmaxf(g, fmaxf(fmaxf(r4.x, r4.y), fmaxf(r4.z, r4.w)));
-  }
-  const int E = act_exponent(g * rot_scale(rotate));
-  auto put = [&](int b, float (&u)[8]) {
-    uint32_t o[4];
-    float xe, xt;
-    arrange8<BITS>(rotate, u, jj, E, o, xe, xt);
-    store_slice_part(orow + (size_t)(4 * b + (jj >> 2)) * kSliceStride, jj, o, xe, xt, E);
-  };
-#pragma unroll
-  for (int i = 0; i < kXprepHeld; ++i)
-    if (rg + RG * i < nb) put(rg + RG * i, v[i]);
-  for (int b = rg + RG * kXprepHeld; b < nb; b += RG) {
-    float u[8];
-    load(b, u);
-    put(b, u);
-  }
+  mx = fmaxf(fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mx), 0)),
+                   __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mx), 16))),
+             fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mx), 32)),
+                   __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mx), 48))));
+  const int E = act_exponent(rotate ? mx * 11.313708498984761f : mx);   // sqrt(128) max |x|
+  if (b >= nb) return;   // uniform over the 16 lanes of a DPP row
+  const int kk = 128 * b + 8 * jj;
+  float v[8];
+  load_rotated8(rotate, mine, rotate ? M.signs[kk >> 5] : 0u, kk, jj, v);
+  uint32_t o[4];
+  float xe, xt;
+  arrange8<BITS>(rotate, v, jj, E, o, xe, xt);
+  store_slice_part(M.out + ((size_t)m * S + (size_t)(4 * b + (jj >> 2))) * kSliceStride, jj, o, xe, xt, E);
 }
 
 template <int BITS, bool FULL>
@@ -1939,9 +1926,10 @@ hipError_t launch_xprep(int bits, int count, const uint16_t *const *x, const int
     M.ldx = ldx[i];
     M.k = (int32_t)k[i];
     M.m = (int32_t)m;
+    M.chunks = (int32_t)((k[i] + 511) / 512);
     M.wg_begin = (int32_t)wgs;
     a.first_wg[i] = (int32_t)wgs;
-    wgs += m;   // one workgroup per batch row
+    wgs += m * M.chunks;   // one workgroup per batch row and 512-wide chunk
   }
   if (wgs > INT32_MAX) return hipErrorInvalidValue;
   const dim3 grid((unsigned)wgs), block(kXprepThreads);
