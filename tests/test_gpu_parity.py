@@ -415,6 +415,35 @@ def test_deterministic_with_uninitialised_workspace(m, k):
         assert torch.equal(dq.wq_linear(qw, xd, workspace=ws), first)
 
 
+@pytest.mark.parametrize("m", [24, 63])
+def test_split_k_sums_stable(m):
+    # 17..64 rows: K = 9728 and 4096 are cut over workgroups whose partials
+    # a second kernel adds.  Back-to-back calls on one workspace, no host
+    # sync between them, must give the same bits every time and match the
+    # oracle; a call on the caller's rotated input (natural order instead of
+    # the rotation's pair order) must match it too.
+    say(f"split-K sums m={m}")
+    shapes = [(2560, 9728), (640, 4096), (130, 2560)]
+    qs, xs, xrot, refs = [], [], [], []
+    for i, (n, k) in enumerate(shapes):
+        w, x, signs = _inputs(n, k, m, 900 + 10 * m + i)
+        q, s_, z = OR.prepare(w, signs, 4)
+        refs.append(OL.linear(q, s_, z, x, signs))
+        qs.append(_gpu_weight(w, signs, 4))
+        xs.append(dev(x))
+        xrot.append(dq.rht_apply(dev(x), dev_u32(signs)))
+    ws = dq.new_workspace(dq.wq_linear_batch_workspace(qs, m))
+    outs = [dq.wq_linear_batch(qs, xs, workspace=ws) for _ in range(20)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        for a, b in zip(o, outs[0]):
+            assert torch.equal(a, b)
+    for (n, k), y, ref in zip(shapes, outs[0], refs):
+        check_close(y.float().cpu().numpy(), ref, f"split sums n={n} k={k} m={m}")
+    for (n, k), y, ref in zip(shapes, dq.wq_linear_batch(qs, xrot, fuse_rht=False), refs):
+        check_close(y.float().cpu().numpy(), ref, f"split sums, rotated by the caller n={n} k={k} m={m}")
+
+
 def test_graph_replay_matches_eager():
     say("graph replay")
     w, x, signs = _inputs(384, 2560, 1, 6)
