@@ -629,11 +629,15 @@ struct Ring {
   // 1% slower for int6)
   static constexpr bool stage = BITS == 8;
   static constexpr int slot = codes + (stage ? 0 : 2 * 64 * 4);      // + scales, zeros
-  // steps in flight (deeper rings measured slower: int4 depth 4, 5, 6 took
-  // 13.7, 14.2, 14.9 us against 12.2 us for the seven-projection block; int6
-  // and int8 depth 3 8.56 and 9.66 us against 6.81 and 8.00 us for a
-  // 9728 -> 2560 linear)
-  static constexpr int depth = BITS == 3 ? 4 : BITS == 4 ? 3 : 2;
+  // steps in flight: two (three for int3) keep a compute unit's weight
+  // reads in flight and leave its queue of vector-memory instructions room
+  // for the activation loads at the start.  Measured on the seven-projection
+  // block at batch 1: int4 depth 2 11.17 us against 11.85 us at depth 3
+  // (13.7, 14.2, 14.9 us at 4, 5, 6 in an earlier session); int3 depth 3
+  // 11.97 us against 12.32 at 4, 12.36 at 2, 12.65 at 5 and 13.09 at 6;
+  // int6 and int8 depth 3 8.56 and 9.66 us against 6.81 and 8.00 us at 2
+  // for a 9728 -> 2560 linear.
+  static constexpr int depth = BITS == 3 ? 3 : 2;
   static constexpr int q = (flat ? ni : 2 * nc) + (stage ? 0 : 2);  // vector loads per wave per step
   static constexpr int threads = kRingThreads;
   static constexpr int waves = threads / 64;
