@@ -629,15 +629,17 @@ struct Ring {
   // 1% slower for int6)
   static constexpr bool stage = BITS == 8;
   static constexpr int slot = codes + (stage ? 0 : 2 * 64 * 4);      // + scales, zeros
-  // steps in flight: two (three for int3) keep a compute unit's weight
-  // reads in flight and leave its queue of vector-memory instructions room
-  // for the activation loads at the start.  Measured on the seven-projection
-  // block at batch 1: int4 depth 2 11.17 us against 11.85 us at depth 3
-  // (13.7, 14.2, 14.9 us at 4, 5, 6 in an earlier session); int3 depth 3
-  // 11.97 us against 12.32 at 4, 12.36 at 2, 12.65 at 5 and 13.09 at 6;
-  // int6 and int8 depth 3 8.56 and 9.66 us against 6.81 and 8.00 us at 2
-  // for a 9728 -> 2560 linear.
-  static constexpr int depth = BITS == 3 ? 3 : 2;
+  // steps in flight: two (three for int3, one for the wide int8 steps)
+  // keep a compute unit's weight reads in flight and leave its queue of
+  // vector-memory instructions room for the activation loads at the start.
+  // Measured on the seven-projection block at batch 1: int4 depth 2 11.17
+  // us against 11.85 us at depth 3 and 15.7 us at 1 (13.7, 14.2, 14.9 us at
+  // 4, 5, 6 in an earlier session); int3 depth 3 11.97 us against 12.32 at
+  // 4, 12.36 at 2, 12.65 at 5 and 13.09 at 6; int6 15.2 us at depth 2, 18.0
+  // at 1; int6 and int8 depth 3 8.56 and 9.66 us against 6.81 and 8.00 us
+  // at 2 for a 9728 -> 2560 linear; int8 depth 1: the 151936 x 2560 head
+  // 69.2 -> 67.1 us, the mixed 6/8 down_proj 7.07 -> 7.11 us.
+  static constexpr int depth = BITS == 3 ? 3 : BITS == 8 ? 1 : 2;
   static constexpr int q = (flat ? ni : 2 * nc) + (stage ? 0 : 2);  // vector loads per wave per step
   static constexpr int threads = kRingThreads;
   static constexpr int waves = threads / 64;
