@@ -611,9 +611,13 @@ __device__ __forceinline__ void stream_rows(const LinDesc &L, const uint32_t *co
 // lanes 0..31; int6: three), read from g's task.  Lane j of DPP row g finds
 // row r of its slice at byte 256 BITS r + 64 BITS g + 4 BITS j of the
 // region.
-// Workgroup size of every ring: 8 waves.  (16-wave rings for int6 and int8
-// measured slower: 7.57 against 6.81 us for an int6 9728 -> 2560 linear;
-// an 8-bit 16-wave ring does not fit beside a long K's activations.)
+// Workgroup size of the rings: 8 waves, 16 for int3.  (16-wave rings for
+// int6 and int8 measured slower: 7.57 against 6.81 us for an int6 9728 ->
+// 2560 linear, and alike for the int6 block at one step in flight; an 8-bit
+// 16-wave ring does not fit beside a long K's activations; a 16-wave int4
+// ring took the int4 block from 11.17 to 12.35 us at two steps in flight and
+// 11.4 us at one.  The int3 block: 12.1 -> 11.35-11.65 us with 16 waves
+// and two steps in flight, 11.66 us with one.)
 constexpr int kRingThreads = 512;
 
 template <int BITS>
@@ -629,19 +633,19 @@ struct Ring {
   // 1% slower for int6)
   static constexpr bool stage = BITS == 8;
   static constexpr int slot = codes + (stage ? 0 : 2 * 64 * 4);      // + scales, zeros
-  // steps in flight: two (three for int3, one for the wide int8 steps)
-  // keep a compute unit's weight reads in flight and leave its queue of
-  // vector-memory instructions room for the activation loads at the start.
-  // Measured on the seven-projection block at batch 1: int4 depth 2 11.17
-  // us against 11.85 us at depth 3 and 15.7 us at 1 (13.7, 14.2, 14.9 us at
-  // 4, 5, 6 in an earlier session); int3 depth 3 11.97 us against 12.32 at
-  // 4, 12.36 at 2, 12.65 at 5 and 13.09 at 6; int6 15.2 us at depth 2, 18.0
-  // at 1; int6 and int8 depth 3 8.56 and 9.66 us against 6.81 and 8.00 us
-  // at 2 for a 9728 -> 2560 linear; int8 depth 1: the 151936 x 2560 head
+  // steps in flight: two (one for the wide int8 steps) keep a compute
+  // unit's weight reads in flight and leave its queue of vector-memory
+  // instructions room for the activation loads at the start.  Measured on
+  // the seven-projection blocks at batch 1: int4 11.17 us at depth 2
+  // against 11.85 us at 3 and 15.7 us at 1 (13.7, 14.2, 14.9 us at 4, 5, 6
+  // in an earlier session); int3 with 8 waves 11.97 us at depth 3 against
+  // 12.32 at 4, 12.36 at 2, 12.65 at 5, 13.09 at 6; int6 15.2 us at depth 2,
+  // 18.0 at 1; int6 and int8 depth 3 8.56 and 9.66 us against 6.81 and 8.00
+  // us at 2 for a 9728 -> 2560 linear; int8 depth 1: the 151936 x 2560 head
   // 69.2 -> 67.1 us, the mixed 6/8 down_proj 7.07 -> 7.11 us.
-  static constexpr int depth = BITS == 3 ? 3 : BITS == 8 ? 1 : 2;
+  static constexpr int depth = BITS == 8 ? 1 : 2;
   static constexpr int q = (flat ? ni : 2 * nc) + (stage ? 0 : 2);  // vector loads per wave per step
-  static constexpr int threads = kRingThreads;
+  static constexpr int threads = BITS == 3 ? 2 * kRingThreads : kRingThreads;
   static constexpr int waves = threads / 64;
 };
 
@@ -927,9 +931,9 @@ struct ActAhead {
   uint32_t sw[XC];
 };
 
-template <int XC>
+template <int XC, int TH = kRingThreads>
 __device__ __forceinline__ void act_ahead_loads(const LinDesc &L, ActAhead<XC> &a) {
-  constexpr int RG = kRingThreads / 16;
+  constexpr int RG = TH / 16;
   const int t = threadIdx.x, rg = t >> 4, j = t & 15;
   const int items = L.k / kGroup;
   const rsrc_t rx = make_rsrc(L.x, (uint32_t)L.k * 2);
@@ -1637,14 +1641,14 @@ __global__ __launch_bounds__(kXprepThreads) void xprep_kernel(XprepBatch a) {
 }
 
 template <int BITS, bool FULL>
-__global__ __launch_bounds__(kRingThreads) void gemv_ring_kernel(int t1, int t2, int t3, int t4, int t5, int t6, int t7, GemvArgs a) {
+__global__ __launch_bounds__(Ring<BITS>::threads) void gemv_ring_kernel(int t1, int t2, int t3, int t4, int t5, int t6, int t7, GemvArgs a) {
   extern __shared__ uint32_t smem[];
   const int w = blockIdx.x;
   const LinDesc L = fetch_desc(a, w, FirstTiles{t1, t2, t3, t4, t5, t6, t7});
   const int r0 = (w - L.tile_begin) * L.rows_per_wg;
   if (r0 >= L.n) return;
   ActAhead<kActAhead<BITS>> ahead;
-  act_ahead_loads(L, ahead);
+  act_ahead_loads<kActAhead<BITS>, Ring<BITS>::threads>(L, ahead);
   stream_ring<BITS, FULL>(L, L.codes + (size_t)r0 * (L.k / kSlice) * BITS, r0, min(L.rows_per_wg, L.n - r0), smem,
                           ahead);
 }
@@ -1870,9 +1874,9 @@ hipError_t launch_bits(int mt, const GemvArgs &a, hipStream_t s) {
     bool full = true;
     for (int i = 0; i < a.count; ++i) full = full && a.lin[i].k % kSeg == 0;
     if (full)
-      hipLaunchKernelGGL((gemv_ring_kernel<BITS, true>), dim3(a.tiles), dim3(kRingThreads), a.lds_bytes, s, a.first_tile[1], a.first_tile[2], a.first_tile[3], a.first_tile[4], a.first_tile[5], a.first_tile[6], a.first_tile[7], a);
+      hipLaunchKernelGGL((gemv_ring_kernel<BITS, true>), dim3(a.tiles), dim3(Ring<BITS>::threads), a.lds_bytes, s, a.first_tile[1], a.first_tile[2], a.first_tile[3], a.first_tile[4], a.first_tile[5], a.first_tile[6], a.first_tile[7], a);
     else
-      hipLaunchKernelGGL((gemv_ring_kernel<BITS, false>), dim3(a.tiles), dim3(kRingThreads), a.lds_bytes, s, a.first_tile[1], a.first_tile[2], a.first_tile[3], a.first_tile[4], a.first_tile[5], a.first_tile[6], a.first_tile[7], a);
+      hipLaunchKernelGGL((gemv_ring_kernel<BITS, false>), dim3(a.tiles), dim3(Ring<BITS>::threads), a.lds_bytes, s, a.first_tile[1], a.first_tile[2], a.first_tile[3], a.first_tile[4], a.first_tile[5], a.first_tile[6], a.first_tile[7], a);
     return hipGetLastError();
   }
   switch (mt) {
