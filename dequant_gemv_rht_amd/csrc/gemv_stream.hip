@@ -1580,6 +1580,7 @@ __device__ __forceinline__ void stream_quads(const LinDesc &L, int m_valid, int 
 // rotates and stores its four blocks.  Workgroups per (linear, batch row):
 // ceil(K / 512), dealt by a packed table of first workgroups.
 constexpr int kXprepThreads = 64;
+constexpr int kXprepAhead = 20;   // chunks of a row loaded at once (K up to 10240)
 
 struct XprepMat {
   const uint16_t *x;
@@ -1616,13 +1617,25 @@ __global__ __launch_bounds__(kXprepThreads) void xprep_kernel(XprepBatch a) {
   const int lane = threadIdx.x, jj = lane & 15, b = 4 * c + (lane >> 4);
   const bool rotate = M.signs != nullptr;
   const rsrc_t rx = make_rsrc(M.x + (size_t)m * M.ldx, (uint32_t)M.k * 2u);   // elements past K read zero
+  // the first kXprepAhead chunks' loads all go out before any is used (one
+  // round of load latency for K up to 512 kXprepAhead); chunks past the row
+  // read zero
   float mx = 0.f;
   u32x4 mine = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll 4
-  for (int i = 0; i < M.chunks; ++i) {
-    const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (uint32_t)(1024 * i + 16 * lane), 0, 0));
-    mx = fmaxf(mx, absmax8h(v));
-    if (i == c) mine = v;
+  u32x4 rowv[kXprepAhead];
+#pragma unroll
+  for (int i = 0; i < kXprepAhead; ++i)
+    rowv[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (uint32_t)(1024 * i + 16 * lane), 0, 0));
+  __builtin_amdgcn_sched_barrier(0);   // every load out before the first use
+#pragma unroll
+  for (int i = 0; i < kXprepAhead; ++i) {
+    mx = fmaxf(mx, absmax8h(rowv[i]));
+    mine = i == c ? rowv[i] : mine;
+  }
+  for (int i = kXprepAhead; i < M.chunks; ++i) {
+    const u32x4 u = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (uint32_t)(1024 * i + 16 * lane), 0, 0));
+    mx = fmaxf(mx, absmax8h(u));
+    if (i == c) mine = u;
   }
   mx = row16_max(mx);
   mx = fmaxf(fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mx), 0)),
