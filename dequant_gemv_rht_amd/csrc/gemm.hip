@@ -663,6 +663,8 @@ __host__ __device__ inline int64_t finalize_items(const GemmLin &L) {
   return L.n % 4 ? mn : mn / 4;
 }
 
+constexpr int kFinAhead = 8;
+
 __global__ __launch_bounds__(256) void gemm_finalize_kernel(GemmBatch a) {
   int l = -1, base = 0;
   for (int i = 0; i < a.count; ++i) {
@@ -690,8 +692,19 @@ __global__ __launch_bounds__(256) void gemm_finalize_kernel(GemmBatch a) {
     return;
   }
   const int64_t e = item * 4;   // 4 columns of one row
-  float4 s = *reinterpret_cast<const float4 *>(&L.part[e]);
-  for (int q = 1; q < L.ksplit; ++q) {
+  // the first kFinAhead splits' loads all go out before the first add (one
+  // round of load latency instead of one per split), then the rest in turn
+  float4 pv[kFinAhead];
+#pragma unroll
+  for (int q = 0; q < kFinAhead; ++q)
+    pv[q] = q < L.ksplit ? *reinterpret_cast<const float4 *>(&L.part[(size_t)q * mn + e]) : float4{0.f, 0.f, 0.f, 0.f};
+  float4 s = pv[0];
+#pragma unroll
+  for (int q = 1; q < kFinAhead; ++q)
+    if (q < L.ksplit) {
+      s.x += pv[q].x; s.y += pv[q].y; s.z += pv[q].z; s.w += pv[q].w;
+    }
+  for (int q = kFinAhead; q < L.ksplit; ++q) {
     const float4 p = *reinterpret_cast<const float4 *>(&L.part[(size_t)q * mn + e]);
     s.x += p.x; s.y += p.y; s.z += p.z; s.w += p.w;
   }
